@@ -1,0 +1,246 @@
+"""Plain fp64 CPU oracle for paged INT8-KV GQA attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the smoke check of the package entry
+and the CPU-baseline leg of the benchmark use it.  It shares no code, table or
+helper with the HIP library; both sides receive their inputs from the seeded
+generators, which hold none of the method's arithmetic.
+
+What it computes, and where each step comes from
+------------------------------------------------
+Sources are the pages collected for this method:
+
+* [P1] "KV-Cache 全栈优化系统" (project README on gitlink), section
+  "主要特性" (main features), item on low-bit linear and KV-cache
+  compression: the attention layer keeps K/V as INT8 obtained by dynamic
+  per-token quantisation and restores them on demand during attention.
+* [P3] "KV Cache 优化全景解析——从基础原理到工程实践" (cnblogs daily report):
+  section 2.1, the attention equation softmax(Q K^T / sqrt(d_k)) V;
+  section 2.3, the KV-cache size formula 2 x L x B x T x H_kv x d_h x bytes
+  with INT8 = 1 byte; section 3.3, GQA: the query heads are split into groups
+  and every group shares one K/V head; section 4.2, PagedAttention: logical
+  blocks are mapped to physical blocks through a block table; section 6.3,
+  vLLM hashes fixed blocks of 16/32 tokens.
+* [P4] "大模型推理加速：KV Cache与vLLM技术解析" section 4.1: KV cache kept in
+  FP16/INT8 while attention accumulates in FP32.
+
+The pages do not spell out the quantiser's arithmetic.  The readings taken
+here (all listed with reasons in the design notes of the repository):
+
+1. one scale per (token, KV head), separately for K and V;
+2. scale s = fp16_rne(fp32_rne(absmax / 127)), gradual underflow, an fp16
+   overflow saturates to 65504;
+3. codes c_i = clamp(round_half_even(fp32_rne(x_i / s)), -127, 127), all
+   zero when s == 0;
+4. dequantised value x_hat_i = c_i * s (exact in fp64);
+5. attention runs in fp64 over the dequantised cache; head h of Hq reads KV
+   head h // (Hq / Hkv); logical token t of a sequence lives in physical block
+   block_table[b, t // 16] at slot t % 16; an empty context yields zeros;
+6. a prefill chunk of Lc rows for a sequence with ctx tokens (chunk
+   included) places row i at absolute position ctx - Lc + i, which attends to
+   keys 0 .. ctx - Lc + i inclusive.
+
+The code step divides in fp32 exactly as specified, so the integer decision
+is taken in the same precision as the GPU.  For bf16 inputs and fp16 scales
+the fp32 rounding of the quotient can never move a non-tie onto a tie (the
+quotient of an 8-bit-significand value by an 11-bit-significand value is at
+least 2^-12 away from any half-integer it does not equal, far above fp32's
+half-ulp below 128), so the result equals exact rational rounding; the pin
+tests check that exhaustively.
+
+Every function here is written for clarity, not speed.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK_SIZE = 16          # tokens per physical block ([P3] section 6.3)
+QMAX = 127               # symmetric INT8 range, -128 never produced
+FP16_MAX = 65504.0       # largest finite fp16, used when the scale overflows
+
+
+# --------------------------------------------------------------------------
+# KV-cache size ([P3] section 2.3 formula and its symbol table)
+# --------------------------------------------------------------------------
+def kv_cache_bytes(num_layers, batch, seq_len, num_kv_heads, head_dim,
+                   bytes_per_elem):
+    """Closed form 2 * L * B * T * H_kv * d_h * bytes ([P3] section 2.3)."""
+    return 2 * num_layers * batch * seq_len * num_kv_heads * head_dim * bytes_per_elem
+
+
+def paged_cache_bytes(num_blocks, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
+    """Bytes held by one layer of the paged INT8 cache: K and V codes
+    (1 byte each) plus one fp16 scale per (token slot, KV head) for K and V."""
+    slots = num_blocks * block_size * num_kv_heads
+    return 2 * slots * head_dim * 1 + 2 * slots * 2
+
+
+def alloc_paged_cache(num_blocks, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
+    """Zeroed cache arrays in the layout the library uses:
+    codes [NB, Hkv, block_size, d] int8 and scales [NB, Hkv, block_size]
+    fp16, for K and for V."""
+    kc = np.zeros((num_blocks, num_kv_heads, block_size, head_dim), np.int8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((num_blocks, num_kv_heads, block_size), np.float16)
+    vs = np.zeros_like(ks)
+    return kc, vc, ks, vs
+
+
+# --------------------------------------------------------------------------
+# Per-token INT8 quantiser ([P1] main features; readings 1-4 above)
+# --------------------------------------------------------------------------
+def row_scale(x):
+    """fp16 scale of each row of x (last axis = channels of one token and
+    head): absmax / 127, rounded to fp32 then to fp16 (round to nearest
+    even, gradual underflow), saturated to 65504 on overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)   # exact: inputs are bf16
+    s32 = a / np.float32(QMAX)                            # IEEE fp32 divide, RNE
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)                      # RNE, subnormals kept
+    return np.where(np.isinf(s16), np.float16(FP16_MAX), s16).astype(np.float16)
+
+
+def codes_for_scale(x, s):
+    """INT8 codes of x (rows along the last axis) under fp16 scales s (one
+    per row): fp32 quotient, round half to even, clamp to [-127, 127];
+    rows whose scale is zero give all-zero codes."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 / np.where(zero, np.float32(1), s32)   # IEEE fp32 divide
+    q = np.rint(quot.astype(np.float64))                  # half to even
+    q = np.clip(q, -QMAX, QMAX)
+    q = np.where(zero, 0.0, q)
+    return q.astype(np.int8)
+
+
+def quantize_rows(x):
+    """Quantise each row of x (shape [..., d]) to (codes int8 [..., d],
+    scales fp16 [...])."""
+    s = row_scale(x)
+    return codes_for_scale(x, s), s
+
+
+def dequantize_rows(codes, scales):
+    """x_hat = code * scale, exact in fp64."""
+    return codes.astype(np.float64) * np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
+# Append: quantise new tokens and scatter them into the paged cache
+# ([P1] main features: quantised as they are written; [P3] section 4.2)
+# --------------------------------------------------------------------------
+def slot_to_block(slot, block_size=BLOCK_SIZE):
+    """Physical slot -> (physical block, offset inside the block)."""
+    return slot // block_size, slot % block_size
+
+
+def quant_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                 block_size=BLOCK_SIZE):
+    """k_new, v_new: [N, Hkv, d] bf16 values (as float arrays); slot_mapping
+    [N] int, negative entries are skipped.  Writes codes and scales in place
+    and returns nothing.  Repeated slots are the caller's error."""
+    kc, ks = quantize_rows(k_new)
+    vc, vs = quantize_rows(v_new)
+    for n, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        blk, off = slot_to_block(slot, block_size)
+        k_cache[blk, :, off, :] = kc[n]
+        v_cache[blk, :, off, :] = vc[n]
+        k_scale[blk, :, off] = ks[n]
+        v_scale[blk, :, off] = vs[n]
+
+
+# --------------------------------------------------------------------------
+# Paged attention ([P3] sections 2.1, 3.3, 4.2)
+# --------------------------------------------------------------------------
+def kv_head_of(h, group):
+    """Query head h reads KV head h // G (contiguous grouping)."""
+    return h // group
+
+
+def logical_to_physical(block_table_row, t, block_size=BLOCK_SIZE):
+    """Logical token t -> (physical block id, slot in block)."""
+    return block_table_row[t // block_size], t % block_size
+
+
+def gather_dequant(codes, scales, block_table_row, ctx, kv_head,
+                   block_size=BLOCK_SIZE):
+    """Dequantised [ctx, d] fp64 matrix of one sequence and one KV head,
+    read through the block table."""
+    t = np.arange(ctx)
+    blk, off = logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return dequantize_rows(codes[blk, kv_head, off, :], scales[blk, kv_head, off])
+
+
+def softmax_attention(q_rows, k, v, sm_scale, visible=None):
+    """softmax(q k^T * sm_scale) v in fp64 with the max subtracted first.
+    visible: optional boolean [rows, T] mask of the keys each row may see."""
+    scores = (q_rows @ k.T) * sm_scale
+    if visible is not None:
+        scores = np.where(visible, scores, -np.inf)
+    m = np.max(scores, axis=-1, keepdims=True)
+    p = np.exp(scores - m)
+    return (p @ v) / np.sum(p, axis=-1, keepdims=True)
+
+
+def paged_decode(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                 sm_scale=None, block_size=BLOCK_SIZE):
+    """One query token per sequence.  q [B, Hq, d]; returns fp64 [B, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        if ctx <= 0:
+            continue
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[b, h] = softmax_attention(q[b, h][None, :], k, v, sm_scale)[0]
+    return out
+
+
+def causal_visibility(ctx, lc):
+    """[lc, ctx] mask: row i (absolute position ctx - lc + i) sees keys at
+    positions 0 .. ctx - lc + i inclusive."""
+    pos = ctx - lc + np.arange(lc)
+    return np.arange(ctx)[None, :] <= pos[:, None]
+
+
+def paged_prefill_chunk(q, q_start_loc, k_cache, v_cache, k_scale, v_scale,
+                        block_table, context_lens, sm_scale=None,
+                        block_size=BLOCK_SIZE):
+    """Causal chunk attention over a paged cache that already holds the
+    chunk's own K/V.  q [Tq, Hq, d] with sequence b's rows at
+    q_start_loc[b] .. q_start_loc[b+1]-1; context_lens[b] counts every token
+    of sequence b, chunk included.  Returns fp64 [Tq, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    Tq, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((Tq, Hq, d), np.float64)
+    B = len(context_lens)
+    for b in range(B):
+        r0, r1 = int(q_start_loc[b]), int(q_start_loc[b + 1])
+        lc = r1 - r0
+        ctx = int(context_lens[b])
+        if lc <= 0 or ctx <= 0:
+            continue
+        visible = causal_visibility(ctx, lc)
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[r0:r1, h] = softmax_attention(q[r0:r1, h], k, v, sm_scale, visible)
+    return out

@@ -1,0 +1,153 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant swaps one oracle helper for a copy carrying one plausible slip
+(a wrong index, a dropped term, a transposed operand, a wrong rounding or
+clamp).  The pin battery from test_oracle_pins must then fail.  CPU only;
+the mutation lives in the oracle process, never on a GPU.
+"""
+import numpy as np
+import pytest
+
+import tests.test_oracle_pins as P
+from oracle import kv8_oracle as O
+
+
+def _battery():
+    """Run the pins, cheapest first; return the name of the first failing
+    one, or None if all pass."""
+    checks = [
+        ("ties_clamp", P.test_quantiser_ties_to_even_and_clamp),
+        ("invariants", P.test_quantiser_invariants),
+        ("append", P.test_append_scatter_and_skip),
+        ("brute_force", P.test_decode_brute_force_tiny),
+        ("closed_forms", P.test_decode_closed_forms),
+        ("dominant_key", P.test_decode_dominant_key_large_logits),
+        ("sdpa_gqa", lambda: P.test_decode_matches_sdpa_fp64(
+            lambda: P.W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=32,
+                                        context_lens=[1, 17, 300], q_dtype="bf16",
+                                        k_outliers=True, seed=4))),
+        ("prefill_causal", P.test_prefill_no_context_equals_sdpa_causal),
+        ("prefill_ctx", P.test_prefill_with_context_equals_sdpa_masked_and_locality),
+        ("page_example", P.test_block_table_example_from_page),
+        ("scale_exhaustive", P.test_scale_exhaustive_all_bf16_absmax),
+        ("kv_size", P.test_kv_size_printed_tables),
+    ]
+    for name, fn in checks:
+        try:
+            fn()
+        except Exception:          # an assertion or a numerical blow-up
+            return name
+    return None
+
+
+def _softmax_no_scale(q_rows, k, v, sm_scale, visible=None):
+    scores = q_rows @ k.T
+    if visible is not None:
+        scores = np.where(visible, scores, -np.inf)
+    m = np.max(scores, axis=-1, keepdims=True)
+    p = np.exp(scores - m)
+    return (p @ v) / np.sum(p, axis=-1, keepdims=True)
+
+
+def _softmax_no_max(q_rows, k, v, sm_scale, visible=None):
+    scores = (q_rows @ k.T) * sm_scale
+    if visible is not None:
+        scores = np.where(visible, scores, -np.inf)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp(scores)
+        return (p @ v) / np.sum(p, axis=-1, keepdims=True)
+
+
+def _softmax_transposed_v(q_rows, k, v, sm_scale, visible=None):
+    scores = (q_rows @ k.T) * sm_scale
+    if visible is not None:
+        scores = np.where(visible, scores, -np.inf)
+    m = np.max(scores, axis=-1, keepdims=True)
+    p = np.exp(scores - m)
+    w = p / np.sum(p, axis=-1, keepdims=True)
+    return (w @ k)          # multiplies by K instead of V
+
+
+def _row_scale_128(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = (a / np.float32(128)).astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
+def _row_scale_mean(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.mean(np.abs(x), axis=-1).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = (a / np.float32(127)).astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
+def _codes_half_away(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = (x32 / np.where(zero, np.float32(1), s32)).astype(np.float64)
+    q = np.sign(quot) * np.floor(np.abs(quot) + 0.5)
+    q = np.where(zero, 0.0, np.clip(q, -127, 127))
+    return q.astype(np.int8)
+
+
+def _codes_clamp_128(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = (x32 / np.where(zero, np.float32(1), s32)).astype(np.float64)
+    q = np.where(zero, 0.0, np.clip(np.rint(quot), -128, 127))
+    return q.astype(np.int8)
+
+
+def _codes_truncate(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = (x32 / np.where(zero, np.float32(1), s32)).astype(np.float64)
+    q = np.where(zero, 0.0, np.clip(np.trunc(quot), -127, 127))
+    return q.astype(np.int8)
+
+
+def _dequant_sign_flip(codes, scales):
+    return -codes.astype(np.float64) * np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+MUTANTS = {
+    "head_map_mod": ("kv_head_of", lambda h, group: h % group),
+    "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
+    "page_identity": ("logical_to_physical", lambda row, t, bs=16: (t // bs, t % bs)),
+    "slot_swapped": ("slot_to_block", lambda slot, bs=16: (slot % bs, slot // bs)),
+    "softmax_no_scale": ("softmax_attention", _softmax_no_scale),
+    "softmax_no_max": ("softmax_attention", _softmax_no_max),
+    "softmax_times_k": ("softmax_attention", _softmax_transposed_v),
+    "scale_div_128": ("row_scale", _row_scale_128),
+    "scale_mean": ("row_scale", _row_scale_mean),
+    "codes_half_away": ("codes_for_scale", _codes_half_away),
+    "codes_clamp_128": ("codes_for_scale", _codes_clamp_128),
+    "codes_truncate": ("codes_for_scale", _codes_truncate),
+    "dequant_sign": ("dequantize_rows", _dequant_sign_flip),
+    "causal_exclusive": ("causal_visibility",
+                         lambda ctx, lc: np.arange(ctx)[None, :] < (ctx - lc + np.arange(lc))[:, None]),
+    "causal_off_by_one": ("causal_visibility",
+                          lambda ctx, lc: np.arange(ctx)[None, :] <= (ctx - lc + 1 + np.arange(lc))[:, None]),
+    "kv_size_no_two": ("kv_cache_bytes", lambda L, B, T, H, d, nb: L * B * T * H * d * nb),
+}
+
+
+def test_unmutated_battery_passes():
+    assert _battery() is None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(O, attr, repl)
+    caught = _battery()
+    assert caught is not None, f"mutant {name} passed every pin"

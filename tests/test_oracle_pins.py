@@ -1,0 +1,443 @@
+"""Pins of the fp64 CPU oracle against what the pages and mathematics fix.
+
+CPU only.  None of these re-types the oracle's own formula: the quantiser is
+checked against exact rational / exact-residual rounding, attention against
+brute force on tiny inputs, against torch's scaled_dot_product_attention in
+fp64 (the dense, non-paged, MHA special case), against closed forms
+(single token, identical keys) and against invariants (block permutation,
+batch order, causal locality).  The KV-size closed form reproduces the
+numbers the survey page prints.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv8_oracle as O
+from paged_int8_kv_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers independent of the oracle
+# ---------------------------------------------------------------------------
+def all_finite_bf16(positive_only=False):
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = W.bf16_bits_to_f32(bits)
+    keep = np.isfinite(vals)
+    if positive_only:
+        keep &= vals > 0
+    return vals[keep]
+
+
+def fp16_rne_exact(r):
+    """Round a non-negative rational to fp16 (nearest even, subnormals),
+    returning math.inf on overflow.  Pure integer/rational arithmetic."""
+    if r == 0:
+        return 0.0
+    e = r.numerator.bit_length() - r.denominator.bit_length()
+    while Fraction(2) ** e > r:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= r:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -14) - 10)
+    k = round(r / quantum)          # Fraction.__round__ rounds half to even
+    val = k * quantum
+    if val > 65504:
+        return math.inf
+    return float(val)
+
+
+def exact_codes(x, s):
+    """round_half_even(x / s) clamped to +-127, decided by an exact residual
+    test in fp64 (every product and difference below is exact)."""
+    x = np.asarray(x, np.float64)
+    s = float(s)
+    if s == 0:
+        return np.zeros(x.shape, np.int64)
+    big = np.abs(x) > 200 * s
+    xs = np.where(big, 0.0, x)
+    k = np.floor(xs / s)
+    r = xs - k * s
+    k = np.where(r < 0, k - 1, k)
+    r = xs - k * s
+    k = np.where(r >= s, k + 1, k)
+    r = xs - k * s
+    up = (2 * r > s) | ((2 * r == s) & (np.mod(k, 2) == 1))
+    c = k + up
+    c = np.where(big, np.sign(x) * 127, c)
+    return np.clip(c, -127, 127).astype(np.int64)
+
+
+def quantize_reference_rows(rows):
+    """Quantise rows with the exact helpers above (scale from Fraction)."""
+    codes, scales = [], []
+    for row in rows:
+        a = max(abs(float(v)) for v in row)
+        s = fp16_rne_exact(Fraction(a) / 127)
+        if s == math.inf:
+            s = 65504.0
+        codes.append(exact_codes(row, s))
+        scales.append(s)
+    return np.array(codes), np.array(scales)
+
+
+def brute_attention(q, k, v, scale):
+    """Dense softmax attention of one query over rows of k/v, pure python."""
+    logits = [scale * sum(float(a) * float(b) for a, b in zip(q, kr)) for kr in k]
+    m = max(logits)
+    w = [math.exp(z - m) for z in logits]
+    tot = sum(w)
+    return [sum(wi * float(vr[i]) for wi, vr in zip(w, v)) / tot for i in range(len(q))]
+
+
+def build_cache(case):
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, case.num_kv_heads, case.head_dim)
+    O.quant_append(case.k, case.v, case.slot_mapping, kc, vc, ks, vs)
+    return kc, vc, ks, vs
+
+
+def dense_dequant(case, b, which):
+    """Contiguous dequantised [ctx, Hkv, d] of sequence b, quantised from the
+    source tokens in sequence order (no block table involved)."""
+    src = case.k if which == "k" else case.v
+    rows = src[case.token_seq == b]
+    codes, scales = O.quantize_rows(rows)
+    return O.dequantize_rows(codes, scales)
+
+
+# ---------------------------------------------------------------------------
+# KV-size closed form (survey page, sections 2.3 / 3.3 / 11.4)
+# ---------------------------------------------------------------------------
+def test_kv_size_printed_tables():
+    g = json.load(open(os.path.join(GOLDEN, "kv_size_tables.json")))
+    t = g["llama3_70b_fp16_by_length"]
+    for seq, printed in t["rows"]:
+        gib = O.kv_cache_bytes(t["num_layers"], t["batch"], seq, t["num_kv_heads"],
+                               t["head_dim"], t["bytes"]) / 1024 ** 3
+        assert f"{gib:.2f}" == printed
+    t = g["llama3_70b_8k_by_attention_type"]
+    for _, heads, printed in t["rows"]:
+        gib = O.kv_cache_bytes(t["num_layers"], t["batch"], t["seq_len"], heads,
+                               t["head_dim"], t["bytes"]) / 1024 ** 3
+        assert f"{gib:.2f}" == printed
+    t = g["llama3_8b_b16_t8k"]
+    for _, nbytes, printed in t["rows"]:
+        gib = O.kv_cache_bytes(t["num_layers"], t["batch"], t["seq_len"], t["num_kv_heads"],
+                               t["head_dim"], nbytes) / 1024 ** 3
+        assert f"{gib:.2f}" == printed
+
+
+@pytest.mark.parametrize("layers,batch,tokens,hkv,d", [(1, 1, 256, 1, 64), (2, 3, 4096, 8, 128)])
+def test_paged_allocation_matches_closed_form(layers, batch, tokens, hkv, d):
+    nb = batch * tokens // O.BLOCK_SIZE
+    arrays = O.alloc_paged_cache(nb, hkv, d)
+    code_bytes = layers * (arrays[0].nbytes + arrays[1].nbytes)
+    assert code_bytes == O.kv_cache_bytes(layers, batch, tokens, hkv, d, 1)
+    scale_bytes = layers * (arrays[2].nbytes + arrays[3].nbytes)
+    assert scale_bytes == O.kv_cache_bytes(layers, batch, tokens, hkv, 1, 2)
+    assert layers * O.paged_cache_bytes(nb, hkv, d) == code_bytes + scale_bytes
+
+
+# ---------------------------------------------------------------------------
+# Quantiser
+# ---------------------------------------------------------------------------
+def test_scale_exhaustive_all_bf16_absmax():
+    a = all_finite_bf16(positive_only=True)
+    got = O.row_scale(a[:, None]).astype(np.float64)
+    exp = []
+    for v in a.tolist():
+        s = fp16_rne_exact(Fraction(v) / 127)
+        exp.append(65504.0 if s == math.inf else s)
+    exp = np.array(exp)
+    assert np.array_equal(got, exp)
+    # the fp64-quotient reading gives the same scales on the whole bf16 domain
+    with np.errstate(over="ignore"):
+        s64 = (a.astype(np.float64) / 127.0).astype(np.float16)
+    s64 = np.where(np.isinf(s64), np.float16(65504), s64).astype(np.float64)
+    assert np.array_equal(got, s64)
+
+
+def test_scale_edges():
+    # smallest absmax whose scale is non-zero, saturation threshold
+    assert O.row_scale(np.array([[0.0, 0.0]]))[0] == 0
+    assert O.row_scale(np.array([[3.78e-6]]).astype(np.float32))[0] == 0
+    assert O.row_scale(np.array([[8257536.0]]))[0] == np.float16(65024)
+    assert O.row_scale(np.array([[8323072.0]]))[0] == np.float16(65504)
+
+
+SCALES = [1.0, 0.0234375, 0.5 + 2 ** -11, 6.103515625e-05, 2 ** -24, 3 * 2 ** -24,
+          1000 * 2 ** -24, 65504.0, 2.0 ** 10 * 1.5]
+
+
+@pytest.mark.parametrize("s", SCALES)
+def test_codes_exhaustive_all_bf16(s):
+    x = all_finite_bf16()
+    got = O.codes_for_scale(x[None, :], np.array([s], np.float16))[0].astype(np.int64)
+    assert np.array_equal(got, exact_codes(x, np.float16(s)))
+
+
+def test_codes_fraction_spot_check():
+    rng = np.random.default_rng(11)
+    x = all_finite_bf16()
+    pick = x[rng.choice(len(x), 3000, replace=False)]
+    for s in (0.0234375, 3 * 2 ** -24, 1.0):
+        got = O.codes_for_scale(pick[None, :], np.array([s], np.float16))[0]
+        for xv, c in zip(pick.tolist(), got.tolist()):
+            q = round(Fraction(xv) / Fraction(s))
+            assert c == max(-127, min(127, q))
+
+
+def test_quantize_rows_random_vs_exact():
+    rng = np.random.default_rng(5)
+    rows, _ = W.to_bf16(rng.standard_normal((300, 64)).astype(np.float32)
+                        * np.exp(rng.uniform(-18, 18, size=(300, 1))).astype(np.float32))
+    codes, scales = O.quantize_rows(rows)
+    rc, rs = quantize_reference_rows(rows)
+    assert np.array_equal(scales.astype(np.float64), rs)
+    assert np.array_equal(codes.astype(np.int64), rc)
+
+
+def test_quantiser_invariants():
+    rng = np.random.default_rng(7)
+    rows, _ = W.to_bf16(rng.standard_normal((500, 128)).astype(np.float32))
+    c, s = O.quantize_rows(rows)
+    cn, sn = O.quantize_rows(-rows)
+    assert np.array_equal(cn, -c) and np.array_equal(sn, s)
+    for k in (-3, 5):
+        c2, s2 = O.quantize_rows(rows * 2.0 ** k)
+        assert np.array_equal(c2, c)
+        assert np.array_equal(s2.astype(np.float64), s.astype(np.float64) * 2.0 ** k)
+    err = np.abs(rows - O.dequantize_rows(c, s))
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2)
+    am = np.argmax(np.abs(rows), axis=1)
+    assert np.all(np.abs(c[np.arange(500), am]) == 127)
+    assert c.min() >= -127
+
+
+def test_quantiser_ties_to_even_and_clamp():
+    row = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -1.5]])
+    c, s = O.quantize_rows(row)
+    assert s[0] == 1.0
+    assert c[0].tolist() == [127, 2, 4, -2, 0, 0, 2, -2]
+    # subnormal scale: the absmax element's quotient exceeds 127 -> clamped
+    row = np.array([[np.float32(1e-4), -np.float32(1e-4)]]).astype(np.float64)
+    row = W.to_bf16(row.astype(np.float32))[0]
+    c, s = O.quantize_rows(row)
+    assert 0 < s[0] < np.float16(6.103515625e-05)
+    assert c[0].tolist() == [127, -127]
+    assert row[0, 0] / float(s[0]) > 127.5
+
+
+# ---------------------------------------------------------------------------
+# Append (scatter through slot mapping)
+# ---------------------------------------------------------------------------
+def test_append_scatter_and_skip():
+    case = W.make_paged_case(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                             context_lens=[21, 40], seed=9)
+    slots = case.slot_mapping.copy()
+    slots[3] = -1
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, 2, 16)
+    O.quant_append(case.k, case.v, slots, kc, vc, ks, vs)
+    codes_k, sc_k = quantize_reference_rows(case.k.reshape(-1, 16))
+    codes_k = codes_k.reshape(case.k.shape)
+    sc_k = sc_k.reshape(case.k.shape[:2])
+    for n in range(len(slots)):
+        blk, off = divmod(int(case.slot_mapping[n]), 16)
+        if n == 3:
+            assert np.all(kc[blk, :, off] == 0) and np.all(ks[blk, :, off] == 0)
+            continue
+        assert np.array_equal(kc[blk, :, off].astype(np.int64), codes_k[n])
+        assert np.array_equal(ks[blk, :, off].astype(np.float64), sc_k[n])
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def test_decode_brute_force_tiny():
+    case = W.make_paged_case(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=8,
+                             context_lens=[5, 37], q_dtype="f32", seed=3)
+    kc, vc, ks, vs = build_cache(case)
+    out = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    for b in range(2):
+        K = dense_dequant(case, b, "k")
+        V = dense_dequant(case, b, "v")
+        for h in range(4):
+            g = h // 2
+            ref = brute_attention(case.q[b, h], K[:, g], V[:, g], 1 / math.sqrt(8))
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def sdpa_decode(case, kc, vc, ks, vs):
+    outs = []
+    for b in range(case.batch):
+        ctx = int(case.context_lens[b])
+        K = np.stack([O.gather_dequant(kc, ks, case.block_table[b], ctx, g)
+                      for g in range(case.num_kv_heads)])
+        V = np.stack([O.gather_dequant(vc, vs, case.block_table[b], ctx, g)
+                      for g in range(case.num_kv_heads)])
+        Kt = torch.from_numpy(K).repeat_interleave(case.group, dim=0)[None]
+        Vt = torch.from_numpy(V).repeat_interleave(case.group, dim=0)[None]
+        q = torch.from_numpy(case.q[b].astype(np.float64))[None, :, None, :]
+        outs.append(torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt)[0, :, 0].numpy())
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("maker", [
+    lambda: W.tiny_decode(),
+    lambda: W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=32,
+                              context_lens=[1, 17, 300], q_dtype="bf16", k_outliers=True, seed=4),
+    lambda: W.make_paged_case(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=16,
+                              context_lens=[33, 64], seed=5),       # MHA, G = 1
+    lambda: W.make_paged_case(batch=2, num_q_heads=6, num_kv_heads=1, head_dim=16,
+                              context_lens=[48, 7], seed=6),        # MQA, Hkv = 1
+])
+def test_decode_matches_sdpa_fp64(maker):
+    case = maker()
+    kc, vc, ks, vs = build_cache(case)
+    out = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    ref = sdpa_decode(case, kc, vc, ks, vs)
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_closed_forms():
+    case = W.make_paged_case(batch=3, num_q_heads=4, num_kv_heads=1, head_dim=16,
+                             context_lens=[1, 20, 0], seed=8)
+    kc, vc, ks, vs = build_cache(case)
+    out = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    # single token: exactly its dequantised V
+    v0 = O.gather_dequant(vc, vs, case.block_table[0], 1, 0)[0]
+    for h in range(4):
+        assert np.array_equal(out[0, h], v0)
+    # empty context: zeros
+    assert np.all(out[2] == 0)
+    # identical keys: mean of dequantised V; and q = 0 gives the same
+    blk = case.block_table[1]
+    for t in range(20):
+        b_, o_ = blk[t // 16], t % 16
+        kc[b_, 0, o_] = kc[blk[0], 0, 0]
+        ks[b_, 0, o_] = ks[blk[0], 0, 0]
+    out = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    vmean = O.gather_dequant(vc, vs, blk, 20, 0).mean(axis=0)
+    assert np.allclose(out[1], vmean[None, :], rtol=1e-13, atol=1e-14)
+    q0 = np.zeros_like(case.q)
+    out0 = O.paged_decode(q0, kc, vc, ks, vs, case.block_table, case.context_lens)
+    assert np.allclose(out0[1], vmean[None, :], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_dominant_key_large_logits():
+    # logits near 1e3: the max-subtracted softmax must still return the
+    # dominant token's V (an unstabilised exp overflows)
+    case = W.make_paged_case(batch=1, num_q_heads=2, num_kv_heads=1, head_dim=16,
+                             context_lens=[40], q_dtype="f32", seed=12)
+    kc, vc, ks, vs = build_cache(case)
+    t_star = 23
+    blk, off = case.block_table[0][t_star // 16], t_star % 16
+    kd = O.gather_dequant(kc, ks, case.block_table[0], 40, 0)
+    q = np.zeros_like(case.q)
+    q[0, :] = kd[t_star] * (4000.0 / np.dot(kd[t_star], kd[t_star]))
+    out = O.paged_decode(q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    v_star = O.dequantize_rows(vc[blk, 0, off][None], vs[blk, 0, off][None])[0]
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[0, 0], v_star, atol=1e-6)
+
+
+def test_block_permutation_and_batch_shuffle_invariance():
+    base = W.make_paged_case(batch=3, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                             context_lens=[50, 3, 97], seed=10, permute=False)
+    kc, vc, ks, vs = build_cache(base)
+    ref = O.paged_decode(base.q, kc, vc, ks, vs, base.block_table, base.context_lens)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(base.num_blocks)        # physical block p -> perm[p]
+    kc2, vc2, ks2, vs2 = (np.empty_like(a) for a in (kc, vc, ks, vs))
+    for src, dst in ((kc, kc2), (vc, vc2), (ks, ks2), (vs, vs2)):
+        dst[perm] = src
+    table2 = perm[base.block_table]
+    out = O.paged_decode(base.q, kc2, vc2, ks2, vs2, table2, base.context_lens)
+    assert np.array_equal(out, ref)
+    order = np.array([2, 0, 1])
+    out = O.paged_decode(base.q[order], kc, vc, ks, vs, base.block_table[order],
+                         base.context_lens[order])
+    assert np.array_equal(out, ref[order])
+
+
+def test_block_table_example_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "block_table_example.json")))
+    phys = g["request_a"]["physical"]
+    rng = np.random.default_rng(2)
+    rows, _ = W.to_bf16(rng.standard_normal((48, 1, 8)).astype(np.float32))
+    kc, vc, ks, vs = O.alloc_paged_cache(10, 1, 8)
+    slots = [phys[t // 16] * 16 + t % 16 for t in range(48)]
+    O.quant_append(rows, rows, slots, kc, vc, ks, vs)
+    # the free pool's blocks stay untouched
+    for p in g["free_pool_prefix"]:
+        assert np.all(kc[p] == 0)
+    got = O.gather_dequant(kc, ks, np.array(phys), 48, 0)
+    c, s = O.quantize_rows(rows[:, 0])
+    assert np.array_equal(got, O.dequantize_rows(c, s))
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill
+# ---------------------------------------------------------------------------
+def test_prefill_no_context_equals_sdpa_causal():
+    case = W.chunked_prefill(seed=21, batch=2, chunk=24, lo=0, hi=0,
+                             num_q_heads=4, num_kv_heads=2, head_dim=16)
+    kc, vc, ks, vs = build_cache(case)
+    qsl = case.extra["q_start_loc"]
+    out = O.paged_prefill_chunk(case.q, qsl, kc, vc, ks, vs, case.block_table, case.context_lens)
+    for b in range(2):
+        K = np.stack([O.gather_dequant(kc, ks, case.block_table[b], 24, g) for g in range(2)])
+        V = np.stack([O.gather_dequant(vc, vs, case.block_table[b], 24, g) for g in range(2)])
+        Kt = torch.from_numpy(K).repeat_interleave(2, dim=0)[None]
+        Vt = torch.from_numpy(V).repeat_interleave(2, dim=0)[None]
+        q = torch.from_numpy(case.q[qsl[b]:qsl[b + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt, is_causal=True)
+        assert np.allclose(out[qsl[b]:qsl[b + 1]], ref[0].permute(1, 0, 2).numpy(),
+                           rtol=1e-11, atol=1e-12)
+
+
+def test_prefill_with_context_equals_sdpa_masked_and_locality():
+    case = W.chunked_prefill(seed=22, batch=2, chunk=9, lo=20, hi=40,
+                             num_q_heads=4, num_kv_heads=1, head_dim=16)
+    kc, vc, ks, vs = build_cache(case)
+    qsl = case.extra["q_start_loc"]
+    out = O.paged_prefill_chunk(case.q, qsl, kc, vc, ks, vs, case.block_table, case.context_lens)
+    for b in range(2):
+        ctx = int(case.context_lens[b])
+        prev = ctx - 9
+        K = O.gather_dequant(kc, ks, case.block_table[b], ctx, 0)
+        V = O.gather_dequant(vc, vs, case.block_table[b], ctx, 0)
+        mask = np.arange(ctx)[None, :] <= (prev + np.arange(9))[:, None]
+        q = torch.from_numpy(case.q[qsl[b]:qsl[b + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None],
+            attn_mask=torch.from_numpy(mask))
+        assert np.allclose(out[qsl[b]:qsl[b + 1]], ref[0].permute(1, 0, 2).numpy(),
+                           rtol=1e-11, atol=1e-12)
+    # causal locality: changing the last token's K/V leaves earlier rows alone
+    b = 1
+    ctx = int(case.context_lens[b])
+    t = ctx - 1
+    blk, off = case.block_table[b][t // 16], t % 16
+    kc[blk, 0, off] = -kc[blk, 0, off]
+    vc[blk, 0, off] = 127
+    out2 = O.paged_prefill_chunk(case.q, qsl, kc, vc, ks, vs, case.block_table, case.context_lens)
+    r1 = qsl[b + 1]
+    assert np.array_equal(out2[:r1 - 1], out[:r1 - 1])
+    assert not np.allclose(out2[r1 - 1], out[r1 - 1])
+
+
+def test_prefill_single_row_equals_decode():
+    case = W.chunked_prefill(seed=23, batch=3, chunk=1, lo=5, hi=70,
+                             num_q_heads=8, num_kv_heads=2, head_dim=32)
+    kc, vc, ks, vs = build_cache(case)
+    out_p = O.paged_prefill_chunk(case.q, case.extra["q_start_loc"], kc, vc, ks, vs,
+                                  case.block_table, case.context_lens)
+    out_d = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    assert np.allclose(out_p, out_d, rtol=1e-13, atol=1e-14)
