@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged INT8-KV GQA hot path on one MI355X.
+
+One step = one decode step of a Llama-3.1-8B-shaped attention layer:
+kv8_quant_append writes the newest token of each of the 32 sequences into
+the INT8 cache, then paged_decode_attn_kv8 attends every sequence's whole
+context (1024..4096 tokens, 32 query / 8 KV heads, d = 128).  The cache is
+resident in HBM before timing starts; four replicas are rotated so that
+the 256 MB last-level cache cannot serve a replica from the previous step.
+
+Prints one JSON line: whole-step algorithmic HBM GB/s as `value`, KV
+tokens/s, the decode kernel's roofline fraction (HIP events on the stream
+the library launches on), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) + KV-tokens/s, paged INT8-KV GQA decode attention"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=4)
+    p.add_argument("--tokens-per-split", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-steps", type=int, default=4)
+    return p.parse_args()
+
+
+def decode_bytes(ctx, hkv, d, hq, q_bytes):
+    """Algorithmic bytes of one decode call: K and V codes plus their fp16
+    scales for every attended token and KV head, q, out, block-table entries
+    and context lengths."""
+    ctx = np.asarray(ctx, np.int64)
+    b = len(ctx)
+    kv = int(ctx.sum()) * 2 * hkv * (d + 2)
+    table = 4 * int(np.sum((ctx + 15) // 16))
+    return kv + b * hq * d * q_bytes + b * hq * d * 4 + table + 4 * b
+
+
+def append_bytes(n, hkv, d):
+    """Read bf16 K and V, write codes and scales, read slot indices."""
+    return n * hkv * d * 2 * 2 + n * hkv * (d + 2) * 2 + 4 * n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange; see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_int8_kv_amd import binding as B
+    from paged_int8_kv_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = W.llama8b_decode()
+    bsz, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    ctx = case.context_lens
+    max_ctx = int(ctx.max())
+
+    # newest token of every sequence: appended each step
+    last = np.cumsum(ctx) - 1
+    k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    slots_all = torch.from_numpy(case.slot_mapping).to(dev)
+    last_t = torch.from_numpy(last).to(dev)
+    k_new = k_all.index_select(0, last_t).contiguous()
+    v_new = v_all.index_select(0, last_t).contiguous()
+    slots_new = slots_all.index_select(0, last_t).contiguous()
+
+    caches = []
+    for _ in range(args.replicas):
+        c = B.alloc_cache(case.num_blocks, hkv, d, dev)
+        B.kv8_quant_append(k_all, v_all, slots_all, *c)
+        caches.append(c)
+    del k_all, v_all
+    q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    table = torch.from_numpy(case.block_table).to(dev)
+    lens = torch.from_numpy(ctx).to(dev)
+    out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx, args.tokens_per_split),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        if ev is not None:
+            ev[0].record()
+        B.kv8_quant_append(k_new, v_new, slots_new, *c)
+        if ev is not None:
+            ev[1].record()
+        B.paged_decode_attn_kv8(q, *c, table, lens, max_ctx, out, ws,
+                                tokens_per_split=args.tokens_per_split)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    step_ms = total_ms / args.steps
+    d_bytes = decode_bytes(ctx, hkv, d, hq, 2)
+    a_bytes = append_bytes(bsz, hkv, d)
+    step_gbs = (d_bytes + a_bytes) / (step_ms * 1e-3) / 1e9
+    dec_avg = float(dec_ms.mean())
+    dec_gbs = d_bytes / (dec_avg * 1e-3) / 1e9
+    kv_tok_s = float(ctx.sum()) / (step_ms * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3.1-8B-shaped decode layer: append 1 token/seq + paged INT8-KV "
+                        "GQA decode; B=32, Hq=32, Hkv=8, d=128, ctx~U[1024,4096], block 16",
+            "kv_dtype": "int8 codes + fp16 per-token scales",
+            "q_dtype": "bf16",
+            "sum_ctx": int(ctx.sum()),
+            "replicas_rotated": len(caches),
+            "tokens_per_split": args.tokens_per_split or "library default",
+        },
+        "pct_of_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(kv_tok_s, 1),
+        "decode_us": {"mean": round(dec_avg * 1e3, 2),
+                      "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                      "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 2),
+                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
+        "append_us": {"mean": round(float(app_ms.mean()) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_decode_attn_kv8 (split + merge launches)",
+                     "bytes_per_launch": d_bytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_steps, d_bytes + a_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, n_steps, step_bytes):
+    """The fp64 oracle on the host: the same step (append the newest token of
+    every sequence, then decode the whole batch), repeated n_steps times."""
+    from oracle import kv8_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, case.num_kv_heads, case.head_dim)
+    O.quant_append(case.k, case.v, case.slot_mapping, kc, vc, ks, vs)
+    last = np.cumsum(case.context_lens) - 1
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        O.quant_append(case.k[last], case.v[last], case.slot_mapping[last], kc, vc, ks, vs)
+        O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    dt = (time.perf_counter() - t0) / n_steps
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_step": round(dt, 3),
+            "kv_tokens_per_s": round(float(case.context_lens.sum()) / dt, 1),
+            "sample": f"{n_steps} full steps of the same workload (append 32 tokens + decode "
+                      f"all 32 sequences), numpy fp64 oracle"}
+
+
+if __name__ == "__main__":
+    main()

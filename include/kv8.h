@@ -1,0 +1,203 @@
+/*
+ * kv8.h - C ABI of the paged INT8-KV GQA attention library (libkv8.so),
+ * written for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * The attention layer keeps its K/V cache as INT8 codes obtained by dynamic
+ * per-token quantisation and restores them on demand inside attention
+ * ("KV-Cache 全栈优化系统" README, section 主要特性, item on low-bit linear
+ * and KV-cache compression).  Attention itself is softmax(Q K^T / sqrt(d)) V
+ * ("KV Cache 优化全景解析——从基础原理到工程实践", section 2.1 equation),
+ * grouped so that every group of G = Hq / Hkv query heads shares one KV head
+ * (same page, section 3.3), and the cache is paged: a per-sequence block
+ * table maps logical 16-token blocks to physical blocks (same page, section
+ * 4.2 and the 16/32-token blocks of section 6.3).
+ *
+ * Quantiser (per token n, KV head h, separately for K and V; x is bf16[d]):
+ *   a = max_i |x_i|;  s = fp16(fp32(a / 127)) rounded to nearest even with
+ *   gradual underflow, saturated to 65504 on overflow;
+ *   code_i = clamp(round_half_even(fp32(x_i / s)), -127, 127), or 0 if s == 0;
+ *   the restored value is code_i * s.
+ *
+ * Memory layout (all device memory, caller-owned)
+ * ------------------------------------------------
+ *   k_cache, v_cache : int8   [num_blocks, Hkv, 16, d]   codes of one
+ *                      (block, head) are 16*d contiguous bytes
+ *   k_scale, v_scale : uint16 [num_blocks, Hkv, 16]      fp16 bit patterns
+ *   block_table      : int32  [B, max_blocks_per_seq]    physical block ids
+ *   context_lens     : int32  [B]                        tokens to attend,
+ *                      including any token just appended
+ *   slot_mapping     : int32  [N]   physical slot = block * 16 + offset;
+ *                      a negative slot skips the token
+ *   bf16 / fp16 values are passed as their 16-bit patterns (uint16_t).
+ * Query head hq reads KV head hq / G.  Logical token t of sequence b lives
+ * in block block_table[b][t / 16] at offset t % 16.
+ *
+ * Conventions
+ * -----------
+ * - Ownership: the caller allocates every buffer, including the workspace;
+ *   the library allocates nothing and keeps no state between calls.
+ * - Ordering: each call validates its host arguments, enqueues its kernels
+ *   on `stream` (a hipStream_t; NULL = the default stream) and returns
+ *   without synchronising.
+ * - Errors: every call returns a kv8_status.  Host validation runs before
+ *   any HIP call and rejects null pointers, bad sizes, unsupported shapes,
+ *   misaligned pointers and short workspaces; nothing is launched then.  A
+ *   failed launch returns KV8_ERR_HIP.  No exception crosses the ABI and
+ *   the library never aborts.
+ * - Device data is not validated on the host.  Physical block ids outside
+ *   [0, num_blocks) are clamped into range, so they never fault but give an
+ *   undefined result.  context_lens values are clamped to
+ *   [0, min(max_context_len, 16 * max_blocks_per_seq)].  Non-finite K/V/Q
+ *   values give undefined results.  Slots at or beyond a sequence's context
+ *   length are never read into a result, whatever they hold.
+ * - Alignment: cache, scale, q, k_new/v_new and out base pointers must be
+ *   16-byte aligned.
+ * - Supported shapes: block_size == 16, d in {64, 128},
+ *   G = Hq / Hkv in {1, 2, 4, 8}.
+ */
+#ifndef KV8_H
+#define KV8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv8_status {
+  KV8_OK = 0,
+  KV8_ERR_NULL = -1,        /* a required pointer is NULL                  */
+  KV8_ERR_SHAPE = -2,       /* a size is negative, zero where it must not
+                               be, or inconsistent (Hq % Hkv != 0, ...)    */
+  KV8_ERR_UNSUPPORTED = -3, /* block_size != 16, d not in {64,128}, G not
+                               in {1,2,4,8}, unknown dtype                  */
+  KV8_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned       */
+  KV8_ERR_WORKSPACE = -5,   /* workspace missing or too small              */
+  KV8_ERR_HIP = -6          /* the HIP runtime reported a launch error     */
+} kv8_status;
+
+typedef enum kv8_dtype {
+  KV8_F32 = 0,              /* IEEE binary32                               */
+  KV8_BF16 = 1              /* bfloat16 bit patterns in uint16_t           */
+} kv8_dtype;
+
+#define KV8_BLOCK_SIZE 16
+
+/* Human-readable name of a kv8_status value (static string, never NULL). */
+const char* kv8_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int kv8_version(void);
+
+/*
+ * kv8_quant_append - quantise N new tokens' K and V and scatter them into
+ * the paged cache (the quantise-on-write half of the KV8 method: "KV-Cache
+ * 全栈优化系统" README, section 主要特性; slot addressing per the block
+ * table of "KV Cache 优化全景解析", section 4.2).
+ *
+ *   k_new, v_new   device bf16 [n_tokens, num_kv_heads, head_dim]
+ *   slot_mapping   device int32 [n_tokens]; slot = block*16 + offset;
+ *                  slot < 0 or slot >= 16*num_blocks skips the token
+ *   k_cache/v_cache/k_scale/v_scale  the cache (layout above); for every
+ *                  kept token n and head h the 16-byte-aligned code row and
+ *                  the fp16 scale of (slot, h) are overwritten
+ *   stream         hipStream_t
+ * Two tokens mapping to the same slot race (undefined which one wins).
+ * n_tokens == 0 is a no-op returning KV8_OK.
+ */
+int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* slot_mapping, int64_t n_tokens,
+                     int num_kv_heads, int head_dim, int block_size,
+                     int64_t num_blocks,
+                     int8_t* k_cache, int8_t* v_cache,
+                     uint16_t* k_scale, uint16_t* v_scale,
+                     void* stream);
+
+/*
+ * kv8_decode_workspace_size - bytes of workspace paged_decode_attn_kv8
+ * needs for these sizes.  tokens_per_split: tokens each workgroup covers
+ * (a multiple of 64 in [64, 2048]), or <= 0 for the library's choice,
+ * which depends on batch, num_kv_heads and max_context_len only.  Returns
+ * 0 for invalid sizes.
+ */
+size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int max_context_len,
+                                 int tokens_per_split);
+
+/*
+ * paged_decode_attn_kv8 - one query token per sequence attends to its
+ * whole paged INT8 context (decode).  For every sequence b and query head
+ * hq:  out[b,hq] = sum_t softmax_t(<q[b,hq], k_hat[b,g,t]> * sm_scale)
+ * v_hat[b,g,t], t = 0 .. ctx_b - 1, g = hq / G, k_hat/v_hat the restored
+ * codes ("KV Cache 优化全景解析", sections 2.1 and 3.3; dequantisation on
+ * the fly per the KV8 item of the "KV-Cache 全栈优化系统" README).  The
+ * softmax and all accumulation run in fp32 ("大模型推理加速：KV Cache与vLLM
+ * 技术解析", section 4.1).  Split-K: each workgroup covers up to
+ * tokens_per_split tokens of one (sequence, KV head) for all G query heads
+ * and a second kernel merges the partial results by log-sum-exp.
+ *
+ *   q             device [B, Hq, d], dtype q_dtype (KV8_F32 or KV8_BF16)
+ *   block_table   device int32 [B, max_blocks_per_seq]
+ *   context_lens  device int32 [B]; ctx_b == 0 gives out[b] = 0
+ *   max_context_len  host-side upper bound of context_lens (sizes the
+ *                 split grid; larger device values are clamped to it)
+ *   sm_scale      softmax scale, normally 1/sqrt(d)
+ *   out           device fp32 [B, Hq, d]
+ *   workspace     device scratch of at least kv8_decode_workspace_size()
+ *                 bytes (16-byte aligned); contents need no initialisation
+ *   tokens_per_split  as for kv8_decode_workspace_size (same value!)
+ * Same inputs and same tokens_per_split give bitwise-identical output.
+ */
+int paged_decode_attn_kv8(const void* q, int q_dtype,
+                          const int8_t* k_cache, const int8_t* v_cache,
+                          const uint16_t* k_scale, const uint16_t* v_scale,
+                          int64_t num_blocks,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* context_lens, int max_context_len,
+                          int batch, int num_q_heads, int num_kv_heads,
+                          int head_dim, int block_size, float sm_scale,
+                          float* out, void* workspace, size_t workspace_bytes,
+                          int tokens_per_split, void* stream);
+
+/*
+ * paged_prefill_chunk_attn_kv8 - causal attention of a chunk of query rows
+ * per sequence over the paged INT8 cache that already holds the chunk's own
+ * K/V (append first with kv8_quant_append).  Chunked prefill as in the
+ * vLLM chunked-prefill option ("KV Cache 优化全景解析", section 11.2) with
+ * the attention of section 2.1 and the KV8 cache of the "KV-Cache 全栈优化
+ * 系统" README.  Row i of sequence b's chunk (Lc_b = q_start_loc[b+1] -
+ * q_start_loc[b] rows) sits at absolute position p = ctx_b - Lc_b + i and
+ * attends to keys 0 .. p inclusive.  QK^T and PV run on the matrix cores.
+ *
+ *   q             device bf16 [total_q, Hq, d]
+ *   q_start_loc   device int32 [B + 1], q_start_loc[0] == 0, non-decreasing,
+ *                 q_start_loc[B] == total_q
+ *   max_q_len     host-side upper bound of every Lc_b (sizes the grid)
+ *   context_lens  device int32 [B], counts the chunk's tokens too; must be
+ *                 >= Lc_b (rows of a sequence violating this are undefined)
+ *   out           device fp32 [total_q, Hq, d]
+ *   workspace     may be NULL when kv8_prefill_workspace_size() returns 0
+ */
+size_t kv8_prefill_workspace_size(int batch, int num_q_heads, int head_dim,
+                                  int max_q_len, int max_context_len);
+
+int paged_prefill_chunk_attn_kv8(const uint16_t* q, const int32_t* q_start_loc,
+                                 int64_t total_q, int max_q_len,
+                                 const int8_t* k_cache, const int8_t* v_cache,
+                                 const uint16_t* k_scale, const uint16_t* v_scale,
+                                 int64_t num_blocks,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len,
+                                 int batch, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, float sm_scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KV8_H */

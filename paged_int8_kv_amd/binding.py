@@ -1,0 +1,170 @@
+"""ctypes binding of libkv8.so (the C ABI in include/kv8.h).
+
+Argument marshalling only: torch tensors give device pointers and the
+current HIP stream; every step of the computation runs in the library's
+kernels.  The library must have been built (python -m
+paged_int8_kv_amd.build); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+KV8_OK = 0
+KV8_ERR_NULL = -1
+KV8_ERR_SHAPE = -2
+KV8_ERR_UNSUPPORTED = -3
+KV8_ERR_ALIGN = -4
+KV8_ERR_WORKSPACE = -5
+KV8_ERR_HIP = -6
+KV8_F32 = 0
+KV8_BF16 = 1
+BLOCK_SIZE = 16
+
+EXPORTED = (
+    "kv8_status_string", "kv8_version", "kv8_quant_append", "kv8_decode_workspace_size",
+    "paged_decode_attn_kv8", "kv8_prefill_workspace_size", "paged_prefill_chunk_attn_kv8",
+)
+
+_lib = None
+
+
+class Kv8Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def lib_path():
+    return _build.LIB_PATH
+
+
+def load():
+    """Load libkv8.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkv8.so not built at {path}; run python -m paged_int8_kv_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.kv8_status_string.restype = ctypes.c_char_p
+    lib.kv8_status_string.argtypes = [i32]
+    lib.kv8_version.restype = i32
+    lib.kv8_version.argtypes = []
+    lib.kv8_quant_append.restype = i32
+    lib.kv8_quant_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.kv8_decode_workspace_size.restype = sz
+    lib.kv8_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_decode_attn_kv8.restype = i32
+    lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
+                                          i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
+    lib.kv8_prefill_workspace_size.restype = sz
+    lib.kv8_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.paged_prefill_chunk_attn_kv8.restype = i32
+    lib.paged_prefill_chunk_attn_kv8.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp, i64, vp,
+                                                 i32, vp, i32, i32, i32, i32, i32, i32, f32,
+                                                 vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().kv8_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != KV8_OK:
+        raise Kv8Error(status, where)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (same names as the C entry points)
+# ---------------------------------------------------------------------------
+def kv8_quant_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                     stream=None):
+    """k_new/v_new: bf16 [N, Hkv, d]; slot_mapping int32 [N]; caches as in
+    include/kv8.h.  Enqueues on the current (or given) stream."""
+    n, hkv, d = k_new.shape
+    nb = k_cache.shape[0]
+    st = load().kv8_quant_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n, hkv, d,
+                                 BLOCK_SIZE, nb, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                 _ptr(v_scale), _stream(stream))
+    _check(st, "kv8_quant_append")
+
+
+def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                              tokens_per_split=0):
+    return int(load().kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, tokens_per_split))
+
+
+def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                          max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
+                          stream=None):
+    """q: fp32 or bf16 [B, Hq, d]; out fp32 [B, Hq, d]; workspace uint8 of at
+    least kv8_decode_workspace_size() bytes."""
+    import torch
+    b, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    dt = KV8_BF16 if q.dtype == torch.bfloat16 else KV8_F32
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    st = load().paged_decode_attn_kv8(
+        _ptr(q), dt, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nb,
+        _ptr(block_table), block_table.shape[1], _ptr(context_lens), int(max_context_len),
+        b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        int(tokens_per_split), _stream(stream))
+    _check(st, "paged_decode_attn_kv8")
+
+
+def kv8_prefill_workspace_size(batch, num_q_heads, head_dim, max_q_len, max_context_len):
+    return int(load().kv8_prefill_workspace_size(batch, num_q_heads, head_dim, max_q_len,
+                                                 max_context_len))
+
+
+def paged_prefill_chunk_attn_kv8(q, q_start_loc, max_q_len, k_cache, v_cache, k_scale, v_scale,
+                                 block_table, context_lens, max_context_len, out,
+                                 workspace=None, sm_scale=None, stream=None):
+    """q: bf16 [total_q, Hq, d]; q_start_loc int32 [B+1]; out fp32
+    [total_q, Hq, d]."""
+    tq, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    b = context_lens.shape[0]
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    st = load().paged_prefill_chunk_attn_kv8(
+        _ptr(q), _ptr(q_start_loc), tq, int(max_q_len), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), nb, _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), int(max_context_len), b, hq, hkv, d, BLOCK_SIZE, float(sm_scale),
+        _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check(st, "paged_prefill_chunk_attn_kv8")
+
+
+def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda"):
+    """Zeroed paged cache tensors: codes int8 [NB, Hkv, 16, d] and fp16
+    scales [NB, Hkv, 16] (stored as int16 bit patterns), for K and V."""
+    import torch
+    kc = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), dtype=torch.int8,
+                     device=device)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.int16, device=device)
+    vs = torch.zeros_like(ks)
+    return kc, vc, ks, vs

@@ -1,0 +1,130 @@
+// kv8_quant_append kernel: per-token, per-KV-head INT8 quantisation of new
+// K/V rows and their scatter into 16-token physical blocks.
+//
+// The method keeps K/V as INT8 produced by dynamic per-token quantisation
+// ("KV-Cache 全栈优化系统" README, section 主要特性); slots address physical
+// blocks through the block table ("KV Cache 优化全景解析", section 4.2).
+//
+// Work mapping: one row = (token n, KV head h) of length d.  LPR = d / 8
+// lanes share a row, each lane holding 8 bf16 values (one 16-byte load) of
+// K and the same 8 of V.  The absmax is reduced across the LPR lanes with
+// DPP; the fp32 scale is divided with IEEE-correct division (hipcc's
+// default), rounded to fp16 (round-to-nearest-even, subnormals kept) and
+// saturated to 65504; codes use IEEE division, v_rndne (ties to even) and a
+// symmetric clamp.  Each lane stores its 8 codes (8 bytes) so that the LPR
+// lanes write one contiguous d-byte row of the block.
+#include "kv8_device.h"
+#include "kv8_launch.h"
+
+namespace kv8 {
+
+namespace {
+
+template <int LPR>
+__device__ __forceinline__ float row_absmax(float a) {
+  static_assert(LPR == 8 || LPR == 16, "row of 64 or 128 channels");
+  if constexpr (LPR == 8) return group8_max(a);
+  else return group16_max(a);
+}
+
+__device__ __forceinline__ float fp16_scale(float absmax) {
+  const float s32 = absmax / 127.0f;                 // IEEE divide, RNE
+  _Float16 s16 = (_Float16)s32;                       // RNE, gradual underflow
+  if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+  return (float)s16;
+}
+
+__device__ __forceinline__ uint32_t code_byte(float x, float s) {
+  float q = __builtin_rintf(x / s);                   // IEEE divide, ties to even
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (uint32_t)((int32_t)q) & 0xFFu;
+}
+
+__device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
+  uint32_t w0 = 0, w1 = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w0 |= code_byte(x[i], s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w1 |= code_byte(x[4 + i], s) << (8 * i);
+  }
+  return make_uint2(w0, w1);
+}
+
+__device__ __forceinline__ void unpack8(uint4 raw, float (&x)[8], float& amax) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quant_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slot_mapping, int64_t n_rows, int num_kv_heads,
+    int64_t num_slots, int8_t* __restrict__ k_cache, int8_t* __restrict__ v_cache,
+    uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale) {
+  constexpr int LPR = D / 8;
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gtid / LPR;          // (token, head) row
+  const int part = (int)(gtid % LPR);      // which 8 channels
+  if (row >= n_rows) return;               // whole rows exit together
+  const int64_t n = row / num_kv_heads;
+  const int h = (int)(row % num_kv_heads);
+  const int64_t slot = slot_mapping[n];
+  const bool keep = slot >= 0 && slot < num_slots;
+
+  const uint4 kraw = *reinterpret_cast<const uint4*>(k_new + row * D + part * 8);
+  const uint4 vraw = *reinterpret_cast<const uint4*>(v_new + row * D + part * 8);
+  float kx[8], vx[8], ka, va;
+  unpack8(kraw, kx, ka);
+  unpack8(vraw, vx, va);
+  // Every lane of the row takes part in the reductions (rows never straddle
+  // an exit), so the DPP partners are always active.
+  ka = row_absmax<LPR>(ka);
+  va = row_absmax<LPR>(va);
+  if (!keep) return;
+
+  const float ks = fp16_scale(ka);
+  const float vs = fp16_scale(va);
+  const uint2 kc = quantise8(kx, ks);
+  const uint2 vc = quantise8(vx, vs);
+
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot % kBlock);
+  const int64_t line = (blk * num_kv_heads + h) * kBlock + off;   // (block, head, slot)
+  *reinterpret_cast<uint2*>(k_cache + line * D + part * 8) = kc;
+  *reinterpret_cast<uint2*>(v_cache + line * D + part * 8) = vc;
+  if (part == 0) {
+    k_scale[line] = __builtin_bit_cast(uint16_t, (_Float16)ks);
+    v_scale[line] = __builtin_bit_cast(uint16_t, (_Float16)vs);
+  }
+}
+
+}  // namespace
+
+int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                        const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                        int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
+                        uint16_t* k_scale, uint16_t* v_scale, hipStream_t stream) {
+  const int64_t n_rows = n_tokens * num_kv_heads;
+  const int64_t threads = n_rows * (head_dim / 8);
+  const int64_t grid = (threads + 255) / 256;
+  const int64_t num_slots = num_blocks * kBlock;
+  if (head_dim == 128) {
+    quant_append_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
+        k_scale, v_scale);
+  } else {
+    quant_append_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
+        k_scale, v_scale);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace kv8

@@ -1,0 +1,135 @@
+// Device-side helpers shared by the gfx950 kernels of libkv8.
+//
+// Cross-lane primitives (DPP, permlane swaps), byte permutes and the
+// int8 -> fp16 conversion used by the attention kernels.  Nothing here is
+// used outside the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kv8 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;          // tokens per physical block
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// DPP lane exchanges inside a 64-lane wave.  Control codes follow the GCN /
+// CDNA DPP encoding: quad_perm(a,b,c,d) = a | b<<2 | c<<4 | d<<6,
+// row_ror:n = 0x120 + n, row_mirror = 0x140, row_half_mirror = 0x141.
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadXor1 = 0xB1,       // [1,0,3,2]
+  kDppQuadXor2 = 0x4E,       // [2,3,0,1]
+  kDppHalfMirror = 0x141,    // lane i <-> 7-i inside each group of 8
+  kDppRowMirror = 0x140,     // lane i <-> 15-i inside each row of 16
+  kDppRowRor8 = 0x128,       // lane i <- (i+8) mod 16 inside each row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum / max over aligned groups of 8 consecutive lanes; every lane of the
+// group receives the result.  After the two quad steps all four lanes of a
+// quad agree, so the half-mirror step adds the two quads of the group.
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float group16_max(float x) {
+  x = group8_max(x);
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  return x;
+}
+
+// Row swaps: v_permlane16_swap exchanges rows 1,3 of its first operand with
+// rows 0,2 of its second; v_permlane32_swap exchanges the upper half of the
+// first with the lower half of the second.  Called with two copies of x,
+// the two results hold x of the partner rows / halves.  Written as inline
+// asm with both operands read-write: through the builtin, the compiler
+// used the first result twice when the two results were added.  The
+// leading s_nop covers the VALU-write -> permlane-read wait states.
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  float u = x, v = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+  a = u;
+  b = v;
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  float u = x, v = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+  a = u;
+  b = v;
+}
+
+// Sum of the eight lanes {l, l^8, l^16, ..., l^56} (same position inside
+// every group of 8); every lane receives the sum of its class.
+__device__ __forceinline__ float across_groups_sum(float x) {
+  float a, b;
+  x += dpp_f<kDppRowRor8>(x);
+  swap16(x, a, b);
+  x = a + b;
+  swap32(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float across_groups_max(float x) {
+  float a, b;
+  x = fmaxf(x, dpp_f<kDppRowRor8>(x));
+  swap16(x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+
+// ---------------------------------------------------------------------------
+// int8 codes -> fp16 pairs without a convert instruction per code.
+// A code c becomes the byte u = c + 128 (xor 0x80); placing u under the fp16
+// high byte 0x64 gives the fp16 value 1024 + u = c + 1152 exactly.  Dot
+// products therefore carry a bias of 1152 * (sum of the other operand),
+// which the kernels subtract once per token or per output.
+// v_perm_b32 selector bytes 0-3 pick bytes of the second operand, 4-7
+// bytes of the first.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kXor80 = 0x80808080u;
+constexpr uint32_t kHi64 = 0x64646464u;
+constexpr float kCodeBias = 1152.0f;
+
+__device__ __forceinline__ half2_t biased_pair_lo(uint32_t u) {   // bytes 0,1
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(kHi64, u, 0x04010400u));
+}
+__device__ __forceinline__ half2_t biased_pair_hi(uint32_t u) {   // bytes 2,3
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(kHi64, u, 0x04030402u));
+}
+// Interleave bytes k, k+1 of two words: [a.k, b.k, a.k+1, b.k+1].
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05010400u);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07030602u);
+}
+
+__device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+}  // namespace kv8

@@ -1,0 +1,43 @@
+// Internal launchers of libkv8: called by the C ABI layer (kv8_api.cpp)
+// after host validation.  Each returns 0 on success and -1 when the HIP
+// runtime reports a launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kv8 {
+
+int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                        const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                        int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
+                        uint16_t* k_scale, uint16_t* v_scale, hipStream_t stream);
+
+struct DecodePlan {
+  int split_tokens;   // tokens per workgroup (multiple of 64)
+  int n_split;        // workgroups per (sequence, KV head)
+  size_t o_bytes;     // partial outputs  fp32 [B, Hq, n_split, d]
+  size_t lse_bytes;   // partial log2-sum-exp fp32 [B, Hq, n_split]
+  size_t total_bytes;
+};
+
+// Split plan shared by the workspace query and the launch.
+bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                 int max_context_len, int tokens_per_split, DecodePlan* plan);
+
+int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t* v_cache,
+                  const uint16_t* k_scale, const uint16_t* v_scale, int64_t num_blocks,
+                  const int32_t* block_table, int max_blocks_per_seq,
+                  const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
+                  int num_kv_heads, int head_dim, float sm_scale, float* out,
+                  void* workspace, const DecodePlan& plan, hipStream_t stream);
+
+int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_q, int max_q_len,
+                   const int8_t* k_cache, const int8_t* v_cache, const uint16_t* k_scale,
+                   const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,
+                   int max_blocks_per_seq, const int32_t* context_lens, int ctx_cap, int batch,
+                   int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
+                   hipStream_t stream);
+
+}  // namespace kv8

@@ -1,0 +1,98 @@
+"""Shared helpers of the GPU parity tests: moving seeded cases to the
+device, building caches on either side, and the tolerance check."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv8_oracle as O
+from paged_int8_kv_amd import binding as B
+
+# Attention tolerance: max |delta| <= 2e-3 and ||delta||_2 / ||ref||_2 <= 1e-3,
+# evaluated in fp32 against the fp64 oracle on the same dequantised cache.
+MAX_ABS = 2e-3
+REL_L2 = 1e-3
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bits_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev())
+
+
+def f16_to_i16(a):
+    return np.ascontiguousarray(np.asarray(a, np.float16)).view(np.int16)
+
+
+def oracle_cache(case):
+    """Cache built by the oracle's quantiser (host arrays)."""
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, case.num_kv_heads, case.head_dim)
+    O.quant_append(case.k, case.v, case.slot_mapping, kc, vc, ks, vs)
+    return kc, vc, ks, vs
+
+
+def upload_cache(kc, vc, ks, vs):
+    return (torch.from_numpy(kc).to(dev()), torch.from_numpy(vc).to(dev()),
+            torch.from_numpy(f16_to_i16(ks)).to(dev()), torch.from_numpy(f16_to_i16(vs)).to(dev()))
+
+
+def download_cache(t):
+    kc, vc, ks, vs = (x.cpu().numpy() for x in t)
+    return kc, vc, ks.view(np.float16), vs.view(np.float16)
+
+
+def gpu_append(case, cache=None, slots=None, k_bits=None, v_bits=None):
+    """Run the library's append on the case's K/V (bf16 bits) into `cache`
+    (allocated zeroed if None); returns the device cache tuple."""
+    if cache is None:
+        cache = B.alloc_cache(case.num_blocks, case.num_kv_heads, case.head_dim, dev())
+    kb = case.k_bits if k_bits is None else k_bits
+    vb = case.v_bits if v_bits is None else v_bits
+    sl = case.slot_mapping if slots is None else slots
+    k = bits_tensor(kb).view(torch.bfloat16)
+    v = bits_tensor(vb).view(torch.bfloat16)
+    s = torch.from_numpy(np.ascontiguousarray(sl, np.int32)).to(dev())
+    B.kv8_quant_append(k, v, s, *cache)
+    return cache
+
+
+def q_tensor(case, q=None):
+    if case.q_dtype == "bf16":
+        bits = case.q_bits if q is None else q
+        return bits_tensor(bits).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(case.q if q is None else q, np.float32)).to(dev())
+
+
+def gpu_decode(case, cache, q=None, tokens_per_split=0, block_table=None, context_lens=None,
+               max_context_len=None, sm_scale=None):
+    bt = case.block_table if block_table is None else block_table
+    cl = case.context_lens if context_lens is None else context_lens
+    mcl = int(np.max(cl)) if max_context_len is None else max_context_len
+    qt = q_tensor(case, q)
+    b, hq, d = qt.shape
+    ws_bytes = B.kv8_decode_workspace_size(b, hq, case.num_kv_heads, d, mcl, tokens_per_split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev())
+    out = torch.full((b, hq, d), float("nan"), dtype=torch.float32, device=dev())
+    B.paged_decode_attn_kv8(qt, *cache,
+                            torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev()),
+                            torch.from_numpy(np.ascontiguousarray(cl, np.int32)).to(dev()),
+                            mcl, out, ws, sm_scale=sm_scale, tokens_per_split=tokens_per_split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_close(out, ref, what=""):
+    """Tolerance check in fp32; returns (max_abs, rel_l2)."""
+    o = np.asarray(out, np.float32)
+    r = np.asarray(ref, np.float64).astype(np.float32)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    diff = o.astype(np.float32) - r
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(r))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    assert max_abs <= MAX_ABS, f"{what}: max|delta| {max_abs:.3e} > {MAX_ABS}"
+    assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e} > {REL_L2}"
+    return max_abs, rel

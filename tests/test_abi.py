@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/kv8.h declares, and rejects bad arguments on the host before
+any HIP call (so no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_int8_kv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kv8.h")
+
+# Fake, 16-byte aligned, never dereferenced device addresses
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for st in range(-6, 1):
+        assert B.status_string(st).startswith("KV8_")
+    assert "unknown" in B.status_string(-99)
+    assert B.load().kv8_version() >= 100
+
+
+def append(**kw):
+    a = dict(k_new=P, v_new=P, slots=P, n=4, hkv=8, d=128, bs=16, nb=10,
+             kc=P, vc=P, ks=P, vs=P, stream=None)
+    a.update(kw)
+    return B.load().kv8_quant_append(a["k_new"], a["v_new"], a["slots"], a["n"], a["hkv"],
+                                     a["d"], a["bs"], a["nb"], a["kc"], a["vc"], a["ks"],
+                                     a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(k_new=None), B.KV8_ERR_NULL),
+    (dict(slots=None), B.KV8_ERR_NULL),
+    (dict(kc=None), B.KV8_ERR_NULL),
+    (dict(vs=None), B.KV8_ERR_NULL),
+    (dict(n=-1), B.KV8_ERR_SHAPE),
+    (dict(hkv=0), B.KV8_ERR_SHAPE),
+    (dict(nb=0), B.KV8_ERR_SHAPE),
+    (dict(d=96), B.KV8_ERR_UNSUPPORTED),
+    (dict(bs=32), B.KV8_ERR_UNSUPPORTED),
+    (dict(kc=MIS), B.KV8_ERR_ALIGN),
+    (dict(k_new=MIS), B.KV8_ERR_ALIGN),
+    (dict(n=0), B.KV8_OK),                      # empty append is a no-op
+])
+def test_append_validation(kw, expected):
+    assert append(**kw) == expected
+
+
+def decode(**kw):
+    a = dict(q=P, dt=B.KV8_BF16, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
+             maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=P2,
+             wsb=1 << 30, tps=0, stream=None)
+    a.update(kw)
+    return B.load().paged_decode_attn_kv8(
+        a["q"], a["dt"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"], a["bt"], a["mbs"],
+        a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"],
+        a["out"], a["ws"], a["wsb"], a["tps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(q=None), B.KV8_ERR_NULL),
+    (dict(bt=None), B.KV8_ERR_NULL),
+    (dict(ctx=None), B.KV8_ERR_NULL),
+    (dict(out=None), B.KV8_ERR_NULL),
+    (dict(ks=None), B.KV8_ERR_NULL),
+    (dict(b=0), B.KV8_ERR_SHAPE),
+    (dict(hq=30), B.KV8_ERR_SHAPE),             # Hq % Hkv != 0
+    (dict(maxctx=-1), B.KV8_ERR_SHAPE),
+    (dict(mbs=0), B.KV8_ERR_SHAPE),
+    (dict(nb=0), B.KV8_ERR_SHAPE),
+    (dict(hq=24), B.KV8_ERR_UNSUPPORTED),       # G = 3
+    (dict(d=256), B.KV8_ERR_UNSUPPORTED),
+    (dict(bs=32), B.KV8_ERR_UNSUPPORTED),
+    (dict(dt=7), B.KV8_ERR_UNSUPPORTED),
+    (dict(tps=100), B.KV8_ERR_UNSUPPORTED),
+    (dict(tps=4096), B.KV8_ERR_UNSUPPORTED),
+    (dict(q=MIS), B.KV8_ERR_ALIGN),
+    (dict(kc=MIS), B.KV8_ERR_ALIGN),
+    (dict(out=MIS), B.KV8_ERR_ALIGN),
+    (dict(ws=None), B.KV8_ERR_WORKSPACE),
+    (dict(wsb=16), B.KV8_ERR_WORKSPACE),
+])
+def test_decode_validation(kw, expected):
+    assert decode(**kw) == expected
+
+
+def test_decode_workspace_size():
+    ws = B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 512)
+    n_split = 8
+    assert ws >= 32 * 32 * n_split * (128 + 1) * 4
+    assert ws < 32 * 32 * n_split * (128 + 1) * 4 + 1024
+    assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 0) > 0
+    assert B.kv8_decode_workspace_size(32, 30, 8, 128, 4096, 0) == 0
+    assert B.kv8_decode_workspace_size(32, 32, 8, 96, 4096, 0) == 0
+    assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 100) == 0
+    # default split for a Llama-3.1-8B-shaped batch: 512 tokens
+    assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 0) == \
+        B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 512)
+
+
+def prefill(**kw):
+    a = dict(q=P, qsl=P, tq=64, mq=32, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
+             maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return B.load().paged_prefill_chunk_attn_kv8(
+        a["q"], a["qsl"], a["tq"], a["mq"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"],
+        a["bt"], a["mbs"], a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"],
+        a["scale"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(qsl=None), B.KV8_ERR_NULL),
+    (dict(q=None), B.KV8_ERR_NULL),
+    (dict(out=None), B.KV8_ERR_NULL),
+    (dict(vc=None), B.KV8_ERR_NULL),
+    (dict(b=0), B.KV8_ERR_SHAPE),
+    (dict(tq=-1), B.KV8_ERR_SHAPE),
+    (dict(hq=31), B.KV8_ERR_SHAPE),
+    (dict(hq=48), B.KV8_ERR_UNSUPPORTED),
+    (dict(d=80), B.KV8_ERR_UNSUPPORTED),
+    (dict(bs=8), B.KV8_ERR_UNSUPPORTED),
+    (dict(q=MIS), B.KV8_ERR_ALIGN),
+    (dict(ks=MIS), B.KV8_ERR_ALIGN),
+    (dict(tq=0), B.KV8_OK),
+])
+def test_prefill_validation(kw, expected):
+    assert prefill(**kw) == expected

@@ -1,0 +1,161 @@
+"""paged_decode_attn_kv8 on the GPU against the fp64 oracle (same
+dequantised cache), plus the invariants the method fixes: block-permutation
+invariance (bitwise), single-token exactness, poisoned unused slots, empty
+contexts, determinism, any split count."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv8_oracle as O
+from paged_int8_kv_amd import workloads as W
+from tests.kv8_testutil import (check_close, dev, gpu_append, gpu_decode, needs_gpu,
+                                oracle_cache, upload_cache)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def run_parity(case, tokens_per_split=0, cache_from="oracle"):
+    kc, vc, ks, vs = oracle_cache(case)
+    cache = upload_cache(kc, vc, ks, vs) if cache_from == "oracle" else gpu_append(case)
+    out = gpu_decode(case, cache, tokens_per_split=tokens_per_split)
+    ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    return check_close(out, ref, f"decode tps={tokens_per_split}"), out, ref
+
+
+def test_decode_tiny_config():
+    run_parity(W.tiny_decode())
+
+
+@pytest.mark.parametrize("tps", [0, 64, 128, 512, 2048])
+def test_decode_llama8b_reduced_batch_splits(tps):
+    run_parity(W.llama8b_decode(batch=4), tokens_per_split=tps)
+
+
+def test_decode_llama8b_full_batch():
+    """Llama-3.1-8B-shaped batch at full size (32 x 32/8 x 128, contexts
+    1024..4096), default split as the benchmark launches it, cache built by
+    the GPU append kernel."""
+    run_parity(W.llama8b_decode(), cache_from="gpu")
+
+
+@pytest.mark.parametrize("hq,hkv,d,qdt", [
+    (4, 4, 128, "bf16"), (8, 4, 64, "f32"), (16, 2, 128, "f32"), (64, 8, 128, "bf16"),
+    (8, 1, 64, "bf16"), (32, 8, 128, "f32"),
+])
+def test_decode_group_sizes_and_dims(hq, hkv, d, qdt):
+    case = W.make_paged_case(batch=3, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                             context_lens=[1, 77, 700], q_dtype=qdt, k_outliers=True,
+                             seed=hq * 7 + d)
+    run_parity(case)
+    run_parity(case, tokens_per_split=64)
+
+
+def test_decode_long_context_step():
+    """Long-context shape (4 x 32768 tokens, 32/8 heads, fp32 q) after one
+    appended token per sequence."""
+    case = W.long_context_decode(steps=1)
+    kc, vc, ks, vs = oracle_cache(case)
+    slots = W.step_slots(case, 0)
+    O.quant_append(case.extra["step_k"][0], case.extra["step_v"][0], slots, kc, vc, ks, vs)
+    ctx = case.context_lens + 1
+    cache = upload_cache(kc, vc, ks, vs)
+    q = case.extra["step_q"][0]
+    out = gpu_decode(case, cache, q=q, context_lens=ctx)
+    ref = O.paged_decode(q, kc, vc, ks, vs, case.block_table, ctx)
+    check_close(out, ref, "long context")
+
+
+def test_decode_single_token_is_exact_v():
+    case = W.make_paged_case(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             context_lens=[1, 1, 1, 1], seed=31)
+    kc, vc, ks, vs = oracle_cache(case)
+    out = gpu_decode(case, upload_cache(kc, vc, ks, vs))
+    for b in range(4):
+        for h in range(32):
+            v = O.gather_dequant(vc, vs, case.block_table[b], 1, h // 4)[0]
+            assert np.array_equal(out[b, h], v.astype(np.float32))
+
+
+def test_decode_identical_keys_give_mean_v():
+    case = W.make_paged_case(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                             context_lens=[37, 300], seed=32)
+    case.k[:] = case.k[0]
+    case.k_bits[:] = case.k_bits[0]
+    kc, vc, ks, vs = oracle_cache(case)
+    out = gpu_decode(case, upload_cache(kc, vc, ks, vs))
+    for b in range(2):
+        for g in range(2):
+            vm = O.gather_dequant(vc, vs, case.block_table[b], int(case.context_lens[b]), g).mean(0)
+            for h in range(g * 4, g * 4 + 4):
+                check_close(out[b, h], vm, "identical keys")
+
+
+def test_decode_block_permutation_bitwise_invariant():
+    base = W.make_paged_case(batch=5, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             context_lens=[16, 300, 1000, 17, 2048], seed=33, permute=False)
+    kc, vc, ks, vs = oracle_cache(base)
+    out = gpu_decode(base, upload_cache(kc, vc, ks, vs))
+    perm = np.random.default_rng(4).permutation(base.num_blocks)
+    arrs = []
+    for a in (kc, vc, ks, vs):
+        p = np.empty_like(a)
+        p[perm] = a
+        arrs.append(p)
+    out2 = gpu_decode(base, upload_cache(*arrs), block_table=perm[base.block_table])
+    assert np.array_equal(out, out2)
+    # batch order
+    order = np.array([4, 2, 0, 3, 1])
+    out3 = gpu_decode(base, upload_cache(kc, vc, ks, vs), q=base.q_bits[order],
+                      block_table=base.block_table[order], context_lens=base.context_lens[order])
+    assert np.array_equal(out3, out[order])
+
+
+def test_decode_poisoned_unused_slots_and_empty_context():
+    case = W.make_paged_case(batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                             context_lens=[21, 0, 70], seed=34, spare_blocks=3)
+    kc, vc, ks, vs = oracle_cache(case)
+    ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    # poison every slot beyond each context and the spare blocks
+    used = set()
+    for b in range(3):
+        n = int(case.context_lens[b])
+        for t in range(n):
+            used.add((int(case.block_table[b][t // 16]), t % 16))
+    nanbits = np.float16(np.nan)
+    for blk in range(case.num_blocks):
+        for off in range(16):
+            if (blk, off) not in used:
+                kc[blk, :, off] = 127
+                vc[blk, :, off] = -127
+                ks[blk, :, off] = nanbits
+                vs[blk, :, off] = np.float16(np.inf)
+    out = gpu_decode(case, upload_cache(kc, vc, ks, vs))
+    assert np.all(out[1] == 0)
+    check_close(out, ref, "poisoned")
+
+
+def test_decode_deterministic_and_context_cap():
+    case = W.llama8b_decode(batch=6)
+    kc, vc, ks, vs = oracle_cache(case)
+    cache = upload_cache(kc, vc, ks, vs)
+    a = gpu_decode(case, cache)
+    b = gpu_decode(case, cache)
+    assert np.array_equal(a, b)
+    # max_context_len below some lengths clamps those sequences
+    cap = 2000
+    out = gpu_decode(case, cache, max_context_len=cap)
+    ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table,
+                         np.minimum(case.context_lens, cap))
+    check_close(out, ref, "context cap")
+
+
+def test_decode_large_logits_dominant_key():
+    case = W.make_paged_case(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=128,
+                             context_lens=[500], q_dtype="f32", seed=35)
+    kc, vc, ks, vs = oracle_cache(case)
+    kd = O.gather_dequant(kc, ks, case.block_table[0], 500, 0)
+    q = np.zeros_like(case.q)
+    q[0, :] = (kd[123] * (3000.0 / np.dot(kd[123], kd[123]))).astype(np.float32)
+    out = gpu_decode(case, upload_cache(kc, vc, ks, vs), q=q)
+    ref = O.paged_decode(q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    check_close(out, ref, "dominant key")
