@@ -92,7 +92,7 @@ def main():
     table = torch.from_numpy(case.block_table).to(dev)
     lens = torch.from_numpy(ctx).to(dev)
     out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx, args.tokens_per_split),
+    ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx, args.tokens_per_split),
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 

@@ -136,8 +136,9 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * the fly per the KV8 item of the "KV-Cache 全栈优化系统" README).  The
  * softmax and all accumulation run in fp32 ("大模型推理加速：KV Cache与vLLM
  * 技术解析", section 4.1).  Split-K: each workgroup covers up to
- * tokens_per_split tokens of one (sequence, KV head) for all G query heads
- * and a second kernel merges the partial results by log-sum-exp.
+ * tokens_per_split tokens of one (sequence, KV head) for all G query heads;
+ * the last workgroup of each (sequence, KV head) to finish merges the
+ * partial results by log-sum-exp inside the same launch.
  *
  *   q             device [B, Hq, d], dtype q_dtype (KV8_F32 or KV8_BF16)
  *   block_table   device int32 [B, max_blocks_per_seq]
@@ -147,7 +148,12 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *   sm_scale      softmax scale, normally 1/sqrt(d)
  *   out           device fp32 [B, Hq, d]
  *   workspace     device scratch of at least kv8_decode_workspace_size()
- *                 bytes (16-byte aligned); contents need no initialisation
+ *                 bytes (16-byte aligned).  It must be zero-filled once
+ *                 before its first use; every completed call leaves it
+ *                 ready for the next (its leading per-(sequence, KV head)
+ *                 counters return to zero).  Calls sharing one workspace
+ *                 must not overlap in time (use one stream, or one
+ *                 workspace per stream).
  *   tokens_per_split  as for kv8_decode_workspace_size (same value!)
  * Same inputs and same tokens_per_split give bitwise-identical output.
  */

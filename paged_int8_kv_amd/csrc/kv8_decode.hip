@@ -1,11 +1,13 @@
-// paged_decode_attn_kv8 kernels: split-K flash-decoding over the paged
-// INT8 cache for gfx950.
+// paged_decode_attn_kv8 kernel: split-K flash-decoding over the paged INT8
+// cache for gfx950.
 //
 // Attention softmax(q K^T * sm_scale) V ("KV Cache 优化全景解析", section 2.1)
 // per GQA group (section 3.3) over K/V restored on the fly from INT8 codes
 // and per-token fp16 scales ("KV-Cache 全栈优化系统" README, section
 // 主要特性), with fp32 softmax and accumulation ("大模型推理加速：KV Cache
-// 与vLLM技术解析", section 4.1).  Split results are merged by log-sum-exp.
+// 与vLLM技术解析", section 4.1).  Split results are merged by log-sum-exp
+// inside the same launch: the last workgroup of a (sequence, KV head) to
+// finish merges the partials of all its splits.
 //
 // One workgroup (4 waves) serves one (sequence b, KV head g, split) and all
 // G query heads of the group, so each cache byte is read from HBM once.
@@ -30,6 +32,10 @@
 // output (pass 2: 1152 * sum w).  q enters as fp16 after an exact
 // per-head power-of-two rescale (bf16 q is exact in fp16 then); an fp32 q
 // is split into a high and a low fp16 part.
+//
+// Each wave keeps kPf blocks in flight in a register ring; the ring is
+// branch-free around its loads so that the compiler's wait counts stay
+// exact, and scheduling barriers keep later slots' waits from being hoisted.
 #include "kv8_device.h"
 #include "kv8_launch.h"
 
@@ -39,6 +45,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kPf = 4;        // blocks in flight per wave and pass
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SplitArgs {
@@ -49,8 +56,10 @@ struct SplitArgs {
   const uint16_t* v_scale;
   const int32_t* block_table;
   const int32_t* context_lens;
+  float* out;
   float* o_part;
   float* lse_part;
+  unsigned* counters;
   int64_t num_blocks;
   int max_blocks_per_seq;
   int ctx_cap;
@@ -64,11 +73,12 @@ struct SplitArgs {
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
 struct SmemLayout {
-  int blk_off, z_off, vs_off, pp_off, red_off, total;
+  int blk_off, z_off, vs_off, pp_off, red_off, flag_off, total;
 };
 
 // LDS carve-up of one workgroup: block ids, logits (reused for the final
-// cross-wave reduction), v scales, packed fp16 weights, per-head scalars.
+// cross-wave reduction), v scales, packed fp16 weights, per-head scalars,
+// and the last-workgroup flag.
 __host__ __device__ inline SmemLayout smem_layout(int split_tokens, int G, int D) {
   SmemLayout L{};
   const int zbytes = split_tokens * G * 4;
@@ -78,7 +88,8 @@ __host__ __device__ inline SmemLayout smem_layout(int split_tokens, int G, int D
   L.vs_off = L.z_off + align16(zbytes > finbytes ? zbytes : finbytes);
   L.pp_off = L.vs_off + align16(split_tokens * 2);
   L.red_off = L.pp_off + align16((split_tokens / 2) * G * 4);
-  L.total = L.red_off + align16(3 * kWaves * G * 4);
+  L.flag_off = L.red_off + align16(3 * kWaves * G * 4);
+  L.total = L.flag_off + 16;
   return L;
 }
 
@@ -91,11 +102,72 @@ __device__ __forceinline__ uint32_t dword(const uint4& r, int k) {
 }
 __device__ __forceinline__ uint32_t dword(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
 
+// One reduce-scatter step over lane pairs given by the DPP pattern CTRL:
+// the lane flagged `upper` keeps the second half of its N values, its
+// partner the first half, and each adds the partner's copy of the half it
+// keeps.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2], bool upper) {
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float keep = upper ? in[k + N / 2] : in[k];
+    const float send = upper ? in[k] : in[k + N / 2];
+    out[k] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Reduce the N = 2G partial dot products v[t*G + h] (tokens t = 0, 1 of the
+// lane's pair, heads h) over the 8 lanes of a token group.  Lane i of the
+// group ends with NV = max(1, N/8) full sums: value j is v index
+//   (i>>2)*(N/2) + ((i>>1)&1)*(N/4 if N>=4) + (i&1)*(N/8 if N>=8) + j,
+// i.e. token i>>2.  The first step pairs lanes i and 7-i (half mirror),
+// the next two are quad exchanges.
+template <int G>
+__device__ __forceinline__ void reduce_scatter8(const float (&v)[2 * G],
+                                                float (&out)[(2 * G >= 8) ? (2 * G) / 8 : 1],
+                                                int i) {
+  constexpr int N = 2 * G;
+  float a[N / 2];
+  rs_half<kDppHalfMirror, N>(v, a, i >= 4);
+  if constexpr (N / 2 >= 2) {
+    float b[N / 4];
+    rs_half<kDppQuadXor2, N / 2>(a, b, (i & 2) != 0);
+    if constexpr (N / 4 >= 2) {
+      rs_half<kDppQuadXor1, N / 4>(b, out, (i & 1) != 0);
+    } else {
+      out[0] = b[0] + dpp_f<kDppQuadXor1>(b[0]);
+    }
+  } else {
+    float x = a[0] + dpp_f<kDppQuadXor2>(a[0]);
+    out[0] = x + dpp_f<kDppQuadXor1>(x);
+  }
+}
+
+// Head of value j after reduce_scatter8 on lane i of its group.
+template <int G>
+__device__ __forceinline__ int rs_head(int i, int j) {
+  constexpr int N = 2 * G;
+  int idx = ((i >> 1) & 1) * (N >= 4 ? N / 4 : 0) + (i & 1) * (N >= 8 ? N / 8 : 0) + j;
+  return idx % G;
+}
+
+// Agent-scope relaxed accesses (coherent across the XCDs' L2 caches).
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D, int G, bool QF32>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   constexpr int CPL = D / 8;    // channels (= code bytes) per lane per token
   constexpr int NDW = CPL / 4;  // dwords per lane per token
   constexpr int NP = CPL / 2;   // fp16 pairs per lane per token
+  constexpr int NV = (2 * G >= 8) ? (2 * G) / 8 : 1;   // logits stored per lane
+  constexpr int M = G * CPL;    // accumulators per lane
   using Row = typename RowT<NDW>::type;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -106,19 +178,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   uint16_t* s_vs = reinterpret_cast<uint16_t*>(smem + L.vs_off);
   uint32_t* s_pp = reinterpret_cast<uint32_t*>(smem + L.pp_off);
   float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int slot = lane >> 3, chunk = lane & 7;
+  const int64_t bh0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
 
   int ctx = a.context_lens[b];
   ctx = min(max(ctx, 0), a.ctx_cap);
   const int t0 = split * a.split_tokens;
-  if (t0 >= ctx) return;                       // uniform over the workgroup
+  if (t0 >= ctx) {                             // uniform over the workgroup
+    if (split == 0)                            // empty context: zero output
+      for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
+    return;
+  }
   const int ntok = min(ctx - t0, a.split_tokens);
   const int nblk = (ntok + kBlock - 1) / kBlock;
   const int jb0 = t0 / kBlock;
   const int Hkv = a.num_kv_heads;
+  const int nvalid = (ctx + a.split_tokens - 1) / a.split_tokens;
 
   if (tid < nblk) {
     int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + tid];
@@ -131,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   half2_t ql[QF32 ? G : 1][QF32 ? NP : 1];
   float cz[G], qbias[G];
   {
-    const int64_t qrow0 = ((int64_t)b * a.num_q_heads + (int64_t)g * G) * D + chunk * CPL;
+    const int64_t qrow0 = bh0 * D + chunk * CPL;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float x[CPL];
@@ -144,12 +224,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
         }
       } else {
-        const Row r = *reinterpret_cast<const Row*>(
+        // CPL bf16 values = two Rows of NDW dwords
+        const Row* qp = reinterpret_cast<const Row*>(
             static_cast<const uint16_t*>(a.q) + qrow0 + (int64_t)h * D);
-        // a Row of NDW dwords holds 2*NDW bf16 values; CPL = 4*NDW values
-        // need two Rows
-        const Row r2 = *(reinterpret_cast<const Row*>(
-            static_cast<const uint16_t*>(a.q) + qrow0 + (int64_t)h * D) + 1);
+        const Row r = qp[0], r2 = qp[1];
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
           const uint32_t w = dword(r, k), w2 = dword(r2, k);
@@ -183,82 +261,119 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
       qbias[h] = kCodeBias * qsum;
     }
   }
-  __syncthreads();   // s_blk visible
-
-  // ---- pass 1: logits ----------------------------------------------------
-  float mloc = kNegInf;
-  {
-    auto row_ptr = [&](const int8_t* base, int j) {
-      const int64_t line = ((int64_t)s_blk[j] * Hkv + g) * kBlock;
-      return base + (line + slot) * D + chunk * CPL;
-    };
-    auto scale_idx = [&](int j) { return ((int64_t)s_blk[j] * Hkv + g) * kBlock + slot; };
-
-    int j = wave;
-    Row w0{}, w1{};
-    uint16_t ks0 = 0, ks1 = 0, vs0 = 0, vs1 = 0;
-    if (j < nblk) {
-      const int8_t* p = row_ptr(a.k_cache, j);
-      w0 = *reinterpret_cast<const Row*>(p);
-      w1 = *reinterpret_cast<const Row*>(p + 8 * D);
-      const int64_t si = scale_idx(j);
-      ks0 = a.k_scale[si]; ks1 = a.k_scale[si + 8];
-      vs0 = a.v_scale[si]; vs1 = a.v_scale[si + 8];
-    }
-    for (; j < nblk; j += kWaves) {
-      Row n0{}, n1{};
-      uint16_t nks0 = 0, nks1 = 0, nvs0 = 0, nvs1 = 0;
-      if (j + kWaves < nblk) {                 // prefetch the wave's next block
-        const int8_t* p = row_ptr(a.k_cache, j + kWaves);
-        n0 = *reinterpret_cast<const Row*>(p);
-        n1 = *reinterpret_cast<const Row*>(p + 8 * D);
-        const int64_t si = scale_idx(j + kWaves);
-        nks0 = a.k_scale[si]; nks1 = a.k_scale[si + 8];
-        nvs0 = a.v_scale[si]; nvs1 = a.v_scale[si + 8];
-      }
-      float S0[G], S1[G];
+  // per-lane constants of the logits this lane stores after the reduction
+  const int tk = chunk >> 2;            // token of the pair: slot or slot+8
+  int hv[NV];
+  float czl[NV], qbl[NV];
 #pragma unroll
-      for (int h = 0; h < G; ++h) { S0[h] = 0.0f; S1[h] = 0.0f; }
+  for (int j = 0; j < NV; ++j) {
+    hv[j] = rs_head<G>(chunk, j);
+    czl[j] = cz[0];
+    qbl[j] = qbias[0];
 #pragma unroll
-      for (int k = 0; k < NDW; ++k) {
-        const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
-        const half2_t a0 = biased_pair_lo(x0), b0 = biased_pair_hi(x0);
-        const half2_t a1 = biased_pair_lo(x1), b1 = biased_pair_hi(x1);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          S0[h] = fdot2(qh[h][2 * k], a0, S0[h]);
-          S0[h] = fdot2(qh[h][2 * k + 1], b0, S0[h]);
-          S1[h] = fdot2(qh[h][2 * k], a1, S1[h]);
-          S1[h] = fdot2(qh[h][2 * k + 1], b1, S1[h]);
-          if constexpr (QF32) {
-            S0[h] = fdot2(ql[h][2 * k], a0, S0[h]);
-            S0[h] = fdot2(ql[h][2 * k + 1], b0, S0[h]);
-            S1[h] = fdot2(ql[h][2 * k], a1, S1[h]);
-            S1[h] = fdot2(ql[h][2 * k + 1], b1, S1[h]);
-          }
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) { S0[h] = group8_sum(S0[h]); S1[h] = group8_sum(S1[h]); }
-      const int tl0 = j * kBlock + slot, tl1 = tl0 + 8;
-      const bool ok0 = tl0 < ntok, ok1 = tl1 < ntok;
-      const float k0 = fp16_bits_to_f32(ks0), k1 = fp16_bits_to_f32(ks1);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (chunk == h) {
-          const float z0 = ok0 ? (k0 * cz[h]) * (S0[h] - qbias[h]) : kNegInf;
-          const float z1 = ok1 ? (k1 * cz[h]) * (S1[h] - qbias[h]) : kNegInf;
-          s_z[tl0 * G + h] = z0;
-          s_z[tl1 * G + h] = z1;
-          mloc = fmaxf(mloc, fmaxf(z0, z1));
-        }
-      }
-      if (chunk == 0) { s_vs[tl0] = vs0; s_vs[tl1] = vs1; }
-      w0 = n0; w1 = n1; ks0 = nks0; ks1 = nks1; vs0 = nvs0; vs1 = nvs1;
+    for (int h = 1; h < G; ++h) {
+      czl[j] = hv[j] == h ? cz[h] : czl[j];
+      qbl[j] = hv[j] == h ? qbias[h] : qbl[j];
     }
   }
-  mloc = across_groups_max(mloc);
-  if (slot == 0 && chunk < G) s_red[wave * G + chunk] = mloc;
+  __syncthreads();   // s_blk visible
+
+  // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1.
+  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int last = nmine - 1;
+  auto line_of = [&](int i) {
+    return ((int64_t)s_blk[wave + i * kWaves] * Hkv + g) * kBlock + slot;
+  };
+
+  // ---- pass 1: logits ----------------------------------------------------
+  float mloc[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) mloc[j] = kNegInf;
+  if (nmine > 0) {
+    Row r0[kPf], r1[kPf];
+    uint16_t ks0[kPf], ks1[kPf], vs0[kPf], vs1[kPf];
+    auto issue = [&](int s, int i) {
+      const int64_t line = line_of(i);
+      const int8_t* p = a.k_cache + line * D + chunk * CPL;
+      r0[s] = *reinterpret_cast<const Row*>(p);
+      r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
+      ks0[s] = a.k_scale[line];
+      ks1[s] = a.k_scale[line + 8];
+      vs0[s] = a.v_scale[line];
+      vs1[s] = a.v_scale[line + 8];
+    };
+    // Slots past the wave's last block re-read that block (L2 hits) and skip
+    // the compute, so every load stays unconditional.
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) issue(s, min(s, last));
+    for (int base = 0; base < nmine; base += kPf) {
+#pragma unroll
+      for (int s = 0; s < kPf; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = base + s;
+        if (i < nmine) {
+          const Row w0 = r0[s], w1 = r1[s];
+          float S[2 * G];
+#pragma unroll
+          for (int k = 0; k < 2 * G; ++k) S[k] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NDW; ++k) {
+            const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
+            const half2_t a0 = biased_pair_lo(x0), b0 = biased_pair_hi(x0);
+            const half2_t a1 = biased_pair_lo(x1), b1 = biased_pair_hi(x1);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              S[h] = fdot2(qh[h][2 * k], a0, S[h]);
+              S[h] = fdot2(qh[h][2 * k + 1], b0, S[h]);
+              S[G + h] = fdot2(qh[h][2 * k], a1, S[G + h]);
+              S[G + h] = fdot2(qh[h][2 * k + 1], b1, S[G + h]);
+              if constexpr (QF32) {
+                S[h] = fdot2(ql[h][2 * k], a0, S[h]);
+                S[h] = fdot2(ql[h][2 * k + 1], b0, S[h]);
+                S[G + h] = fdot2(ql[h][2 * k], a1, S[G + h]);
+                S[G + h] = fdot2(ql[h][2 * k + 1], b1, S[G + h]);
+              }
+            }
+          }
+          float R[NV];
+          reduce_scatter8<G>(S, R, chunk);
+          const int tl = (wave + i * kWaves) * kBlock + slot + 8 * tk;
+          const bool ok = tl < ntok;
+          const float ksc = fp16_bits_to_f32(tk ? ks1[s] : ks0[s]);
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            const float z = ok ? (ksc * czl[j]) * (R[j] - qbl[j]) : kNegInf;
+            s_z[tl * G + hv[j]] = z;
+            mloc[j] = fmaxf(mloc[j], z);
+          }
+          s_vs[tl] = tk ? vs1[s] : vs0[s];
+        }
+        issue(s, min(i + kPf, last));
+      }
+    }
+  }
+
+  // V rows of the first kPf blocks are requested now, so that they arrive
+  // while the workgroup finishes the logits and builds the weights.
+  Row r0[kPf], r1[kPf];
+  auto issue_v = [&](int s, int i) {
+    const int8_t* p = a.v_cache + line_of(i) * D + chunk * CPL;
+    r0[s] = *reinterpret_cast<const Row*>(p);
+    r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
+  };
+  if (nmine > 0) {
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) issue_v(s, min(s, last));
+  }
+
+  // max per head: lanes chunk and chunk^4 hold the two tokens of a head,
+  // the eight token groups hold the other tokens
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float m = fmaxf(mloc[j], __shfl_xor(mloc[j], 4));
+    m = across_groups_max(m);
+    if (slot == 0) s_red[wave * G + hv[j]] = m;
+  }
   __syncthreads();
 
   // ---- middle: weights ----------------------------------------------------
@@ -296,64 +411,67 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   __syncthreads();
 
   // ---- pass 2: weighted sum of V codes ------------------------------------
-  float acc[G][CPL];
+  float acc[M];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int k = 0; k < M; ++k) acc[k] = 0.0f;
+  for (int base = 0; base < nmine; base += kPf) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[h][c] = 0.0f;
-  {
-    auto row_ptr = [&](int j) {
-      const int64_t line = ((int64_t)s_blk[j] * Hkv + g) * kBlock;
-      return a.v_cache + (line + slot) * D + chunk * CPL;
-    };
-    int j = wave;
-    Row w0{}, w1{};
-    if (j < nblk) {
-      const int8_t* p = row_ptr(j);
-      w0 = *reinterpret_cast<const Row*>(p);
-      w1 = *reinterpret_cast<const Row*>(p + 8 * D);
-    }
-    for (; j < nblk; j += kWaves) {
-      Row n0{}, n1{};
-      if (j + kWaves < nblk) {
-        const int8_t* p = row_ptr(j + kWaves);
-        n0 = *reinterpret_cast<const Row*>(p);
-        n1 = *reinterpret_cast<const Row*>(p + 8 * D);
-      }
-      half2_t wp[G];
-      const uint32_t* src = s_pp + (j * 8 + slot) * G;
+    for (int s = 0; s < kPf; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = base + s;
+      if (i < nmine) {
+        const Row w0 = r0[s], w1 = r1[s];
+        half2_t wp[G];
+        const uint32_t* src = s_pp + ((wave + i * kWaves) * 8 + slot) * G;
 #pragma unroll
-      for (int h = 0; h < G; ++h) wp[h] = __builtin_bit_cast(half2_t, src[h]);
+        for (int h = 0; h < G; ++h) wp[h] = __builtin_bit_cast(half2_t, src[h]);
 #pragma unroll
-      for (int k = 0; k < NDW; ++k) {
-        const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
-        const uint32_t i01 = interleave_lo(x0, x1), i23 = interleave_hi(x0, x1);
-        const half2_t f0 = biased_pair_lo(i01), f1 = biased_pair_hi(i01);
-        const half2_t f2 = biased_pair_lo(i23), f3 = biased_pair_hi(i23);
+        for (int k = 0; k < NDW; ++k) {
+          const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
+          const uint32_t i01 = interleave_lo(x0, x1), i23 = interleave_hi(x0, x1);
+          const half2_t f0 = biased_pair_lo(i01), f1 = biased_pair_hi(i01);
+          const half2_t f2 = biased_pair_lo(i23), f3 = biased_pair_hi(i23);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][4 * k] = fdot2(wp[h], f0, acc[h][4 * k]);
-          acc[h][4 * k + 1] = fdot2(wp[h], f1, acc[h][4 * k + 1]);
-          acc[h][4 * k + 2] = fdot2(wp[h], f2, acc[h][4 * k + 2]);
-          acc[h][4 * k + 3] = fdot2(wp[h], f3, acc[h][4 * k + 3]);
+          for (int h = 0; h < G; ++h) {
+            acc[h * CPL + 4 * k] = fdot2(wp[h], f0, acc[h * CPL + 4 * k]);
+            acc[h * CPL + 4 * k + 1] = fdot2(wp[h], f1, acc[h * CPL + 4 * k + 1]);
+            acc[h * CPL + 4 * k + 2] = fdot2(wp[h], f2, acc[h * CPL + 4 * k + 2]);
+            acc[h * CPL + 4 * k + 3] = fdot2(wp[h], f3, acc[h * CPL + 4 * k + 3]);
+          }
         }
       }
-      w0 = n0; w1 = n1;
+      issue_v(s, min(i + kPf, last));
     }
   }
+
+  // ---- sum the eight token groups: a row step, then two reduce-scatter
+  // steps on the row/half swaps.  Lane l keeps M/4 sums: value k is
+  // accumulator k + (M/2)*(row of l is odd) + (M/4)*(l in upper half).
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int k = 0; k < M; ++k) acc[k] += dpp_f<kDppRowRor8>(acc[k]);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[h][c] = across_groups_sum(acc[h][c]);
-  if (slot == 0) {
+  for (int k = 0; k < M / 2; ++k) {
+    float x, y;
+    swap16_pair(acc[k], acc[k + M / 2], x, y);
+    acc[k] = x + y;
+  }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int k = 0; k < M / 4; ++k) {
+    float x, y;
+    swap32_pair(acc[k], acc[k + M / 4], x, y);
+    acc[k] = x + y;
+  }
+  if ((lane & 8) == 0) {               // the two groups of a row agree
+    const int off = (M / 2) * ((lane >> 4) & 1) + (M / 4) * (lane >> 5);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) s_fin[(wave * G + h) * D + chunk * CPL + c] = acc[h][c];
+    for (int k = 0; k < M / 4; ++k) {
+      const int idx = k + off;
+      s_fin[(wave * G + idx / CPL) * D + chunk * CPL + idx % CPL] = acc[k];
+    }
   }
   __syncthreads();
 
-  // ---- normalise and write this split's partial result ---------------------
+  // ---- normalise; write the output or this split's partial ----------------
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, c = e % D;
     float s = s_fin[h * D + c];
@@ -365,37 +483,49 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
       Lh += s_red[kWaves * G + w * G + h];
       Ph += s_red[2 * kWaves * G + w * G + h];
     }
-    const int64_t bh = (int64_t)b * a.num_q_heads + (int64_t)g * G + h;
-    a.o_part[(bh * a.n_split + split) * D + c] = (s - kCodeBias * Ph) / Lh;
-    if (c == 0) a.lse_part[bh * a.n_split + split] = Mh + __builtin_amdgcn_logf(Lh);
+    const float o = (s - kCodeBias * Ph) / Lh;
+    if (nvalid == 1) {
+      a.out[(bh0 + h) * D + c] = o;
+    } else {
+      store_agent(a.o_part + ((bh0 + h) * a.n_split + split) * D + c, o);
+      if (c == 0)
+        store_agent(a.lse_part + (bh0 + h) * a.n_split + split, Mh + __builtin_amdgcn_logf(Lh));
+    }
   }
-}
+  if (nvalid == 1) return;
 
-// Log-sum-exp merge of the split partials: one workgroup per (b, query
-// head), one thread per channel.
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    const int32_t* __restrict__ context_lens, int ctx_cap, int split_tokens, int n_split,
-    int num_q_heads, float* __restrict__ out) {
-  const int64_t bh = blockIdx.x;
-  const int b = (int)(bh / num_q_heads);
-  const int c = threadIdx.x;
-  int ctx = context_lens[b];
-  ctx = min(max(ctx, 0), ctx_cap);
-  const int nv = (ctx + split_tokens - 1) / split_tokens;
-  float* dst = out + bh * D + c;
-  if (nv == 0) { *dst = 0.0f; return; }
-  const float* lse = lse_part + bh * n_split;
-  float M = kNegInf;
-  for (int s = 0; s < nv; ++s) M = fmaxf(M, lse[s]);
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < nv; ++s) {
-    const float w = __builtin_amdgcn_exp2f(lse[s] - M);
-    den += w;
-    num += w * o_part[(bh * n_split + s) * D + c];
+  // ---- the last workgroup of (b, g) merges the splits by log-sum-exp ------
+  // Partials travel through agent-scope stores and loads, which write
+  // through / bypass the per-XCD L2, so no cache-wide writeback or
+  // invalidate is needed: each wave waits for its stores to complete before
+  // the barrier, and only then is the split counted.
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    unsigned* cnt = a.counters + (int64_t)b * Hkv + g;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const int is_last = prev == (unsigned)(nvalid - 1);
+    if (is_last)                       // leave the counter zero for the next call
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[0] = is_last;
   }
-  *dst = num / den;
+  __syncthreads();
+  if (!s_flag[0]) return;
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int h = e / D, c = e % D;
+    const int64_t bh = bh0 + h;
+    const float* lse = a.lse_part + bh * a.n_split;
+    float Mx = kNegInf;
+    for (int s = 0; s < nvalid; ++s) Mx = fmaxf(Mx, load_agent(lse + s));
+    float num = 0.0f, den = 0.0f;
+    for (int s = 0; s < nvalid; ++s) {
+      const float w = __builtin_amdgcn_exp2f(load_agent(lse + s) - Mx);
+      den += w;
+      num += w * load_agent(a.o_part + (bh * a.n_split + s) * D + c);
+    }
+    a.out[bh * D + c] = num / den;
+  }
 }
 
 template <int D, int G, bool QF32>
@@ -421,10 +551,6 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-int decode_smem_bytes(int split_tokens, int G, int D) {
-  return smem_layout(split_tokens, G, D).total;
-}
-
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                  int max_context_len, int tokens_per_split, DecodePlan* plan) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
@@ -432,14 +558,14 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
   const int G = num_q_heads / num_kv_heads;
   int tps = tokens_per_split;
   if (tps <= 0) {
-    // Largest split that still gives about 2048 workgroups over the grid;
-    // larger splits amortise the per-split reductions and partial traffic.
+    // Largest split that still gives at least ~4 workgroups per CU over the
+    // grid: larger splits amortise the per-workgroup prologue, reductions
+    // and partial-result traffic.
     tps = 64;
     const int cands[] = {1024, 512, 256, 128};
     for (int c : cands) {
-      const long long wgs = (long long)batch * num_kv_heads *
-                            ((max_context_len + c - 1) / c > 0 ? (max_context_len + c - 1) / c : 1);
-      if (wgs >= 2048) { tps = c; break; }
+      const long long per_seq = max_context_len > 0 ? (max_context_len + c - 1) / c : 1;
+      if ((long long)batch * num_kv_heads * per_seq >= 1024) { tps = c; break; }
     }
     while (tps > 64 && smem_layout(tps, G, head_dim).total > 64 * 1024) tps /= 2;
   } else if (tps % 64 != 0 || tps < 64 || tps > 2048) {
@@ -449,9 +575,10 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
   const int n_split = max_context_len > 0 ? (max_context_len + tps - 1) / tps : 1;
   plan->split_tokens = tps;
   plan->n_split = n_split;
+  plan->counter_bytes = align256((size_t)batch * num_kv_heads * sizeof(unsigned));
   plan->o_bytes = align256((size_t)batch * num_q_heads * n_split * head_dim * sizeof(float));
   plan->lse_bytes = align256((size_t)batch * num_q_heads * n_split * sizeof(float));
-  plan->total_bytes = plan->o_bytes + plan->lse_bytes;
+  plan->total_bytes = plan->counter_bytes + plan->o_bytes + plan->lse_bytes;
   return true;
 }
 
@@ -461,6 +588,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
   SplitArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -469,8 +597,10 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.v_scale = v_scale;
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes);
+  a.out = out;
+  a.counters = reinterpret_cast<unsigned*>(ws);
+  a.o_part = reinterpret_cast<float*>(ws + plan.counter_bytes);
+  a.lse_part = reinterpret_cast<float*>(ws + plan.counter_bytes + plan.o_bytes);
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.ctx_cap = ctx_cap;
@@ -486,15 +616,6 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   else ok = q_f32 ? dispatch_g<64, true>(G, a, batch, stream)
                   : dispatch_g<64, false>(G, a, batch, stream);
   if (!ok) return -2;
-  const unsigned nbh = (unsigned)((int64_t)batch * num_q_heads);
-  if (head_dim == 128)
-    decode_merge_kernel<128><<<dim3(nbh), dim3(128), 0, stream>>>(
-        a.o_part, a.lse_part, context_lens, ctx_cap, plan.split_tokens, plan.n_split,
-        num_q_heads, out);
-  else
-    decode_merge_kernel<64><<<dim3(nbh), dim3(64), 0, stream>>>(
-        a.o_part, a.lse_part, context_lens, ctx_cap, plan.split_tokens, plan.n_split,
-        num_q_heads, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

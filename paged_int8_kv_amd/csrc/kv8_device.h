@@ -56,24 +56,27 @@ __device__ __forceinline__ float group16_max(float x) {
 }
 
 // Row swaps: v_permlane16_swap exchanges rows 1,3 of its first operand with
-// rows 0,2 of its second; v_permlane32_swap exchanges the upper half of the
-// first with the lower half of the second.  Called with two copies of x,
-// the two results hold x of the partner rows / halves.  Written as inline
-// asm with both operands read-write: through the builtin, the compiler
-// used the first result twice when the two results were added.  The
-// leading s_nop covers the VALU-write -> permlane-read wait states.
-__device__ __forceinline__ void swap16(float x, float& a, float& b) {
-  float u = x, v = x;
+// rows 0,2 of its second (x' = [x.r0, y.r0, x.r2, y.r2], y' = [x.r1, y.r1,
+// x.r3, y.r3] for rows of 16 lanes); v_permlane32_swap exchanges the upper
+// half of the first with the lower half of the second (x' = [x.lo, y.lo],
+// y' = [x.hi, y.hi]).  Written as inline asm with both operands read-write:
+// through the builtin, the compiler used the first result twice when the
+// two results were added.  The leading s_nop covers the VALU-write ->
+// permlane-read wait states.
+__device__ __forceinline__ void swap16_pair(float x, float y, float& xo, float& yo) {
+  float u = x, v = y;
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(u), "+v"(v));
-  a = u;
-  b = v;
+  xo = u;
+  yo = v;
 }
-__device__ __forceinline__ void swap32(float x, float& a, float& b) {
-  float u = x, v = x;
+__device__ __forceinline__ void swap32_pair(float x, float y, float& xo, float& yo) {
+  float u = x, v = y;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(v));
-  a = u;
-  b = v;
+  xo = u;
+  yo = v;
 }
+__device__ __forceinline__ void swap16(float x, float& a, float& b) { swap16_pair(x, x, a, b); }
+__device__ __forceinline__ void swap32(float x, float& a, float& b) { swap32_pair(x, x, a, b); }
 
 // Sum of the eight lanes {l, l^8, l^16, ..., l^56} (same position inside
 // every group of 8); every lane receives the sum of its class.

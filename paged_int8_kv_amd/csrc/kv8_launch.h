@@ -15,10 +15,11 @@ int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                         uint16_t* k_scale, uint16_t* v_scale, hipStream_t stream);
 
 struct DecodePlan {
-  int split_tokens;   // tokens per workgroup (multiple of 64)
-  int n_split;        // workgroups per (sequence, KV head)
-  size_t o_bytes;     // partial outputs  fp32 [B, Hq, n_split, d]
-  size_t lse_bytes;   // partial log2-sum-exp fp32 [B, Hq, n_split]
+  int split_tokens;      // tokens per workgroup (multiple of 64)
+  int n_split;           // workgroups per (sequence, KV head)
+  size_t counter_bytes;  // uint32 [B, Hkv] finished-split counters (self-resetting)
+  size_t o_bytes;        // partial outputs  fp32 [B, Hq, n_split, d]
+  size_t lse_bytes;      // partial log2-sum-exp fp32 [B, Hq, n_split]
   size_t total_bytes;
 };
 

@@ -67,14 +67,14 @@ def q_tensor(case, q=None):
 
 
 def gpu_decode(case, cache, q=None, tokens_per_split=0, block_table=None, context_lens=None,
-               max_context_len=None, sm_scale=None):
+               max_context_len=None, sm_scale=None, workspace=None):
     bt = case.block_table if block_table is None else block_table
     cl = case.context_lens if context_lens is None else context_lens
     mcl = int(np.max(cl)) if max_context_len is None else max_context_len
     qt = q_tensor(case, q)
     b, hq, d = qt.shape
     ws_bytes = B.kv8_decode_workspace_size(b, hq, case.num_kv_heads, d, mcl, tokens_per_split)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev())
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev()) if workspace is None else workspace
     out = torch.full((b, hq, d), float("nan"), dtype=torch.float32, device=dev())
     B.paged_decode_attn_kv8(qt, *cache,
                             torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev()),

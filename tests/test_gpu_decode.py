@@ -159,3 +159,21 @@ def test_decode_large_logits_dominant_key():
     out = gpu_decode(case, upload_cache(kc, vc, ks, vs), q=q)
     ref = O.paged_decode(q, kc, vc, ks, vs, case.block_table, case.context_lens)
     check_close(out, ref, "dominant key")
+
+
+def test_decode_workspace_reused_across_calls():
+    """One zero-filled workspace serves many calls of different shapes: the
+    split counters return to zero after every call."""
+    big = W.llama8b_decode(batch=8)
+    small = W.make_paged_case(batch=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              context_lens=[5000, 64, 1500], seed=36)
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=dev())
+    for case in (big, small, big, small):
+        kc, vc, ks, vs = oracle_cache(case)
+        for tps in (64, 256):
+            out = gpu_decode(case, upload_cache(kc, vc, ks, vs), tokens_per_split=tps,
+                             workspace=ws)
+            ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+            check_close(out, ref, f"reused workspace tps={tps}")
+    nb = 8 * 8 * 4      # counters of the largest (B, Hkv) used: all back to zero
+    assert int(ws[:nb].count_nonzero()) == 0
