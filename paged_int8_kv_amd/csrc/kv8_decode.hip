@@ -46,6 +46,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kPf = 4;        // blocks in flight per wave and pass
+constexpr int kMergeBatch = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SplitArgs {
@@ -512,17 +513,34 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   }
   __syncthreads();
   if (!s_flag[0]) return;
+  // Partials are read in batches of kMergeBatch splits whose loads are all
+  // issued before any is used (one memory round trip per batch), and folded
+  // in by an online log-sum-exp update.
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, c = e % D;
     const int64_t bh = bh0 + h;
     const float* lse = a.lse_part + bh * a.n_split;
-    float Mx = kNegInf;
-    for (int s = 0; s < nvalid; ++s) Mx = fmaxf(Mx, load_agent(lse + s));
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < nvalid; ++s) {
-      const float w = __builtin_amdgcn_exp2f(load_agent(lse + s) - Mx);
-      den += w;
-      num += w * load_agent(a.o_part + (bh * a.n_split + s) * D + c);
+    const float* op = a.o_part + bh * a.n_split * D + c;
+    float Mx = kNegInf, num = 0.0f, den = 0.0f;
+    for (int s0 = 0; s0 < nvalid; s0 += kMergeBatch) {
+      float lv[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = min(s0 + u, nvalid - 1);
+        lv[u] = load_agent(lse + s);
+        ov[u] = load_agent(op + (int64_t)s * D);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (s0 + u < nvalid) {
+          const float mn = fmaxf(Mx, lv[u]);
+          const float wo = __builtin_amdgcn_exp2f(Mx - mn);   // 0 while Mx = -inf
+          const float wn = __builtin_amdgcn_exp2f(lv[u] - mn);
+          num = num * wo + wn * ov[u];
+          den = den * wo + wn;
+          Mx = mn;
+        }
+      }
     }
     a.out[bh * D + c] = num / den;
   }
