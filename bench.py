@@ -23,6 +23,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix peak
 METRIC = "achieved HBM GB/s (% of peak) + KV-tokens/s, paged INT8-KV GQA decode attention"
 
 
@@ -35,6 +36,7 @@ def parse():
     p.add_argument("--tokens-per-split", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=4)
+    p.add_argument("--prefill-steps", type=int, default=20)
     return p.parse_args()
 
 
@@ -47,6 +49,17 @@ def decode_bytes(ctx, hkv, d, hq, q_bytes):
     kv = int(ctx.sum()) * 2 * hkv * (d + 2)
     table = 4 * int(np.sum((ctx + 15) // 16))
     return kv + b * hq * d * q_bytes + b * hq * d * 4 + table + 4 * b
+
+
+def prefill_flops(ctx, chunk, hq, d):
+    """Causal-aware FLOPs of one chunked-prefill call: row i of a chunk of
+    Lc rows sees ctx - Lc + i + 1 keys; QK^T and PV each cost 2*d per
+    (row, head, visible key)."""
+    total = 0
+    for c, lc in zip(np.asarray(ctx, np.int64), np.asarray(chunk, np.int64)):
+        vis = np.arange(c - lc, c) + 1
+        total += int(np.clip(vis, 0, None).sum())
+    return total * hq * d * 4
 
 
 def append_bytes(n, hkv, d):
@@ -163,12 +176,80 @@ def main():
         "append_us": {"mean": round(float(app_ms.mean()) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_decode_attn_kv8 (split + merge launches)",
+                     "kernel": "paged_decode_attn_kv8 (one launch, split-K + in-launch merge)",
                      "bytes_per_launch": d_bytes},
     }
+    del caches, ws, out
+    torch.cuda.empty_cache()
+    if args.prefill_steps > 0:
+        result["prefill"] = bench_prefill(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_steps, d_bytes + a_bytes)
     print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, dev):
+    """Chunked prefill over the INT8 cache (batch 8, 32/8 heads, d=128,
+    2048..8192 earlier tokens + a 512-row causal chunk): per step, append the
+    chunk's own K/V (4096 tokens), then paged_prefill_chunk_attn_kv8.  HIP
+    events on the stream the library launches on."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    from paged_int8_kv_amd import workloads as W
+    case = W.chunked_prefill()
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    chunk = case.extra["chunk"]
+    ctx = case.context_lens
+    mask = case.extra["chunk_mask"]
+    k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    cache = B.alloc_cache(case.num_blocks, hkv, d, dev)
+    B.kv8_quant_append(k_all, v_all, torch.from_numpy(case.slot_mapping).to(dev), *cache)
+    sel = torch.from_numpy(np.nonzero(mask)[0]).to(dev)
+    k_new = k_all.index_select(0, sel).contiguous()
+    v_new = v_all.index_select(0, sel).contiguous()
+    s_new = torch.from_numpy(case.slot_mapping[mask]).to(dev)
+    del k_all, v_all
+    q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qsl = torch.from_numpy(case.extra["q_start_loc"]).to(dev)
+    table = torch.from_numpy(case.block_table).to(dev)
+    lens = torch.from_numpy(ctx).to(dev)
+    out = torch.empty((q.shape[0], hq, d), dtype=torch.float32, device=dev)
+    max_ctx = int(ctx.max())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.kv8_quant_append(k_new, v_new, s_new, *cache)
+        if ev is not None:
+            ev[1].record()
+        B.paged_prefill_chunk_attn_kv8(q, qsl, chunk, *cache, table, lens, max_ctx, out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.prefill_steps)]
+    for i in range(args.prefill_steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pre = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    flops = prefill_flops(ctx, np.full(len(ctx), chunk), hq, d)
+    tf = flops / (float(pre.mean()) * 1e-3) / 1e12
+    return {"workload": "chunked prefill: B=8, Hq=32, Hkv=8, d=128, ctx_prev~U[2048,8192] + "
+                        "512-row causal chunk, bf16 Q, int8 KV cache",
+            "steps": args.prefill_steps,
+            "prefill_us": {"mean": round(float(pre.mean()) * 1e3, 2),
+                           "p50": round(float(np.percentile(pre, 50)) * 1e3, 2)},
+            "append_chunk_us": {"mean": round(float(app.mean()) * 1e3, 2)},
+            "flops_per_call": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "paged_prefill_chunk_attn_kv8 (fp16 MFMA 32x32x16)"}}
 
 
 def cpu_baseline(case, n_steps, step_bytes):

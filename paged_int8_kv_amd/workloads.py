@@ -218,3 +218,25 @@ def chunked_prefill(seed=5, batch=8, chunk=512, lo=2048, hi=8192,
     case.extra["chunk_mask"] = case.token_pos >= np.repeat(prev, prev + chunk)
     case.extra["chunk"] = chunk
     return case
+
+
+def prefill_case(ctx_prev, chunk_lens, *, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 seed=6, k_outliers=False, spare_blocks=0, permute=True):
+    """Ragged chunked prefill: sequence b holds ctx_prev[b] earlier tokens
+    and a chunk of chunk_lens[b] rows (0 allowed) whose K/V are in the cache
+    too, so context_lens = ctx_prev + chunk_lens.  Q rows of all chunks are
+    packed in sequence order; extra['q_start_loc'] [B+1], extra['max_q_len'].
+    bf16 Q/K/V N(0,1)."""
+    prev = np.asarray(ctx_prev, np.int64)
+    lens = np.asarray(chunk_lens, np.int64)
+    batch = len(prev)
+    case = make_paged_case(batch=batch, num_q_heads=num_q_heads,
+                           num_kv_heads=num_kv_heads, head_dim=head_dim,
+                           context_lens=prev + lens, q_dtype="bf16",
+                           q_rows=max(1, int(lens.sum())), seed=seed,
+                           k_outliers=k_outliers, spare_blocks=spare_blocks,
+                           permute=permute)
+    case.extra["ctx_prev"] = prev.astype(np.int32)
+    case.extra["q_start_loc"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    case.extra["max_q_len"] = int(lens.max()) if batch else 0
+    return case

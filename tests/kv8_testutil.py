@@ -96,3 +96,51 @@ def check_close(out, ref, what=""):
     assert max_abs <= MAX_ABS, f"{what}: max|delta| {max_abs:.3e} > {MAX_ABS}"
     assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e} > {REL_L2}"
     return max_abs, rel
+
+
+def gpu_prefill(case, cache, q=None, q_start_loc=None, context_lens=None, max_q_len=None,
+                block_table=None, max_context_len=None, sm_scale=None):
+    """Run paged_prefill_chunk_attn_kv8 on a prefill case (bf16 Q bits
+    [Tq, Hq, d]); returns fp32 [Tq, Hq, d] (NaN where the kernel wrote
+    nothing)."""
+    qsl = case.extra["q_start_loc"] if q_start_loc is None else q_start_loc
+    qsl = np.ascontiguousarray(qsl, np.int32)
+    bt = case.block_table if block_table is None else block_table
+    cl = case.context_lens if context_lens is None else context_lens
+    mcl = int(np.max(cl)) if max_context_len is None else max_context_len
+    mql = int(np.max(np.diff(qsl))) if max_q_len is None else max_q_len
+    qt = bits_tensor(case.q_bits if q is None else q).view(torch.bfloat16)
+    tq, hq, d = qt.shape
+    out = torch.full((tq, hq, d), float("nan"), dtype=torch.float32, device=dev())
+    B.paged_prefill_chunk_attn_kv8(
+        qt, torch.from_numpy(qsl).to(dev()), mql, *cache,
+        torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev()),
+        torch.from_numpy(np.ascontiguousarray(cl, np.int32)).to(dev()),
+        mcl, out, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_prefill_rows(case, cache_host, picks, q=None, context_lens=None):
+    """fp64 oracle output for selected (sequence b, chunk row i) pairs, all
+    query heads: the oracle's gather, causal rule and softmax applied to
+    those rows only.  Returns [len(picks), Hq, d]."""
+    kc, vc, ks, vs = cache_host
+    qv = case.q if q is None else q
+    cl = case.context_lens if context_lens is None else context_lens
+    qsl = case.extra["q_start_loc"]
+    hq, hkv = case.num_q_heads, case.num_kv_heads
+    G = hq // hkv
+    sm = 1.0 / np.sqrt(case.head_dim)
+    res = np.zeros((len(picks), hq, case.head_dim), np.float64)
+    for n, (b, i) in enumerate(picks):
+        ctx = int(cl[b])
+        lc = int(qsl[b + 1] - qsl[b])
+        vis = O.causal_visibility(ctx, lc)[i:i + 1]
+        for g in range(hkv):
+            k = O.gather_dequant(kc, ks, case.block_table[b], ctx, g)
+            v = O.gather_dequant(vc, vs, case.block_table[b], ctx, g)
+            for h in range(g * G, g * G + G):
+                qrow = np.asarray(qv[qsl[b] + i, h], np.float64)[None, :]
+                res[n, h] = O.softmax_attention(qrow, k, v, sm, vis)[0]
+    return res
