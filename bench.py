@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=4)
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain elementwise copy of known size (for HBM counters)")
     return p.parse_args()
 
 
@@ -49,6 +51,24 @@ def decode_bytes(ctx, hkv, d, hq, q_bytes):
     kv = int(ctx.sum()) * 2 * hkv * (d + 2)
     table = 4 * int(np.sum((ctx + 15) // 16))
     return kv + b * hq * d * q_bytes + b * hq * d * 4 + table + 4 * b
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` ('decode' or 'prefill') from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the
+    kernel's sources changed since those counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        info = json.load(open(os.path.join(root, "profiles", "hbm_traffic.json")))[kernel]
+        h = hashlib.sha256()
+        for f in info["sources"]:
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest()[:16] != info["sources_sha256_16"]:
+            return None
+        return int(info["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def prefill_flops(ctx, chunk, hq, d):
@@ -80,6 +100,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+        return
     case = W.llama8b_decode()
     bsz, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
     ctx = case.context_lens
@@ -175,7 +198,8 @@ def main():
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "append_us": {"mean": round(float(app_ms.mean()) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode"),
                      "kernel": "paged_decode_attn_kv8 (one launch, split-K + in-launch merge)",
                      "bytes_per_launch": d_bytes},
     }
@@ -248,8 +272,23 @@ def bench_prefill(args, dev):
             "flops_per_call": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": measured_traffic("prefill"),
                          "kernel": "paged_prefill_chunk_attn_kv8 (fp16 MFMA 32x32x16)"}}
+
+
+def calibrate_copy(dev, n_bytes=256 << 20, launches=5):
+    """A plain elementwise kernel that reads n_bytes and writes n_bytes per
+    launch: the reference against which the HBM byte counters (FETCH_SIZE,
+    WRITE_SIZE) of the attention kernels are scaled."""
+    import torch
+    x = torch.ones(n_bytes // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(launches):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy y = x * 1.0 (fp32)",
+                      "bytes_read_per_launch": n_bytes, "bytes_written_per_launch": n_bytes,
+                      "launches": launches}), flush=True)
 
 
 def cpu_baseline(case, n_steps, step_bytes):
