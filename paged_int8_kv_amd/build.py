@@ -34,6 +34,13 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
+# ordinary VGPRs: with the accumulator-register form the compiler copied all
+# 128 accumulators between register files on every key tile.
+EXTRA_FLAGS = {
+    "kv8_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
 
 def hipcc_path():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -44,7 +51,8 @@ def hipcc_path():
 
 def _compile(hipcc, src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,11 +10,12 @@
 // accumulation run in fp32 ("大模型推理加速：KV Cache与vLLM技术解析",
 // section 4.1).
 //
-// Work split: one workgroup of 4 waves per (sequence b, KV head g, tile of
+// Work split: one workgroup of 8 waves per (sequence b, KV head g, tile of
 // 256 queries).  A query is a (chunk row, head of the group) pair with the
 // G heads innermost, so every K/V byte staged by the workgroup serves all G
-// heads of its group.  Each wave owns 64 queries: two 32-query column
-// blocks of the MFMA output.
+// heads of its group.  Each wave owns 32 queries (one 32-column block of the
+// MFMA output) and keeps their Q operands in registers; at two waves per
+// SIMD one wave's softmax overlaps the other's matrix work.
 //
 // Key tiles of 64 tokens (4 cache blocks) are staged once per workgroup in
 // LDS, double-buffered (the next tile's codes are loaded into registers
@@ -34,8 +35,10 @@
 //                     bf16 q is exact in fp16 (max |q| in [2^14, 2^15));
 //   z = S^T * (k_scale[key] * sm_scale * log2(e)) * 2^-e_q; the last factor
 //       is exact, so the largest z of a row gives 2^0 = 1 exactly;
-//   online softmax in base 2: running max m_q and sum l_q per query; the
-//   accumulator is rescaled only when some running max of the wave grew;
+//   online softmax in base 2: running max m_q and sum l_q per query; m_q
+//   moves (and the accumulator is rescaled) only when the tile's max exceeds
+//   it by more than kSlack, so 2^(z - m_q) <= 2^kSlack (exactly when the tile
+//   holds a large v_scale);
 //   w = 2^(z - m_q) * v_scale[key], rounded to fp16;
 //   O^T[channel][query] += V_code^T . W^T.
 // The output is O / l (0 for a query with no visible key).
@@ -53,12 +56,18 @@ namespace kv8 {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kQueriesPerWave = 64;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kQueriesPerWave = 32;
 constexpr int kQueriesPerGroup = kWaves * kQueriesPerWave;   // 256
 constexpr int kTileKeys = 64;                                // 4 cache blocks
 constexpr float kLog2e = 1.4426950408889634f;
+// A row's running max is moved (and the accumulator rescaled) only when the
+// tile max exceeds it by more than kSlack (log2 units), so weights p may
+// reach 2^kSlack.  Tiles holding a v_scale >= kBigVScale rescale exactly
+// instead, so that p * v_scale always stays below the fp16 maximum.
+constexpr float kSlack = 8.0f;
+constexpr float kBigVScale = 128.0f;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -79,6 +88,8 @@ struct PrefillArgs {
   int ctx_cap;
   int num_q_heads;
   int num_kv_heads;
+  int batch;
+  int tiles_per_pair;      // query tiles per (sequence, KV head)
   float sm_scale_log2;     // sm_scale * log2(e)
 };
 
@@ -90,7 +101,16 @@ struct __attribute__((aligned(16))) Lds {
   _Float16 v[2][D][kVRow];
   float ks[2][kTileKeys];
   float vs[2][kTileKeys];
+  int big_vs[2];                                // some v_scale of the tile >= kBigVScale
 };
+
+// V^T rows hold 8 chunks of 8 keys (16 bytes); chunk c of row r is stored at
+// c ^ vt_swizzle(r), which makes both the staging writes (rows 4 apart) and
+// the operand reads (consecutive rows) free of LDS bank conflicts on the
+// 64-bank LDS (16 lanes served per cycle for 16-byte accesses).
+__device__ __forceinline__ int vt_swizzle(int row) {
+  return (((row >> 4) & 1) << 1) | ((row >> 5) & 1);
+}
 
 __device__ __forceinline__ half8_t as_half8(uint4 u) { return __builtin_bit_cast(half8_t, u); }
 
@@ -116,12 +136,17 @@ __device__ __forceinline__ float wave_sum32(float x) {
 }
 
 // Registers holding one key tile's codes and scales on their way to LDS.
+// K: thread t holds key t/8, channels (t%8)*d/8 ... +d/8.  V: task t (t < d,
+// four per channel quad and 16-key group) holds 4 keys x 4 channels: the
+// keys 16grp + 8a + 4hh + {0..3}, which sit at positions 8hh + 4a + {0..3}
+// of their group in the transposed layout.  Scales: threads 0..63 K,
+// 64..127 (wave 1) V.
 template <int D>
 struct Stage {
-  static constexpr int kKVec = D / 64;          // uint4 of K codes per thread
-  static constexpr int kVTasks = 2 * D;         // (8-key group, channel quad) tasks
-  uint4 k[kKVec];
-  uint32_t v[8];
+  static constexpr int kKBytes = D / 8;         // K code bytes per thread (16 or 8)
+  static constexpr int kVTasks = 4 * D;         // 512 (d=128) or 256 (d=64)
+  uint32_t k[kKBytes / 4];
+  uint32_t v[4];
   uint16_t sc;
 };
 
@@ -137,28 +162,28 @@ template <int D>
 __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* table_row,
                                            int kt, int last_blk, int g, int tid,
                                            Stage<D>& st) {
-  // K: key tid/4, channel part tid%4 of D/4 bytes
   {
-    const int key = tid >> 2, part = tid & 3;
+    const int key = tid >> 3, part = tid & 7;
     const int64_t slab = block_base<D>(a, table_row, kt * 4 + (key >> 4), last_blk, g);
-    const uint4* src = reinterpret_cast<const uint4*>(
-        a.k_cache + slab * (kBlock * D) + (key & 15) * D + part * (D / 4));
-#pragma unroll
-    for (int i = 0; i < Stage<D>::kKVec; ++i) st.k[i] = src[i];
-  }
-  // V: 8 rows x 4 channels per task; rows 4hh+{0..3}, 8+4hh+{0..3} of group grp
-  if (tid < Stage<D>::kVTasks) {
-    const int cq = tid % (D / 4), kg = tid / (D / 4);
-    const int grp = kg >> 1, hh = kg & 1;
-    const int64_t slab = block_base<D>(a, table_row, kt * 4 + grp, last_blk, g);
-    const int8_t* base = a.v_cache + slab * (kBlock * D) + cq * 4;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = 4 * hh + (r & 3) + 8 * (r >> 2);
-      st.v[r] = *reinterpret_cast<const uint32_t*>(base + row * D);
+    const int8_t* src = a.k_cache + slab * (kBlock * D) + (key & 15) * D + part * (D / 8);
+    if constexpr (D == 128) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      st.k[0] = u.x; st.k[1] = u.y; st.k[2] = u.z; st.k[3] = u.w;
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(src);
+      st.k[0] = u.x; st.k[1] = u.y;
     }
   }
-  // scales: threads 0..63 K, 64..127 V
+  if (tid < Stage<D>::kVTasks) {
+    const int cq = tid % (D / 4), kq = tid / (D / 4);
+    const int grp = kq >> 2, sub = kq & 3;
+    const int64_t slab = block_base<D>(a, table_row, kt * 4 + grp, last_blk, g);
+    const int8_t* base = a.v_cache + slab * (kBlock * D) + cq * 4;
+    const int row0 = 8 * (sub >> 1) + 4 * (sub & 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      st.v[r] = *reinterpret_cast<const uint32_t*>(base + (row0 + r) * D);
+  }
   if (tid < 2 * kTileKeys) {
     const int key = tid & 63;
     const int64_t slab = block_base<D>(a, table_row, kt * 4 + (key >> 4), last_blk, g);
@@ -171,63 +196,132 @@ template <int D>
 __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_keys, int tid,
                                             float k_mult, const Stage<D>& st) {
   {
-    const int key = tid >> 2, part = tid & 3;
-    _Float16* dst = &lds.k[buf][key][part * (D / 4)];
+    const int key = tid >> 3, part = tid & 7;
+    uint32_t o[Stage<D>::kKBytes / 2];
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kKVec; ++i) {
-      const uint32_t w[4] = {st.k[i].x, st.k[i].y, st.k[i].z, st.k[i].w};
-      uint32_t o[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half2_t lo, hi;
-        codes_to_f16(w[j], lo, hi);
-        o[2 * j] = h2_bits(lo);
-        o[2 * j + 1] = h2_bits(hi);
-      }
-      reinterpret_cast<uint4*>(dst)[2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
-      reinterpret_cast<uint4*>(dst)[2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int j = 0; j < Stage<D>::kKBytes / 4; ++j) {
+      half2_t lo, hi;
+      codes_to_f16(st.k[j], lo, hi);
+      o[2 * j] = h2_bits(lo);
+      o[2 * j + 1] = h2_bits(hi);
     }
+    uint4* dst = reinterpret_cast<uint4*>(&lds.k[buf][key][part * (D / 8)]);
+#pragma unroll
+    for (int i = 0; i < Stage<D>::kKBytes / 8; ++i)
+      dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
   if (tid < Stage<D>::kVTasks) {
-    const int cq = tid % (D / 4), kg = tid / (D / 4);
-    const int grp = kg >> 1, hh = kg & 1;
-    // [r0.c, r1.c, r0.c', r1.c'] for the row pairs (0,1) (2,3) (4,5) (6,7)
-    uint32_t plo[4], phi[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      plo[p] = interleave_lo(st.v[2 * p], st.v[2 * p + 1]) ^ kXor80;
-      phi[p] = interleave_hi(st.v[2 * p], st.v[2 * p + 1]) ^ kXor80;
-    }
+    const int cq = tid % (D / 4), kq = tid / (D / 4);
+    const int grp = kq >> 2, sub = kq & 3;
+    const int a4 = sub >> 1, hh = sub & 1;
+    // 4 rows x 4 channel bytes -> per channel the 4 rows' codes
+    const uint32_t t01l = interleave_lo(st.v[0], st.v[1]) ^ kXor80;   // [r0c0 r1c0 r0c1 r1c1]
+    const uint32_t t01h = interleave_hi(st.v[0], st.v[1]) ^ kXor80;   // [r0c2 r1c2 r0c3 r1c3]
+    const uint32_t t23l = interleave_lo(st.v[2], st.v[3]) ^ kXor80;
+    const uint32_t t23h = interleave_hi(st.v[2], st.v[3]) ^ kXor80;
     const half2_t bias = {(_Float16)kCodeBias, (_Float16)kCodeBias};
 #pragma unroll
     for (int ci = 0; ci < 4; ++ci) {
-      uint32_t o[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t src = (ci < 2) ? plo[p] : phi[p];
-        const half2_t h = ((ci & 1) ? biased_pair_hi(src) : biased_pair_lo(src)) - bias;
-        o[p] = h2_bits(h);
-      }
-      *reinterpret_cast<uint4*>(&lds.v[buf][cq * 4 + ci][grp * 16 + hh * 8]) =
-          make_uint4(o[0], o[1], o[2], o[3]);
+      const uint32_t x01 = ci < 2 ? t01l : t01h, x23 = ci < 2 ? t23l : t23h;
+      const half2_t p01 = ((ci & 1) ? biased_pair_hi(x01) : biased_pair_lo(x01)) - bias;
+      const half2_t p23 = ((ci & 1) ? biased_pair_hi(x23) : biased_pair_lo(x23)) - bias;
+      const int row = cq * 4 + ci;
+      *reinterpret_cast<uint2*>(
+          &lds.v[buf][row][8 * ((grp * 2 + hh) ^ vt_swizzle(row)) + 4 * a4]) =
+          make_uint2(h2_bits(p01), h2_bits(p23));
     }
   }
   if (tid < 2 * kTileKeys) {
     const int key = tid & 63;
     const float s = (kt * kTileKeys + key < n_keys) ? fp16_bits_to_f32(st.sc) : 0.0f;
-    if (tid < kTileKeys) lds.ks[buf][key] = s * k_mult;
-    else lds.vs[buf][key] = s;
+    if (tid < kTileKeys) {
+      lds.ks[buf][key] = s * k_mult;
+    } else {
+      lds.vs[buf][key] = s;
+      // threads 64..127 are exactly wave 1: one ballot covers the tile
+      const bool big = __builtin_amdgcn_ballot_w64(!(s < kBigVScale)) != 0;
+      if (key == 0) lds.big_vs[buf] = big;
+    }
   }
 }
 
+// Online softmax of one 64-key tile for the lane's query: scales the raw
+// scores S^T by k_scale (sm_scale * log2(e) folded in) and the exact
+// per-query 2^-e, applies the causal rule when MASK, moves the running max
+// (rescaling the accumulator) when the slack rule asks for it, and returns
+// the fp16 weights 2^(z - m) * v_scale as the PV B operands.  The lane's
+// keys in 32-key block kb are 32kb + 8a + 4h + i for S register r = 4a + i.
+template <bool MASK, int CB>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&sc)[2], const float* ks, const float* vs,
+                                             int h, int key0, int qpos, float cq, bool big_tile,
+                                             float& mrun, float& lrun, f32x16_t (&acc)[CB],
+                                             half8_t (&pw)[2][2]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(ks + 32 * kb + 8 * a4 + 4 * h);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * a4 + i;
+        float x = sc[kb][r] * kv[i];
+        if (MASK) x = (key0 + 32 * kb + 8 * a4 + 4 * h + i > qpos) ? kNegInf : x;
+        sc[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+  mx = wave_max32(mx);
+  const float mcand = mx * cq;
+  const bool grow = mcand > mrun + (big_tile ? 0.0f : kSlack);
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float mnew = grow ? mcand : mrun;
+    const float alpha = mnew == mrun ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+    lrun *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+    mrun = mnew;
+  }
+  const float muse = mrun == kNegInf ? 0.0f : mrun;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(vs + 32 * kb + 8 * a4 + 4 * h);
+      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * a4 + i;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], cq, -muse));
+        lsum += p;
+        pw[kb][r >> 3][r & 7] = (_Float16)(p * vv[i]);
+      }
+    }
+  lrun += lsum;
+}
+
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;        // k-steps of the QK^T product
   constexpr int CB = D / 32;        // 32-channel blocks of the output
   constexpr int kRowsPerTile = kQueriesPerGroup / G;
   __shared__ Lds<D> lds;
 
-  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: workgroup id L runs on XCD L % 8, so pair p = (b, g)
+  // takes ids with L % 8 == p % 8 and its query tiles are consecutive among
+  // them: all tiles of a pair share one XCD's L2 and run at about the same
+  // time, so the pair's K/V is fetched from HBM about once.
+  const int L = blockIdx.x;
+  const int tiles = a.tiles_per_pair;
+  const int k8 = L >> 3;
+  const int pair = ((k8 / tiles) << 3) + (L & 7);
+  const int tile = k8 % tiles;
+  if (pair >= a.batch * a.num_kv_heads) return;                  // padding
+  const int b = pair / a.num_kv_heads, g = pair % a.num_kv_heads;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int m = lane & 31, h = lane >> 5;
@@ -250,23 +344,19 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   Stage<D> st;
   if (nkt > 0) stage_load<D>(a, table_row, 0, last_blk, g, tid, st);
 
-  // ---- this lane's queries: load Q, exact fp16 after a power-of-two scale --
-  half8_t qf[2][KS];
-  float cq[2];
-  int qpos[2], qrow[2], qhead[2];
-  bool qvalid[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int nq = wave * kQueriesPerWave + qb * 32 + m;
-    const int row = row_begin + nq / G;
-    qrow[qb] = row;
-    qhead[qb] = g * G + nq % G;
-    qvalid[qb] = row < row_end;
-    qpos[qb] = pos0 + row;
+  // ---- this lane's query: load Q, exact fp16 after a power-of-two scale ----
+  const int nq = wave * kQueriesPerWave + m;
+  const int qrow = row_begin + nq / G;
+  const int qhead = g * G + nq % G;
+  const bool qvalid = qrow < row_end;
+  const int qpos = pos0 + qrow;
+  half8_t qf[KS];
+  float cq;
+  {
     uint4 raw[KS];
-    if (qvalid[qb]) {
+    if (qvalid) {
       const uint4* src = reinterpret_cast<const uint4*>(
-          a.q + ((int64_t)(r0 + row) * a.num_q_heads + qhead[qb]) * D + (D / 2) * h);
+          a.q + ((int64_t)(r0 + qrow) * a.num_q_heads + qhead) * D + (D / 2) * h);
 #pragma unroll
       for (int s = 0; s < KS; ++s) raw[s] = src[s];
     } else {
@@ -291,16 +381,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
       e = 15 - ex;                     // mx * 2^e in [2^14, 2^15)
       e = e > 120 ? 120 : (e < -120 ? -120 : e);
     }
-    cq[qb] = ldexpf(1.0f, -e);         // exact: z = x * cq rounds nowhere
+    cq = ldexpf(1.0f, -e);             // exact: z = x * cq rounds nowhere
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qf[qb][s][2 * j] =
-            (_Float16)ldexpf(__builtin_bit_cast(float, w[j] << 16), e);
-        qf[qb][s][2 * j + 1] =
-            (_Float16)ldexpf(__builtin_bit_cast(float, w[j] & 0xFFFF0000u), e);
+        qf[s][2 * j] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] << 16), e);
+        qf[s][2 * j + 1] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] & 0xFFFF0000u), e);
       }
     }
   }
@@ -312,14 +400,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   const int wave_pos_lo = pos0 + wave_row_lo;   // smallest position of the wave
   const int wave_pos_hi = pos0 + wave_row_hi;   // largest
 
-  f32x16_t acc[CB][2];
+  f32x16_t acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][qb][r] = 0.0f;
-  float mrun[2] = {kNegInf, kNegInf}, lrun[2] = {0.0f, 0.0f};
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+  float mrun = kNegInf, lrun = 0.0f;
 
   if (nkt > 0) stage_store<D>(lds, 0, 0, n_keys, tid, a.sm_scale_log2, st);
   __syncthreads();
@@ -332,87 +418,40 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
     const int key0 = kt * kTileKeys;
     if (wave_live && key0 <= wave_pos_hi) {
       const bool live1 = key0 + 32 <= wave_pos_hi;   // second 32-key block visible
-      // ---- S^T = K . Q^T ---------------------------------------------------
-      f32x16_t sacc[2][2];
+      // ---- S^T = K . Q^T: 64 keys x 32 queries ------------------------------
+      f32x16_t sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+      const _Float16* krow0 = &lds.k[buf][m][(D / 2) * h];
+      const _Float16* krow1 = krow0 + 32 * Lds<D>::kRow;
+      if (live1) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && !live1) break;
-        half8_t ka[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          ka[s] = as_half8(*reinterpret_cast<const uint4*>(
-              &lds.k[buf][kb * 32 + m][(D / 2) * h + 8 * s]));
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s], qf[qb][s],
-                                                                  sacc[kb][qb], 0, 0, 0);
-      }
-      // ---- online softmax (base 2) and fp16 weights, one query block at a time.
-      // Lane keys of a 32-key block: 8a + 4h + i for register r = 4a + i.
-      const bool need_mask = key0 + kTileKeys - 1 > wave_pos_lo;
-      half8_t pw[2][2][2];     // [qb][kb][k-step]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const float4 k4 =
-                *reinterpret_cast<const float4*>(&lds.ks[buf][kb * 32 + 8 * a4 + 4 * h]);
-            const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * a4 + i;
-              float x = sacc[kb][qb][r] * kv[i];
-              if (need_mask) {
-                const int key = key0 + kb * 32 + 8 * a4 + 4 * h + i;
-                x = key > qpos[qb] ? kNegInf : x;
-              }
-              if (kb == 1 && !live1) x = kNegInf;
-              sacc[kb][qb][r] = x;
-              mx = fmaxf(mx, x);
-            }
-          }
-        mx = wave_max32(mx);
-        const float mnew = fmaxf(mrun[qb], mx * cq[qb]);
-        if (__builtin_amdgcn_ballot_w64(mnew > mrun[qb]) != 0) {
-          const float alpha = mnew == mrun[qb] ? 1.0f : __builtin_amdgcn_exp2f(mrun[qb] - mnew);
-          lrun[qb] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[cb][qb][r] *= alpha;
-          mrun[qb] = mnew;
+        for (int s = 0; s < KS; ++s) {
+          const half8_t k0 = *reinterpret_cast<const half8_t*>(krow0 + 8 * s);
+          const half8_t k1 = *reinterpret_cast<const half8_t*>(krow1 + 8 * s);
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[s], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[s], sacc[1], 0, 0, 0);
         }
-        const float muse = mrun[qb] == kNegInf ? 0.0f : mrun[qb];
-        float lsum = 0.0f;
+      } else {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const float4 v4 =
-                *reinterpret_cast<const float4*>(&lds.vs[buf][kb * 32 + 8 * a4 + 4 * h]);
-            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * a4 + i;
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][r], cq[qb], -muse));
-              lsum += p;
-              pw[qb][kb][r >> 3][r & 7] = (_Float16)(p * vv[i]);
-            }
-          }
-        lrun[qb] += lsum;
+        for (int s = 0; s < KS; ++s) {
+          const half8_t k0 = *reinterpret_cast<const half8_t*>(krow0 + 8 * s);
+          sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[s], sacc[0], 0, 0, 0);
+        }
       }
-      // ---- O^T += V^T . W^T ----------------------------------------------------
+      // ---- online softmax and fp16 weights -------------------------------------
+      const bool need_mask = key0 + kTileKeys - 1 > wave_pos_lo;
+      const bool big_tile = lds.big_vs[buf] != 0;
+      half8_t pw[2][2];     // [kb][k-step]
+      if (need_mask)
+        softmax_tile<true, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, cq, big_tile,
+                               mrun, lrun, acc, pw);
+      else
+        softmax_tile<false, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, cq, big_tile,
+                                mrun, lrun, acc, pw);
+      // ---- O^T += V^T . W^T ------------------------------------------------------
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb == 1 && !live1) break;
@@ -422,13 +461,10 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
             va[cb] = as_half8(*reinterpret_cast<const uint4*>(
-                &lds.v[buf][cb * 32 + m][kb * 32 + 16 * j + 8 * h]));
+                &lds.v[buf][cb * 32 + m][8 * ((4 * kb + 2 * j + h) ^ vt_swizzle(cb * 32 + m))]));
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              acc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cb], pw[qb][kb][j],
-                                                                   acc[cb][qb], 0, 0, 0);
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cb], pw[kb][j], acc[cb], 0, 0, 0);
         }
       }
     }
@@ -438,30 +474,31 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l, channel 32cb + 8(r/4) + 4h + r%4 --------------------
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l = wave_sum32(lrun[qb]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (!qvalid[qb]) continue;
-    float* dst = a.out + ((int64_t)(r0 + qrow[qb]) * a.num_q_heads + qhead[qb]) * D + 4 * h;
+  const float l = wave_sum32(lrun);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qvalid) {
+    float* dst = a.out + ((int64_t)(r0 + qrow) * a.num_q_heads + qhead) * D + 4 * h;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int r = 4 * a4;
         *reinterpret_cast<float4*>(dst + cb * 32 + 8 * a4) =
-            make_float4(acc[cb][qb][r] * inv, acc[cb][qb][r + 1] * inv,
-                        acc[cb][qb][r + 2] * inv, acc[cb][qb][r + 3] * inv);
+            make_float4(acc[cb][r] * inv, acc[cb][r + 1] * inv, acc[cb][r + 2] * inv,
+                        acc[cb][r + 3] * inv);
       }
   }
 }
 
 template <int D, int G>
-int launch_dg(const PrefillArgs& a, int batch, int max_q_len, hipStream_t stream) {
+int launch_dg(PrefillArgs a, int batch, int max_q_len, hipStream_t stream) {
   const int64_t tiles = ((int64_t)max_q_len * G + kQueriesPerGroup - 1) / kQueriesPerGroup;
-  if (tiles > 0x7FFFFFFF) return -1;
-  dim3 grid((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)batch);
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(kThreads), 0, stream, a);
+  const int64_t pairs8 = ((int64_t)batch * a.num_kv_heads + 7) / 8 * 8;
+  if (tiles * pairs8 > 0x7FFFFFFF) return -2;
+  a.tiles_per_pair = (int)tiles;
+  a.batch = batch;
+  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)(tiles * pairs8)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
