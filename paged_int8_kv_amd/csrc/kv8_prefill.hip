@@ -31,10 +31,11 @@
 // of 1152 leaves c exactly.
 //
 // Per wave and key tile (v_mfma_f32_32x32x16_f16, fp32 accumulate):
-//   S^T[key][query] = K_code . Q^T, with Q scaled per query by 2^e_q so that
-//                     bf16 q is exact in fp16 (max |q| in [2^14, 2^15));
-//   z = S^T * (k_scale[key] * sm_scale * log2(e)) * 2^-e_q; the last factor
-//       is exact, so the largest z of a row gives 2^0 = 1 exactly;
+//   S^T[key][query] = K_code . Q^T, with Q scaled by one power of two 2^e
+//                     per workgroup so that bf16 q is exact in fp16 (the
+//                     workgroup's max |q| in [2^14, 2^15));
+//   z = S^T * (k_scale[key] * sm_scale * log2(e) * 2^-e), the factor staged
+//       with the scales; a row whose max moves gets 2^0 = 1 exactly;
 //   online softmax in base 2: running max m_q and sum l_q per query; m_q
 //   moves (and the accumulator is rescaled) only when the tile's max exceeds
 //   it by more than kSlack, so 2^(z - m_q) <= 2^kSlack (exactly when the tile
@@ -102,6 +103,7 @@ struct __attribute__((aligned(16))) Lds {
   float ks[2][kTileKeys];
   float vs[2][kTileKeys];
   int big_vs[2];                                // some v_scale of the tile >= kBigVScale
+  float qmax[kWaves];                           // per-wave max |q| (prologue)
 };
 
 // V^T rows hold 8 chunks of 8 keys (16 bytes); chunk c of row r is stored at
@@ -245,17 +247,49 @@ __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_
   }
 }
 
-// Online softmax of one 64-key tile for the lane's query: scales the raw
-// scores S^T by k_scale (sm_scale * log2(e) folded in) and the exact
-// per-query 2^-e, applies the causal rule when MASK, moves the running max
-// (rescaling the accumulator) when the slack rule asks for it, and returns
-// the fp16 weights 2^(z - m) * v_scale as the PV B operands.  The lane's
-// keys in 32-key block kb are 32kb + 8a + 4h + i for S register r = 4a + i.
+// Online softmax of one 64-key tile for the lane's query.  ks holds
+// k_scale * sm_scale * log2(e) * 2^-e (e: the workgroup's Q exponent), so
+// z = S^T * ks is the logit in log2 units; vs holds v_scale.  Returns the
+// fp16 weights 2^(z - m) * v_scale as the PV B operands.  The lane's keys in
+// 32-key block kb are 32kb + 8a + 4h + i for S register r = 4a + i.
+//
+// Fast path (no causal mask, no large v_scale, every running max already
+// set): p = 2^fma(S, ks, -m) with the current maxima, accepted when every
+// lane's tile sum of p is <= 256, which bounds each p and keeps p * v_scale
+// in fp16 range.  Otherwise the exact path runs: z = S * ks, the tile max,
+// and the slack rule (a lane's max moves, rescaling its accumulator, when
+// the tile max exceeds it by more than kSlack, or at all on a tile with a
+// large v_scale).  A lane that moved its max uses 2^(z - m), so its largest
+// weight is exactly 1; every other lane uses the fast path's formula, so a
+// lane's result never depends on which path its wave took.
 template <bool MASK, int CB>
 __device__ __forceinline__ void softmax_tile(f32x16_t (&sc)[2], const float* ks, const float* vs,
-                                             int h, int key0, int qpos, float cq, bool big_tile,
+                                             int h, int key0, int qpos, bool big_tile,
                                              float& mrun, float& lrun, f32x16_t (&acc)[CB],
                                              half8_t (&pw)[2][2]) {
+  if (!MASK && !big_tile && __builtin_amdgcn_ballot_w64(mrun == kNegInf) == 0) {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(ks + 32 * kb + 8 * a4 + 4 * h);
+        const float4 v4 = *reinterpret_cast<const float4*>(vs + 32 * kb + 8 * a4 + 4 * h);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * a4 + i;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], kv[i], -mrun));
+          lsum += p;
+          pw[kb][r >> 3][r & 7] = (_Float16)(p * vv[i]);
+        }
+      }
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= 256.0f)) == 0) {
+      lrun += lsum;
+      return;
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -265,18 +299,15 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&sc)[2], const float* ks,
       const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 4 * a4 + i;
-        float x = sc[kb][r] * kv[i];
+        float x = sc[kb][4 * a4 + i] * kv[i];
         if (MASK) x = (key0 + 32 * kb + 8 * a4 + 4 * h + i > qpos) ? kNegInf : x;
-        sc[kb][r] = x;
         mx = fmaxf(mx, x);
       }
     }
   mx = wave_max32(mx);
-  const float mcand = mx * cq;
-  const bool grow = mcand > mrun + (big_tile ? 0.0f : kSlack);
+  const bool grow = mx > mrun + (big_tile ? 0.0f : kSlack);
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    const float mnew = grow ? mcand : mrun;
+    const float mnew = grow ? mx : mrun;
     const float alpha = mnew == mrun ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
     lrun *= alpha;
 #pragma unroll
@@ -291,12 +322,23 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&sc)[2], const float* ks,
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(ks + 32 * kb + 8 * a4 + 4 * h);
       const float4 v4 = *reinterpret_cast<const float4*>(vs + 32 * kb + 8 * a4 + 4 * h);
+      const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
       const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * a4 + i;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], cq, -muse));
+        const float sv = sc[kb][r];
+        float exact;
+        {
+          // the rounded product, as the max saw it, minus the max: no fma
+#pragma clang fp contract(off)
+          exact = sv * kv[i] - muse;
+        }
+        float arg = grow ? exact : __builtin_fmaf(sv, kv[i], -muse);
+        if (MASK) arg = (key0 + 32 * kb + 8 * a4 + 4 * h + i > qpos) ? kNegInf : arg;
+        const float p = __builtin_amdgcn_exp2f(arg);
         lsum += p;
         pw[kb][r >> 3][r & 7] = (_Float16)(p * vv[i]);
       }
@@ -311,16 +353,39 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   constexpr int kRowsPerTile = kQueriesPerGroup / G;
   __shared__ Lds<D> lds;
 
-  // XCD-aware order: workgroup id L runs on XCD L % 8, so pair p = (b, g)
-  // takes ids with L % 8 == p % 8 and its query tiles are consecutive among
-  // them: all tiles of a pair share one XCD's L2 and run at about the same
-  // time, so the pair's K/V is fetched from HBM about once.
+  // XCD-aware, longest-first order.  Workgroup id L runs on XCD L % 8; pair
+  // p = (b, g) is served by the XCD p % 8, so all query tiles of a pair share
+  // that XCD's L2 and its K/V is fetched from HBM about once.  Within an XCD
+  // the k-th workgroup (k = L / 8) takes the pair of rank k / tiles when the
+  // XCD's pairs are ordered by decreasing context length (longest first
+  // balances the CUs), and its tiles from the last (most keys) down.  Every
+  // workgroup computes the same ranks, so the map is a bijection.
   const int L = blockIdx.x;
   const int tiles = a.tiles_per_pair;
-  const int k8 = L >> 3;
-  const int pair = ((k8 / tiles) << 3) + (L & 7);
-  const int tile = k8 % tiles;
-  if (pair >= a.batch * a.num_kv_heads) return;                  // padding
+  const int npairs = a.batch * a.num_kv_heads;
+  const int xcd = L & 7, kx = L >> 3;
+  const int npx = (npairs - xcd + 7) >> 3;                      // pairs on this XCD
+  const int prank = kx / tiles;
+  const int tile = tiles - 1 - kx % tiles;
+  if (prank >= npx) return;                                      // padding
+  int pair = xcd + 8 * prank;
+  if (npx > 1 && npx <= 64) {
+    const int ln = threadIdx.x & 63;
+    int cost = -1;
+    if (ln < npx) {
+      const int bb = (xcd + 8 * ln) / a.num_kv_heads;
+      const int c = a.context_lens[bb];
+      const bool has_rows = a.q_start_loc[bb + 1] > a.q_start_loc[bb];
+      cost = has_rows ? (c < a.ctx_cap ? c : a.ctx_cap) : -1;
+    }
+    int rank = 0;
+    for (int j = 0; j < npx; ++j) {
+      const int cj = __builtin_amdgcn_readlane(cost, j);
+      rank += (cj > cost || (cj == cost && j < ln)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(ln < npx && rank == prank);
+    pair = xcd + 8 * (int)__builtin_ctzll(hit);
+  }
   const int b = pair / a.num_kv_heads, g = pair % a.num_kv_heads;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -350,19 +415,22 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int qhead = g * G + nq % G;
   const bool qvalid = qrow < row_end;
   const int qpos = pos0 + qrow;
+  // One power-of-two exponent e for the whole workgroup: max |q| over its
+  // 256 queries lands in [2^14, 2^15), so bf16 q is exact in fp16 (bits far
+  // below the workgroup's largest element aside) and the factor 2^-e folds
+  // into the staged k_scale.
   half8_t qf[KS];
-  float cq;
+  uint4 raw[KS];
+  if (qvalid) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        a.q + ((int64_t)(r0 + qrow) * a.num_q_heads + qhead) * D + (D / 2) * h);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) raw[s] = src[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) raw[s] = make_uint4(0, 0, 0, 0);
+  }
   {
-    uint4 raw[KS];
-    if (qvalid) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          a.q + ((int64_t)(r0 + qrow) * a.num_q_heads + qhead) * D + (D / 2) * h);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) raw[s] = src[s];
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) raw[s] = make_uint4(0, 0, 0, 0);
-    }
     float mx = 0.0f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -373,24 +441,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
         mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w[j] & 0xFFFF0000u)));
       }
     }
-    mx = wave_max32(mx);
-    int e = 0;
-    if (mx > 0.0f) {
-      int ex;
-      frexpf(mx, &ex);                 // mx = f * 2^ex, f in [0.5, 1)
-      e = 15 - ex;                     // mx * 2^e in [2^14, 2^15)
-      e = e > 120 ? 120 : (e < -120 ? -120 : e);
-    }
-    cq = ldexpf(1.0f, -e);             // exact: z = x * cq rounds nowhere
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qf[s][2 * j] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] << 16), e);
-        qf[s][2 * j + 1] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] & 0xFFFF0000u), e);
-      }
-    }
+    mx = across_groups_max(group8_max(mx));
+    if (lane == 0) lds.qmax[wave] = mx;
   }
   // wave-uniform causal bounds of this wave's valid queries
   const int wave_row_lo = row_begin + (wave * kQueriesPerWave) / G;
@@ -407,7 +459,31 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
   float mrun = kNegInf, lrun = 0.0f;
 
-  if (nkt > 0) stage_store<D>(lds, 0, 0, n_keys, tid, a.sm_scale_log2, st);
+  __syncthreads();
+  float k_mult;
+  {
+    float mx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, lds.qmax[w]);
+    int e = 0;
+    if (mx > 0.0f) {
+      int ex;
+      frexpf(mx, &ex);                 // mx = f * 2^ex, f in [0.5, 1)
+      e = 15 - ex;                     // mx * 2^e in [2^14, 2^15)
+      e = e > 120 ? 120 : (e < -120 ? -120 : e);
+    }
+    k_mult = ldexpf(a.sm_scale_log2, -e);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t w[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qf[s][2 * j] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] << 16), e);
+        qf[s][2 * j + 1] = (_Float16)ldexpf(__builtin_bit_cast(float, w[j] & 0xFFFF0000u), e);
+      }
+    }
+  }
+  if (nkt > 0) stage_store<D>(lds, 0, 0, n_keys, tid, k_mult, st);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -446,11 +522,11 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       const bool big_tile = lds.big_vs[buf] != 0;
       half8_t pw[2][2];     // [kb][k-step]
       if (need_mask)
-        softmax_tile<true, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, cq, big_tile,
-                               mrun, lrun, acc, pw);
+        softmax_tile<true, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, big_tile, mrun,
+                               lrun, acc, pw);
       else
-        softmax_tile<false, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, cq, big_tile,
-                                mrun, lrun, acc, pw);
+        softmax_tile<false, CB>(sacc, lds.ks[buf], lds.vs[buf], h, key0, qpos, big_tile, mrun,
+                                lrun, acc, pw);
       // ---- O^T += V^T . W^T ------------------------------------------------------
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -469,7 +545,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (more) stage_store<D>(lds, buf ^ 1, kt + 1, n_keys, tid, a.sm_scale_log2, st);
+    if (more) stage_store<D>(lds, buf ^ 1, kt + 1, n_keys, tid, k_mult, st);
     __syncthreads();
   }
 
