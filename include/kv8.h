@@ -138,7 +138,10 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * 技术解析", section 4.1).  Split-K: each workgroup covers up to
  * tokens_per_split tokens of one (sequence, KV head) for all G query heads;
  * the last workgroup of each (sequence, KV head) to finish merges the
- * partial results by log-sum-exp inside the same launch.
+ * partial results by log-sum-exp inside the same launch.  Workgroups are
+ * assigned from a dense list of the (sequence, split, KV head) items that
+ * hold tokens, so the work spreads evenly over the CUs whatever the mix of
+ * context lengths.
  *
  *   q             device [B, Hq, d], dtype q_dtype (KV8_F32 or KV8_BF16)
  *   block_table   device int32 [B, max_blocks_per_seq]
