@@ -178,3 +178,27 @@ def test_decode_workspace_reused_across_calls():
             check_close(out, ref, f"reused workspace tps={tps}")
     nb = 8 * 8 * 4      # counters of the largest (B, Hkv) used: all back to zero
     assert int(ws[:nb].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("tps", [0, 128, 1024])
+def test_decode_rising_logits_rescale_every_block(tps):
+    """Keys whose logits climb block after block (about 9 in log2 units per
+    16 tokens) move every wave's running max on every block, so the
+    accumulator rescale runs each time; also contexts of 1 block, a few
+    blocks and many blocks per wave."""
+    for ctx in ([5], [200], [3000]):
+        case = W.make_paged_case(batch=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                 context_lens=ctx, q_dtype="f32", seed=50 + ctx[0])
+        n = int(case.context_lens[0])
+        u = np.zeros(128, np.float32)
+        u[:8] = 1.0
+        ramp = (np.arange(n, dtype=np.float32) / 16.0) * 1.5     # ~9 log2 units per block
+        k = case.k.copy()
+        k[:, :, :8] = ramp[:, None, None] + 0.05 * k[:, :, :8]
+        case.k, case.k_bits = W.to_bf16(k)
+        case.q[:] = 0.0
+        case.q[:, :, :8] = 6.0
+        kc, vc, ks, vs = oracle_cache(case)
+        out = gpu_decode(case, upload_cache(kc, vc, ks, vs), tokens_per_split=tps)
+        ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+        check_close(out, ref, f"rising logits ctx={ctx} tps={tps}")
