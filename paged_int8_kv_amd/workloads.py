@@ -240,3 +240,45 @@ def prefill_case(ctx_prev, chunk_lens, *, num_q_heads=32, num_kv_heads=8, head_d
     case.extra["q_start_loc"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     case.extra["max_q_len"] = int(lens.max()) if batch else 0
     return case
+
+
+def llama70b_layer_device(layer, device, batch=64, seed=4):
+    """One layer of the Llama-3-70B sweep with its K/V/Q drawn on the device
+    (the full sweep holds tens of GB of cache).  Context lengths, key outlier
+    channels and the permuted block table come from numpy (PCG64 seeded
+    seed * 100000 + layer, drawn in that order); K, V and Q are drawn fp32
+    N(0, 1) on the device by torch.Generator seeded 4000 + layer (K, then V,
+    then Q), outlier channels of K scaled by 10, rounded to bf16.
+    Returns a dict: context_lens, block_table, num_blocks (numpy),
+    outlier_channels, token_seq, token_pos, slot_mapping (numpy int32), and
+    device tensors k, v [Ntok, 8, 128] and q [B, 64, 128] (bf16)."""
+    import torch
+    lens = llama70b_layer_lens(layer, batch=batch, seed=seed).astype(np.int64)
+    rng = np.random.Generator(np.random.PCG64(seed * 100000 + layer))
+    hkv, d = 8, 128
+    outl = np.stack([rng.choice(d, size=4, replace=False) for _ in range(hkv)])
+    blocks_per_seq = -(-lens // BLOCK_SIZE)
+    nb = int(blocks_per_seq.sum())
+    phys = rng.permutation(nb)
+    table = np.zeros((batch, int(blocks_per_seq.max())), np.int32)
+    cur = 0
+    for b in range(batch):
+        n = int(blocks_per_seq[b])
+        table[b, :n] = phys[cur:cur + n]
+        cur += n
+    seq = np.repeat(np.arange(batch), lens).astype(np.int32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    pos = (np.arange(int(lens.sum())) - np.repeat(starts, lens)).astype(np.int32)
+    slots = _slots_for(table, seq, pos)
+    g = torch.Generator(device=device)
+    g.manual_seed(4000 + layer)
+    ntok = int(lens.sum())
+    k = torch.randn((ntok, hkv, d), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((ntok, hkv, d), generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((batch, 64, d), generator=g, device=device, dtype=torch.float32)
+    for h in range(hkv):
+        idx = torch.from_numpy(outl[h]).to(device)
+        k[:, h, idx] *= 10.0
+    return dict(context_lens=lens.astype(np.int32), block_table=table, num_blocks=nb,
+                outlier_channels=outl, token_seq=seq, token_pos=pos, slot_mapping=slots,
+                k=k.to(torch.bfloat16), v=v.to(torch.bfloat16), q=q.to(torch.bfloat16))

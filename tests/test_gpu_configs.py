@@ -1,0 +1,106 @@
+"""The long-context workload (4 sequences of 32768 tokens, 64 append+decode
+steps) and the Llama-3-70B-shaped sweep (80 layers, 64 sequences of 512..16384
+tokens) at full size on the GPU, launched as a serving loop would launch
+them, checked against the fp64 oracle on sampled outputs: codes and scales
+bit-exact, attention within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kv8_oracle as O
+from paged_int8_kv_amd import binding as B
+from paged_int8_kv_amd import workloads as W
+from tests.kv8_testutil import (check_close, dev, download_cache, gpu_append, gpu_decode,
+                                needs_gpu, oracle_cache)
+from tests.test_gpu_append import assert_cache_equal
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def test_long_context_append_decode_loop_full_size():
+    """64 steps of (append one bf16 K/V token per sequence, decode the whole
+    32768+ token contexts with fp32 Q); outputs checked at steps 0, 31, 63
+    and the whole cache bit-exact after the last append."""
+    case = W.long_context_decode()
+    steps = case.extra["steps"]
+    cache = gpu_append(case)
+    kc, vc, ks, vs = oracle_cache(case)
+    for s in range(steps):
+        slots = W.step_slots(case, s)
+        gpu_append(case, cache=cache, slots=slots, k_bits=case.extra["step_k_bits"][s],
+                   v_bits=case.extra["step_v_bits"][s])
+        O.quant_append(case.extra["step_k"][s], case.extra["step_v"][s], slots, kc, vc, ks, vs)
+        ctx = (case.context_lens + s + 1).astype(np.int32)
+        q = case.extra["step_q"][s]
+        out = gpu_decode(case, cache, q=q, context_lens=ctx)
+        if s in (0, steps // 2 - 1, steps - 1):
+            ref = O.paged_decode(q, kc, vc, ks, vs, case.block_table, ctx)
+            check_close(out, ref, f"long context step {s}")
+    assert_cache_equal(download_cache(cache), (kc, vc, ks, vs), "long context after appends")
+
+
+def test_llama70b_sweep_80_layers_sampled():
+    """All 80 layers: K/V drawn on the device, quantised into per-layer caches
+    by the append kernel (about 49 GB in all), then the 80 decode calls back
+    to back.  On layers 0, 1, 40, 79 and sequences 0, 21, 42, 63 the codes and
+    scales match the oracle's quantiser bit for bit and the outputs match the
+    oracle's attention over them."""
+    d, hkv, hq = 128, 8, 64
+    layers = 80
+    sampled_layers = (0, 1, 40, 79)
+    sampled_seqs = (0, 21, 42, 63)
+    caches, meta, keep = [], [], {}
+    for layer in range(layers):
+        g = W.llama70b_layer_device(layer, dev())
+        cache = B.alloc_cache(g["num_blocks"], hkv, d, dev())
+        slots = torch.from_numpy(g["slot_mapping"]).to(dev())
+        B.kv8_quant_append(g["k"], g["v"], slots, *cache)
+        table = torch.from_numpy(g["block_table"]).to(dev())
+        lens = torch.from_numpy(g["context_lens"]).to(dev())
+        if layer in sampled_layers:
+            sel = np.isin(g["token_seq"], sampled_seqs)
+            idx = torch.from_numpy(np.nonzero(sel)[0]).to(dev())
+            keep[layer] = dict(
+                k=g["k"].index_select(0, idx).float().cpu().numpy(),
+                v=g["v"].index_select(0, idx).float().cpu().numpy(),
+                seq=g["token_seq"][sel], pos=g["token_pos"][sel], slots=g["slot_mapping"][sel],
+                q=g["q"].float().cpu().numpy(), lens=g["context_lens"])
+        caches.append(cache)
+        meta.append((g["q"], table, lens, int(g["context_lens"].max())))
+        del g, slots
+    torch.cuda.synchronize()
+    outs = []
+    max_ctx = max(m[3] for m in meta)
+    ws = torch.zeros(B.kv8_decode_workspace_size(64, hq, hkv, d, max_ctx), dtype=torch.uint8,
+                     device=dev())
+    for layer in range(layers):
+        q, table, lens, mc = meta[layer]
+        out = torch.empty((64, hq, d), dtype=torch.float32, device=dev())
+        B.paged_decode_attn_kv8(q, *caches[layer], table, lens, mc, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    sm = 1.0 / np.sqrt(d)
+    for layer in sampled_layers:
+        kp = keep[layer]
+        kc, vc, ks, vs = download_cache(caches[layer])
+        out = outs[layer].cpu().numpy()
+        for b in sampled_seqs:
+            m = kp["seq"] == b
+            order = np.argsort(kp["pos"][m])
+            k_rows, v_rows, sl = kp["k"][m][order], kp["v"][m][order], kp["slots"][m][order]
+            kq, kscale = O.quantize_rows(k_rows)
+            vq, vscale = O.quantize_rows(v_rows)
+            blk, off = sl // 16, sl % 16
+            assert np.array_equal(kc[blk, :, off], kq), f"layer {layer} seq {b}: K codes"
+            assert np.array_equal(vc[blk, :, off], vq), f"layer {layer} seq {b}: V codes"
+            assert np.array_equal(ks[blk, :, off].view(np.uint16),
+                                  np.asarray(kscale, np.float16).view(np.uint16))
+            assert np.array_equal(vs[blk, :, off].view(np.uint16),
+                                  np.asarray(vscale, np.float16).view(np.uint16))
+            kd, vd = O.dequantize_rows(kq, kscale), O.dequantize_rows(vq, vscale)
+            ref = np.zeros((hq, d))
+            for h in range(hq):
+                gg = O.kv_head_of(h, hq // hkv)
+                ref[h] = O.softmax_attention(kp["q"][b, h][None, :].astype(np.float64),
+                                             kd[:, gg], vd[:, gg], sm)[0]
+            check_close(out[b], ref, f"70B layer {layer} seq {b}")
