@@ -147,16 +147,22 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: exactly K steps, nothing else on the stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+
+    # per-kernel breakdown in a separate pass: events around each launch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
 

@@ -118,7 +118,7 @@ int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 
 /*
  * kv8_decode_workspace_size - bytes of workspace paged_decode_attn_kv8
- * needs for these sizes.  tokens_per_split: tokens each workgroup covers
+ * needs for these sizes.  tokens_per_split: most tokens one workgroup covers
  * (a multiple of 64 in [64, 2048]), or <= 0 for the library's choice,
  * which depends on batch, num_kv_heads and max_context_len only.  Returns
  * 0 for invalid sizes.
@@ -135,13 +135,14 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * codes ("KV Cache 优化全景解析", sections 2.1 and 3.3; dequantisation on
  * the fly per the KV8 item of the "KV-Cache 全栈优化系统" README).  The
  * softmax and all accumulation run in fp32 ("大模型推理加速：KV Cache与vLLM
- * 技术解析", section 4.1).  Split-K: each workgroup covers up to
- * tokens_per_split tokens of one (sequence, KV head) for all G query heads;
- * the last workgroup of each (sequence, KV head) to finish merges the
- * partial results by log-sum-exp inside the same launch.  Workgroups are
- * assigned from a dense list of the (sequence, split, KV head) items that
- * hold tokens, so the work spreads evenly over the CUs whatever the mix of
- * context lengths.
+ * 技术解析", section 4.1).  Split-K: a sequence's blocks are shared evenly
+ * by ceil(ctx_b / tokens_per_split) splits; each workgroup covers one split
+ * of one (sequence, KV head) for all G query heads, and the last workgroup
+ * of each (sequence, KV head) to finish merges the partial results by
+ * log-sum-exp inside the same launch.  Workgroups take the (sequence,
+ * split, KV head) items that hold tokens, longest first (up to 64
+ * sequences) or in sequence order, so the work spreads evenly over the CUs
+ * whatever the mix of context lengths.
  *
  *   q             device [B, Hq, d], dtype q_dtype (KV8_F32 or KV8_BF16)
  *   block_table   device int32 [B, max_blocks_per_seq]

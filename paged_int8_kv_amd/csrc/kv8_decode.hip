@@ -36,6 +36,8 @@
 // Each wave keeps kPf blocks in flight in a register ring; the ring is
 // branch-free around its loads so that the compiler's wait counts stay
 // exact, and scheduling barriers keep later slots' waits from being hoisted.
+#include <atomic>
+
 #include "kv8_device.h"
 #include "kv8_launch.h"
 
@@ -69,6 +71,8 @@ struct SplitArgs {
   int split_tokens;
   int n_split;
   int batch;
+  int period;        // workgroups per dispatch round (the CU count)
+  int snake_rounds;  // rounds resident at once (workgroups per CU)
   float qk_scale_log2;
 };
 
@@ -192,34 +196,78 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // Dense work list: workgroup i takes item i of the list of (sequence b,
-  // split, KV head g) that hold tokens, in sequence order (a sequence with an
-  // empty context keeps one item, which writes its zero output).  Items that
-  // hold work therefore occupy the first workgroup indices and are spread
-  // over all CUs by the dispatcher, whatever the mix of context lengths; the
-  // grid is sized by the longest context and the surplus workgroups exit.
-  // Every wave locates the item itself (one prefix scan per 64 sequences).
-  int b = -1, g = 0, split = 0;
-  {
+  // Work items are (sequence b, split, KV head g).  A sequence's n splits
+  // share its blocks evenly (n = ceil(blocks / blocks_per_split)), so its
+  // items are of one size and only the last block of the last split is
+  // partial; a sequence with an empty context keeps one item, which writes
+  // its zero output.  The grid is sized by the longest context and
+  // workgroups past the last item exit.
+  //
+  // Item order.  The dispatcher places workgroup i on the CU that i mod
+  // `period` names, as long as every workgroup of the first snake_rounds
+  // rounds of `period` is resident at once.  With at most 64 sequences the
+  // items are ranked longest first and dealt to those rounds in a snake
+  // (even rounds forward, odd rounds backward), which evens out the tokens
+  // per CU; later rounds keep the longest-first order, which the dispatcher
+  // fills greedily as CUs free up.  With more sequences the items keep
+  // sequence order.  Every wave locates its item itself.
+  const int bps = a.split_tokens / kBlock;      // blocks per split at most
+  int b = -1, g = 0, split = 0, nsplit = 1, nbt = 0;
+  if (a.batch <= 64 && a.period > 0) {
+    int key = -1, cnt = 0, nb = 0, n = 1;
+    if (lane < a.batch) {
+      const int cx = min(max(a.context_lens[lane], 0), a.ctx_cap);
+      nb = (cx + kBlock - 1) / kBlock;
+      n = max(1, (nb + bps - 1) / bps);
+      key = ((nb + n - 1) / n) * 64 + (63 - lane);  // unique; larger goes first
+      cnt = n * a.num_kv_heads;
+    }
+    int start = 0, total = 0;
+    for (int j = 0; j < a.batch; ++j) {
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      const int cj = __builtin_amdgcn_readlane(cnt, j);
+      start += kj > key ? cj : 0;
+      total += cj;
+    }
+    const int bid = (int)blockIdx.x;
+    const int r = bid / a.period;
+    int rank = bid;
+    if (r < a.snake_rounds) {
+      const int c = bid - r * a.period;
+      rank = r * a.period + ((r & 1) ? a.period - 1 - c : c);
+    }
+    if (rank < total) {
+      const uint64_t hit = __ballot(lane < a.batch && start <= rank && rank < start + cnt);
+      b = (int)__builtin_ctzll(hit);
+      const int j = rank - __builtin_amdgcn_readlane(start, b);
+      split = j / a.num_kv_heads;
+      g = j - split * a.num_kv_heads;
+      nsplit = __builtin_amdgcn_readlane(n, b);
+      nbt = __builtin_amdgcn_readlane(nb, b);
+    }
+  } else {
     const int sg = (int)blockIdx.x / a.num_kv_heads;     // global split index
     g = (int)blockIdx.x - sg * a.num_kv_heads;
     int base = 0;
     for (int c0 = 0; c0 < a.batch; c0 += 64) {
       const int bi = c0 + lane;
-      int n = 0;
+      int n = 0, nb = 0;
       if (bi < a.batch) {
         const int cx = min(max(a.context_lens[bi], 0), a.ctx_cap);
-        n = max(1, (cx + a.split_tokens - 1) / a.split_tokens);
+        nb = (cx + kBlock - 1) / kBlock;
+        n = max(1, (nb + bps - 1) / bps);
       }
       const int incl = wave_incl_scan(n, lane);
-      const int total = __builtin_amdgcn_readlane(incl, 63);
-      if (sg < base + total) {
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (sg < base + tot) {
         const int idx = __builtin_popcountll(__ballot(base + incl <= sg));
         b = c0 + idx;
-        split = sg - base - (__builtin_amdgcn_readlane(incl, idx) - __builtin_amdgcn_readlane(n, idx));
+        nsplit = __builtin_amdgcn_readlane(n, idx);
+        nbt = __builtin_amdgcn_readlane(nb, idx);
+        split = sg - base - (__builtin_amdgcn_readlane(incl, idx) - nsplit);
         break;
       }
-      base += total;
+      base += tot;
     }
   }
   if (b < 0) return;                           // uniform: past the work list
@@ -229,17 +277,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 
   int ctx = a.context_lens[b];
   ctx = min(max(ctx, 0), a.ctx_cap);
-  const int t0 = split * a.split_tokens;
-  if (t0 >= ctx) {                             // uniform over the workgroup
-    if (split == 0)                            // empty context: zero output
-      for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
+  if (ctx == 0) {                              // uniform: empty context, zero output
+    for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
     return;
   }
-  const int ntok = min(ctx - t0, a.split_tokens);
-  const int nblk = (ntok + kBlock - 1) / kBlock;
-  const int jb0 = t0 / kBlock;
+  // blocks [jb0, jb0 + nblk) of the sequence: nbt blocks shared by nsplit
+  const int bq = nbt / nsplit, brem = nbt - bq * nsplit;
+  const int nblk = bq + (split < brem ? 1 : 0);
+  const int jb0 = split * bq + min(split, brem);
+  const int t0 = jb0 * kBlock;
+  const int ntok = min(ctx - t0, nblk * kBlock);
   const int Hkv = a.num_kv_heads;
-  const int nvalid = (ctx + a.split_tokens - 1) / a.split_tokens;
+  const int nvalid = nsplit;
 
   if (tid < nblk) {
     int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + tid];
@@ -586,12 +635,50 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   }
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count() {
+  static std::atomic<int> cache[64];   // 0 = not queried, -1 = unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = -1;
+    c = v > 0 ? v : -1;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c > 0 ? c : 0;
+}
+
 template <int D, int G, bool QF32>
 bool launch_split(const SplitArgs& a, int batch, hipStream_t stream) {
   const SmemLayout L = smem_layout(a.split_tokens, G, D);
-  if ((int64_t)a.n_split * a.num_kv_heads * batch > 0x7FFFFFFF) return false;
-  decode_split_kernel<D, G, QF32><<<dim3(a.n_split * a.num_kv_heads * batch), dim3(kThreads),
-                                    L.total, stream>>>(a);
+  int64_t grid = (int64_t)a.n_split * a.num_kv_heads * batch;
+  SplitArgs args = a;
+  args.period = 0;
+  args.snake_rounds = 0;
+  if (batch <= 64) {
+    // resident workgroups per CU for this shared-memory size (cached)
+    // (shared-memory bytes << 32 | workgroups); 0 until first computed
+    static std::atomic<uint64_t> occ_cache{0};
+    uint64_t oc = occ_cache.load(std::memory_order_relaxed);
+    if ((oc >> 32) != (uint64_t)L.total) {
+      int v = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &v, decode_split_kernel<D, G, QF32>, kThreads, L.total) != hipSuccess) v = 0;
+      oc = ((uint64_t)L.total << 32) | (uint32_t)(v > 0 ? v : 0);
+      occ_cache.store(oc, std::memory_order_relaxed);
+    }
+    const int occ = (int)(uint32_t)oc;
+    const int cus = device_cu_count();
+    if (cus > 0 && occ > 0) {
+      args.period = cus;
+      args.snake_rounds = occ;
+      grid = (grid + cus - 1) / cus * cus;
+    }
+  }
+  if (grid > 0x7FFFFFFF) return false;
+  decode_split_kernel<D, G, QF32><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(args);
   return true;
 }
 

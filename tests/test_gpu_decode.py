@@ -202,3 +202,20 @@ def test_decode_rising_logits_rescale_every_block(tps):
         out = gpu_decode(case, upload_cache(kc, vc, ks, vs), tokens_per_split=tps)
         ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
         check_close(out, ref, f"rising logits ctx={ctx} tps={tps}")
+
+
+@pytest.mark.parametrize("batch", [64, 65, 97])
+def test_decode_many_sequences_both_item_orders(batch):
+    """Up to 64 sequences the work items are ranked longest first; above
+    that they keep sequence order.  Both orders, with ragged contexts
+    (empty ones included) and a split size that gives several splits of
+    unequal block counts, match the oracle."""
+    def lens(rng):
+        c = rng.integers(0, 700, size=batch)
+        c[::9] = 0
+        c[1::13] = 16 * rng.integers(1, 40, size=c[1::13].shape)
+        return c
+    case = W.make_paged_case(batch=batch, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                             context_lens=lens, seed=60 + batch)
+    run_parity(case)
+    run_parity(case, tokens_per_split=128)
