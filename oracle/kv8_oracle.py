@@ -244,3 +244,48 @@ def paged_prefill_chunk(q, q_start_loc, k_cache, v_cache, k_scale, v_scale,
             v = gather_dequant(v_cache, v_scale, block_table[b], ctx, g, block_size)
             out[r0:r1, h] = softmax_attention(q[r0:r1, h], k, v, sm_scale, visible)
     return out
+
+
+# --------------------------------------------------------------------------
+# 16-bit KV reference point.  [P1] section "实验效果（摘要）" compares KV8
+# attention with FlashAttention-2 over the unquantised cache when both get
+# the same GPU-memory budget; the 16-bit side is plain attention over the
+# paged bf16 cache ([P3] sections 2.1, 3.3, 4.2), no quantiser involved.
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) -> exact fp64 values (a bf16 value is the
+    fp32 whose upper 16 bits are the pattern)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def gather_bf16(cache_bits, block_table_row, ctx, kv_head, block_size=BLOCK_SIZE):
+    """[ctx, d] fp64 rows of one sequence and one KV head of a paged bf16
+    cache [NB, Hkv, block_size, d] (bit patterns), read through the block
+    table."""
+    t = np.arange(ctx)
+    blk, off = logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return bf16_bits_to_f64(cache_bits[blk, kv_head, off, :])
+
+
+def paged_decode_bf16(q, k_cache_bits, v_cache_bits, block_table, context_lens,
+                      sm_scale=None, block_size=BLOCK_SIZE):
+    """One query token per sequence over a paged bf16 cache.  q [B, Hq, d];
+    returns fp64 [B, Hq, d]; an empty context yields zeros."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_cache_bits.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        if ctx <= 0:
+            continue
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_bf16(k_cache_bits, block_table[b], ctx, g, block_size)
+            v = gather_bf16(v_cache_bits, block_table[b], ctx, g, block_size)
+            out[b, h] = softmax_attention(q[b, h][None, :], k, v, sm_scale)[0]
+    return out

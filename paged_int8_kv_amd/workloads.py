@@ -134,6 +134,21 @@ def make_paged_case(*, batch, num_q_heads, num_kv_heads, head_dim, context_lens,
                      slots, seq, pos, outl)
 
 
+def paged_bf16_cache(case, poison_unused=False):
+    """The case's bf16 K/V tokens laid out as a paged 16-bit cache: bit
+    patterns [NB, Hkv, 16, d] (uint16) for K and V, token n in the slot
+    slot_mapping[n] names.  Slots that no token uses hold 0, or a NaN
+    pattern when poison_unused."""
+    shape = (case.num_blocks, case.num_kv_heads, BLOCK_SIZE, case.head_dim)
+    fill = np.uint16(0x7FC1) if poison_unused else np.uint16(0)
+    kc = np.full(shape, fill, np.uint16)
+    vc = np.full(shape, fill, np.uint16)
+    blk, off = case.slot_mapping // BLOCK_SIZE, case.slot_mapping % BLOCK_SIZE
+    kc[blk, :, off, :] = case.k_bits
+    vc[blk, :, off, :] = case.v_bits
+    return kc, vc
+
+
 # ---------------------------------------------------------------------------
 # The five workloads of this path
 # ---------------------------------------------------------------------------

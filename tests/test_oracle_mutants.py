@@ -31,6 +31,10 @@ def _battery():
         ("page_example", P.test_block_table_example_from_page),
         ("scale_exhaustive", P.test_scale_exhaustive_all_bf16_absmax),
         ("kv_size", P.test_kv_size_printed_tables),
+        ("bf16_brute_force", P.test_bf16_decode_brute_force_tiny),
+        ("bf16_sdpa", P.test_bf16_decode_matches_sdpa_fp64),
+        ("bf16_closed_forms", P.test_bf16_decode_closed_forms_and_permutation),
+        ("bf16_vs_int8", P.test_bf16_decode_equals_int8_decode_on_exact_values),
     ]
     for name, fn in checks:
         try:
@@ -119,6 +123,21 @@ def _dequant_sign_flip(codes, scales):
     return -codes.astype(np.float64) * np.asarray(scales, np.float16).astype(np.float64)[..., None]
 
 
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16_low_half(bits):
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(8)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _gather_bf16_head0(cache_bits, block_table_row, ctx, kv_head, block_size=16):
+    t = np.arange(ctx)
+    blk, off = np.asarray(block_table_row)[t // block_size], t % block_size
+    return O.bf16_bits_to_f64(cache_bits[blk, 0, off, :])
+
+
 MUTANTS = {
     "head_map_mod": ("kv_head_of", lambda h, group: h % group),
     "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
@@ -138,6 +157,9 @@ MUTANTS = {
     "causal_off_by_one": ("causal_visibility",
                           lambda ctx, lc: np.arange(ctx)[None, :] <= (ctx - lc + 1 + np.arange(lc))[:, None]),
     "kv_size_no_two": ("kv_cache_bytes", lambda L, B, T, H, d, nb: L * B * T * H * d * nb),
+    "bf16_read_as_fp16": ("bf16_bits_to_f64", _bf16_as_fp16),
+    "bf16_wrong_shift": ("bf16_bits_to_f64", _bf16_low_half),
+    "bf16_gather_head0": ("gather_bf16", _gather_bf16_head0),
 }
 
 

@@ -441,3 +441,78 @@ def test_prefill_single_row_equals_decode():
                                   case.block_table, case.context_lens)
     out_d = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
     assert np.allclose(out_p, out_d, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# 16-bit KV reference point (README section 实验效果: KV8 against FA2 over the
+# unquantised cache)
+# ---------------------------------------------------------------------------
+def dense_bf16(case, b):
+    """Contiguous [ctx, Hkv, d] source rows of sequence b in sequence order
+    (no block table involved)."""
+    return case.k[case.token_seq == b].astype(np.float64), case.v[case.token_seq == b].astype(np.float64)
+
+
+def test_bf16_decode_brute_force_tiny():
+    case = W.make_paged_case(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=8,
+                             context_lens=[5, 37], q_dtype="f32", seed=13)
+    kc, vc = W.paged_bf16_cache(case, poison_unused=True)
+    out = O.paged_decode_bf16(case.q, kc, vc, case.block_table, case.context_lens)
+    for b in range(2):
+        K, V = dense_bf16(case, b)
+        for h in range(4):
+            ref = brute_attention(case.q[b, h], K[:, h // 2], V[:, h // 2], 1 / math.sqrt(8))
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_decode_matches_sdpa_fp64():
+    case = W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=32,
+                             context_lens=[1, 17, 300], q_dtype="bf16", k_outliers=True, seed=14)
+    kc, vc = W.paged_bf16_cache(case)
+    out = O.paged_decode_bf16(case.q, kc, vc, case.block_table, case.context_lens)
+    for b in range(3):
+        K, V = dense_bf16(case, b)
+        Kt = torch.from_numpy(K.transpose(1, 0, 2)).repeat_interleave(4, dim=0)[None]
+        Vt = torch.from_numpy(V.transpose(1, 0, 2)).repeat_interleave(4, dim=0)[None]
+        q = torch.from_numpy(case.q[b].astype(np.float64))[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt)[0, :, 0].numpy()
+        assert np.allclose(out[b], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_bf16_decode_closed_forms_and_permutation():
+    case = W.make_paged_case(batch=3, num_q_heads=4, num_kv_heads=1, head_dim=16,
+                             context_lens=[1, 20, 0], seed=15, permute=False)
+    kc, vc = W.paged_bf16_cache(case)
+    out = O.paged_decode_bf16(case.q, kc, vc, case.block_table, case.context_lens)
+    v0 = case.v[case.token_seq == 0][0, 0].astype(np.float64)
+    for h in range(4):
+        assert np.array_equal(out[0, h], v0)           # single token: its V
+    assert np.all(out[2] == 0)                         # empty context
+    blk = case.block_table[1]
+    for t in range(20):                                # identical keys: mean V
+        kc[blk[t // 16], 0, t % 16] = kc[blk[0], 0, 0]
+    out = O.paged_decode_bf16(case.q, kc, vc, case.block_table, case.context_lens)
+    vmean = case.v[case.token_seq == 1][:, 0].astype(np.float64).mean(axis=0)
+    assert np.allclose(out[1], vmean[None, :], rtol=1e-13, atol=1e-14)
+    perm = np.random.default_rng(2).permutation(case.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    out2 = O.paged_decode_bf16(case.q, kc2, vc2, perm[case.block_table], case.context_lens)
+    assert np.array_equal(out2, out)
+
+
+def test_bf16_decode_equals_int8_decode_on_exact_values():
+    """With every scale 2^-6, code * scale is exact in bf16, so a bf16 cache
+    holding those values must give the INT8 path's result: the two gathers
+    and the shared attention definition agree."""
+    case = W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=16,
+                             context_lens=[7, 40, 129], q_dtype="f32", seed=16)
+    kc, vc, ks, vs = build_cache(case)
+    ks[:] = np.float16(2.0 ** -6)
+    vs[:] = np.float16(2.0 ** -6)
+    ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    _, kb = W.to_bf16(kc.astype(np.float32) * np.float32(2.0 ** -6))
+    _, vb = W.to_bf16(vc.astype(np.float32) * np.float32(2.0 ** -6))
+    assert np.array_equal(W.bf16_bits_to_f32(kb), kc.astype(np.float32) / 64)   # exact
+    out = O.paged_decode_bf16(case.q, kb, vb, case.block_table, case.context_lens)
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-15)
