@@ -37,6 +37,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=4)
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--budget-steps", type=int, default=10,
+                   help="decode calls timed per side of the 258K equal-budget comparison "
+                        "(0 skips it)")
+    p.add_argument("--budget-bf16-batch", type=int, default=8,
+                   help="sequences the 16-bit cache holds; sets the memory budget")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain elementwise copy of known size (for HBM counters)")
     return p.parse_args()
@@ -229,6 +234,8 @@ def main():
     torch.cuda.empty_cache()
     if args.prefill_steps > 0:
         result["prefill"] = bench_prefill(args, dev)
+    if args.budget_steps > 0:
+        result["equal_budget_258k"] = bench_equal_budget(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_steps, d_bytes + a_bytes)
     print(json.dumps(result), flush=True)
@@ -296,6 +303,89 @@ def bench_prefill(args, dev):
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill"),
                          "kernel": "paged_prefill_chunk_attn_kv8 (fp16 MFMA 32x32x16)"}}
+
+
+def bench_equal_budget(args, dev):
+    """Decode at 258K tokens per sequence with one per-layer KV memory
+    budget for both caches: the budget holds budget_bf16_batch sequences of
+    bf16 K/V, and as many INT8 sequences (codes + fp16 scales) as fit in the
+    same bytes.  Both sides hold the same seeded tokens and queries for the
+    sequences they share.  Reports decode tokens/s (sequences / call time)
+    for each side and their ratio, the comparison the KV8 README draws
+    against FlashAttention-2 at 258K context (1.64x on its own system)."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    from paged_int8_kv_amd import workloads as W
+    hq, hkv, d = 32, 8, 128
+    ctx = 258 * 1024
+    per_tok_bf16 = 2 * hkv * d * 2
+    per_tok_int8 = 2 * hkv * (d + 2)
+    b16 = args.budget_bf16_batch
+    budget = b16 * ctx * per_tok_bf16
+    b8 = budget // (ctx * per_tok_int8)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3     # us per call
+
+    res = {"workload": f"decode, Llama-3.1-8B attention (Hq=32, Hkv=8, d=128), {ctx} tokens per "
+                       "sequence, bf16 q, one KV budget per layer",
+           "context_tokens": ctx, "budget_bytes": int(budget),
+           "bf16_kv": {"batch": b16}, "int8_kv": {"batch": int(b8)}}
+    outs = {}
+    for kind, batch in (("bf16_kv", b16), ("int8_kv", int(b8))):
+        w = W.long_context_258k(batch, dev)
+        nb = w["num_blocks"]
+        table = torch.from_numpy(w["block_table"]).to(dev)
+        lens = torch.from_numpy(w["context_lens"]).to(dev)
+        out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev)
+        ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx, 0),
+                         dtype=torch.uint8, device=dev)
+        if kind == "bf16_kv":
+            kc = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device=dev)
+            vc = torch.empty_like(kc)
+            for b in range(batch):
+                k, v = w["tokens"](b)
+                s = w["slots"](b).long()
+                kc[s // 16, :, s % 16, :] = k
+                vc[s // 16, :, s % 16, :] = v
+                del k, v, s
+            cache = (kc, vc)
+            call = lambda: B.paged_decode_attn_bf16kv(w["q"], *cache, table, lens, ctx, out, ws)
+            nbytes = batch * ctx * per_tok_bf16
+        else:
+            cache = B.alloc_cache(nb, hkv, d, dev)
+            for b in range(batch):
+                k, v = w["tokens"](b)
+                B.kv8_quant_append(k, v, w["slots"](b), *cache)
+                del k, v
+            call = lambda: B.paged_decode_attn_kv8(w["q"], *cache, table, lens, ctx, out, ws)
+            nbytes = batch * ctx * per_tok_int8
+        torch.cuda.synchronize()
+        us = timed(call, args.budget_steps)
+        outs[kind] = out.clone()
+        res[kind].update({"decode_us": round(us, 1),
+                          "decode_tokens_per_s": round(batch / (us * 1e-6), 1),
+                          "kv_tokens_per_s": round(batch * ctx / (us * 1e-6), 1),
+                          "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        del cache, ws, out, table, lens, w
+        torch.cuda.empty_cache()
+    res["throughput_ratio_int8_over_bf16"] = round(
+        res["int8_kv"]["decode_tokens_per_s"] / res["bf16_kv"]["decode_tokens_per_s"], 3)
+    n = min(b16, int(b8))
+    res["int8_vs_bf16_output_max_abs"] = float(
+        (outs["int8_kv"][:n] - outs["bf16_kv"][:n]).abs().max().item())
+    res["pages_figure"] = "1.64x KV8 over FA2 at 258K, same memory budget, L40S, system level"
+    return res
 
 
 def calibrate_copy(dev, n_bytes=256 << 20, launches=5):

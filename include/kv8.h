@@ -173,6 +173,35 @@ int paged_decode_attn_kv8(const void* q, int q_dtype,
                           int tokens_per_split, void* stream);
 
 /*
+ * paged_decode_attn_bf16kv - the same decode attention over a paged cache
+ * that holds K and V unquantised, as bf16: the 16-bit reference point that
+ * the KV8 method is compared with at an equal memory budget ("KV-Cache
+ * 全栈优化系统" README, section 实验效果（摘要）, which compares KV8
+ * attention with FlashAttention-2 over the unquantised cache).  For every
+ * sequence b and query head hq:  out[b,hq] = sum_t softmax_t(<q[b,hq],
+ * k[b,g,t]> * sm_scale) v[b,g,t], g = hq / G ("KV Cache 优化全景解析",
+ * sections 2.1, 3.3 and 4.2), softmax and accumulation in fp32.  Same
+ * split-K scheme, item order and in-launch merge as paged_decode_attn_kv8.
+ *
+ *   k_cache, v_cache  device bf16 bit patterns [num_blocks, Hkv, 16, d]
+ *   all other arguments as for paged_decode_attn_kv8; the workspace is
+ *   sized by kv8_decode_workspace_size() with the same sizes and
+ *   tokens_per_split, zero-filled once, and may be shared with
+ *   paged_decode_attn_kv8 calls that do not overlap in time.
+ * Slots past a sequence's context are never used, whatever they hold.
+ * Returns KV8_OK or a negative kv8_status as paged_decode_attn_kv8 does.
+ */
+int paged_decode_attn_bf16kv(const void* q, int q_dtype,
+                             const uint16_t* k_cache, const uint16_t* v_cache,
+                             int64_t num_blocks,
+                             const int32_t* block_table, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int batch, int num_q_heads, int num_kv_heads,
+                             int head_dim, int block_size, float sm_scale,
+                             float* out, void* workspace, size_t workspace_bytes,
+                             int tokens_per_split, void* stream);
+
+/*
  * paged_prefill_chunk_attn_kv8 - causal attention of a chunk of query rows
  * per sequence over the paged INT8 cache that already holds the chunk's own
  * K/V (append first with kv8_quant_append).  Chunked prefill as in the

@@ -25,7 +25,8 @@ BLOCK_SIZE = 16
 
 EXPORTED = (
     "kv8_status_string", "kv8_version", "kv8_quant_append", "kv8_decode_workspace_size",
-    "paged_decode_attn_kv8", "kv8_prefill_workspace_size", "paged_prefill_chunk_attn_kv8",
+    "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
+    "paged_prefill_chunk_attn_kv8",
 )
 
 _lib = None
@@ -63,6 +64,9 @@ def load():
     lib.paged_decode_attn_kv8.restype = i32
     lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
+    lib.paged_decode_attn_bf16kv.restype = i32
+    lib.paged_decode_attn_bf16kv.argtypes = [vp, i32, vp, vp, i64, vp, i32, vp, i32,
+                                             i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
     lib.kv8_prefill_workspace_size.restype = sz
     lib.kv8_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.paged_prefill_chunk_attn_kv8.restype = i32
@@ -131,6 +135,27 @@ def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, co
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         int(tokens_per_split), _stream(stream))
     _check(st, "paged_decode_attn_kv8")
+
+
+def paged_decode_attn_bf16kv(q, k_cache, v_cache, block_table, context_lens, max_context_len,
+                             out, workspace, sm_scale=None, tokens_per_split=0, stream=None):
+    """Decode over a paged bf16 cache.  q: fp32 or bf16 [B, Hq, d]; k_cache,
+    v_cache: bf16 (or int16 holding bf16 bits) [NB, Hkv, 16, d]; out fp32
+    [B, Hq, d]; workspace uint8 of at least kv8_decode_workspace_size()
+    bytes."""
+    import torch
+    b, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    dt = KV8_BF16 if q.dtype == torch.bfloat16 else KV8_F32
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    st = load().paged_decode_attn_bf16kv(
+        _ptr(q), dt, _ptr(k_cache), _ptr(v_cache), nb, _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), int(max_context_len), b, hq, hkv, d, BLOCK_SIZE, float(sm_scale),
+        _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        int(tokens_per_split), _stream(stream))
+    _check(st, "paged_decode_attn_bf16kv")
 
 
 def kv8_prefill_workspace_size(batch, num_q_heads, head_dim, max_q_len, max_context_len):

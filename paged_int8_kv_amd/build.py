@@ -22,7 +22,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libkv8.so")
 
 ARCH = "gfx950"
-SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_prefill.hip"]
+SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_prefill.hip",
+           "kvbf16_decode.hip"]
 
 # Packed fp32 VALU instructions are kept out of the code object: the
 # compiler's automatic use of them is switched off for every HIP source.

@@ -117,6 +117,44 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
 }
 
+int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache,
+                             const uint16_t* v_cache, int64_t num_blocks,
+                             const int32_t* block_table, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int batch,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             float sm_scale, float* out, void* workspace,
+                             size_t workspace_bytes, int tokens_per_split, void* stream) {
+  if (!q || !block_table || !context_lens || !out || !k_cache || !v_cache) return KV8_ERR_NULL;
+  if (num_blocks <= 0) return KV8_ERR_SHAPE;
+  if (block_size != KV8_BLOCK_SIZE) return KV8_ERR_UNSUPPORTED;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return KV8_ERR_ALIGN;
+  if (batch <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) return KV8_ERR_SHAPE;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return KV8_ERR_SHAPE;
+  if (batch > 65535 || num_kv_heads > 65535) return KV8_ERR_SHAPE;
+  if (q_dtype != KV8_F32 && q_dtype != KV8_BF16) return KV8_ERR_UNSUPPORTED;
+  if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
+    return KV8_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out)) return KV8_ERR_ALIGN;
+  if (tokens_per_split > 0 && (tokens_per_split % 64 != 0 || tokens_per_split > 2048))
+    return KV8_ERR_UNSUPPORTED;
+  kv8::DecodePlan plan;
+  if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        tokens_per_split, &plan))
+    return KV8_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KV8_ERR_ALIGN;
+  const long long cap_blocks = (long long)max_blocks_per_seq * KV8_BLOCK_SIZE;
+  const int ctx_cap = (int)(cap_blocks < max_context_len ? cap_blocks : max_context_len);
+  const int r = kv8::launch_decode_bf16kv(q, q_dtype == KV8_F32, k_cache, v_cache, num_blocks,
+                                          block_table, max_blocks_per_seq, context_lens,
+                                          ctx_cap, batch, num_q_heads, num_kv_heads, head_dim,
+                                          sm_scale, out, workspace, plan,
+                                          static_cast<hipStream_t>(stream));
+  if (r == -2) return KV8_ERR_UNSUPPORTED;
+  return r == 0 ? KV8_OK : KV8_ERR_HIP;
+}
+
 size_t kv8_prefill_workspace_size(int batch, int num_q_heads, int head_dim, int max_q_len,
                                   int max_context_len) {
   (void)batch; (void)num_q_heads; (void)head_dim; (void)max_q_len; (void)max_context_len;

@@ -36,8 +36,7 @@
 // Each wave keeps kPf blocks in flight in a register ring; the ring is
 // branch-free around its loads so that the compiler's wait counts stay
 // exact, and scheduling barriers keep later slots' waits from being hoisted.
-#include <atomic>
-
+#include "kv8_decode_common.h"
 #include "kv8_device.h"
 #include "kv8_launch.h"
 
@@ -48,7 +47,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kPf = 4;        // blocks in flight per wave and pass
-constexpr int kMergeBatch = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SplitArgs {
@@ -108,74 +106,6 @@ __device__ __forceinline__ uint32_t dword(const uint4& r, int k) {
 }
 __device__ __forceinline__ uint32_t dword(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
 
-// One reduce-scatter step over lane pairs given by the DPP pattern CTRL:
-// the lane flagged `upper` keeps the second half of its N values, its
-// partner the first half, and each adds the partner's copy of the half it
-// keeps.
-template <int CTRL, int N>
-__device__ __forceinline__ void rs_half(const float (&in)[N], float (&out)[N / 2], bool upper) {
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const float keep = upper ? in[k + N / 2] : in[k];
-    const float send = upper ? in[k] : in[k + N / 2];
-    out[k] = keep + dpp_f<CTRL>(send);
-  }
-}
-
-// Reduce the N = 2G partial dot products v[t*G + h] (tokens t = 0, 1 of the
-// lane's pair, heads h) over the 8 lanes of a token group.  Lane i of the
-// group ends with NV = max(1, N/8) full sums: value j is v index
-//   (i>>2)*(N/2) + ((i>>1)&1)*(N/4 if N>=4) + (i&1)*(N/8 if N>=8) + j,
-// i.e. token i>>2.  The first step pairs lanes i and 7-i (half mirror),
-// the next two are quad exchanges.
-template <int G>
-__device__ __forceinline__ void reduce_scatter8(const float (&v)[2 * G],
-                                                float (&out)[(2 * G >= 8) ? (2 * G) / 8 : 1],
-                                                int i) {
-  constexpr int N = 2 * G;
-  float a[N / 2];
-  rs_half<kDppHalfMirror, N>(v, a, i >= 4);
-  if constexpr (N / 2 >= 2) {
-    float b[N / 4];
-    rs_half<kDppQuadXor2, N / 2>(a, b, (i & 2) != 0);
-    if constexpr (N / 4 >= 2) {
-      rs_half<kDppQuadXor1, N / 4>(b, out, (i & 1) != 0);
-    } else {
-      out[0] = b[0] + dpp_f<kDppQuadXor1>(b[0]);
-    }
-  } else {
-    float x = a[0] + dpp_f<kDppQuadXor2>(a[0]);
-    out[0] = x + dpp_f<kDppQuadXor1>(x);
-  }
-}
-
-// Head of value j after reduce_scatter8 on lane i of its group.
-template <int G>
-__device__ __forceinline__ int rs_head(int i, int j) {
-  constexpr int N = 2 * G;
-  int idx = ((i >> 1) & 1) * (N >= 4 ? N / 4 : 0) + (i & 1) * (N >= 8 ? N / 8 : 0) + j;
-  return idx % G;
-}
-
-// Agent-scope relaxed accesses (coherent across the XCDs' L2 caches).
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-// Wait until every vector memory access of this wave has completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int D, int G, bool QF32>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   constexpr int CPL = D / 8;    // channels (= code bytes) per lane per token
@@ -196,81 +126,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // Work items are (sequence b, split, KV head g).  A sequence's n splits
-  // share its blocks evenly (n = ceil(blocks / blocks_per_split)), so its
-  // items are of one size and only the last block of the last split is
-  // partial; a sequence with an empty context keeps one item, which writes
-  // its zero output.  The grid is sized by the longest context and
-  // workgroups past the last item exit.
-  //
-  // Item order.  The dispatcher places workgroup i on the CU that i mod
-  // `period` names, as long as every workgroup of the first snake_rounds
-  // rounds of `period` is resident at once.  With at most 64 sequences the
-  // items are ranked longest first and dealt to those rounds in a snake
-  // (even rounds forward, odd rounds backward), which evens out the tokens
-  // per CU; later rounds keep the longest-first order, which the dispatcher
-  // fills greedily as CUs free up.  With more sequences the items keep
-  // sequence order.  Every wave locates its item itself.
-  const int bps = a.split_tokens / kBlock;      // blocks per split at most
-  int b = -1, g = 0, split = 0, nsplit = 1, nbt = 0;
-  if (a.batch <= 64 && a.period > 0) {
-    int key = -1, cnt = 0, nb = 0, n = 1;
-    if (lane < a.batch) {
-      const int cx = min(max(a.context_lens[lane], 0), a.ctx_cap);
-      nb = (cx + kBlock - 1) / kBlock;
-      n = max(1, (nb + bps - 1) / bps);
-      key = ((nb + n - 1) / n) * 64 + (63 - lane);  // unique; larger goes first
-      cnt = n * a.num_kv_heads;
-    }
-    int start = 0, total = 0;
-    for (int j = 0; j < a.batch; ++j) {
-      const int kj = __builtin_amdgcn_readlane(key, j);
-      const int cj = __builtin_amdgcn_readlane(cnt, j);
-      start += kj > key ? cj : 0;
-      total += cj;
-    }
-    const int bid = (int)blockIdx.x;
-    const int r = bid / a.period;
-    int rank = bid;
-    if (r < a.snake_rounds) {
-      const int c = bid - r * a.period;
-      rank = r * a.period + ((r & 1) ? a.period - 1 - c : c);
-    }
-    if (rank < total) {
-      const uint64_t hit = __ballot(lane < a.batch && start <= rank && rank < start + cnt);
-      b = (int)__builtin_ctzll(hit);
-      const int j = rank - __builtin_amdgcn_readlane(start, b);
-      split = j / a.num_kv_heads;
-      g = j - split * a.num_kv_heads;
-      nsplit = __builtin_amdgcn_readlane(n, b);
-      nbt = __builtin_amdgcn_readlane(nb, b);
-    }
-  } else {
-    const int sg = (int)blockIdx.x / a.num_kv_heads;     // global split index
-    g = (int)blockIdx.x - sg * a.num_kv_heads;
-    int base = 0;
-    for (int c0 = 0; c0 < a.batch; c0 += 64) {
-      const int bi = c0 + lane;
-      int n = 0, nb = 0;
-      if (bi < a.batch) {
-        const int cx = min(max(a.context_lens[bi], 0), a.ctx_cap);
-        nb = (cx + kBlock - 1) / kBlock;
-        n = max(1, (nb + bps - 1) / bps);
-      }
-      const int incl = wave_incl_scan(n, lane);
-      const int tot = __builtin_amdgcn_readlane(incl, 63);
-      if (sg < base + tot) {
-        const int idx = __builtin_popcountll(__ballot(base + incl <= sg));
-        b = c0 + idx;
-        nsplit = __builtin_amdgcn_readlane(n, idx);
-        nbt = __builtin_amdgcn_readlane(nb, idx);
-        split = sg - base - (__builtin_amdgcn_readlane(incl, idx) - nsplit);
-        break;
-      }
-      base += tot;
-    }
-  }
-  if (b < 0) return;                           // uniform: past the work list
+  const Item it = locate_item(a.context_lens, a.batch, a.ctx_cap, a.num_kv_heads,
+                              a.split_tokens, a.period, a.snake_rounds, lane);
+  const int b = it.b, g = it.g, split = it.split;
+  if (b < 0) return;                           // uniform: past the item list
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int slot = lane >> 3, chunk = lane & 7;
   const int64_t bh0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
@@ -281,14 +140,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
     return;
   }
-  // blocks [jb0, jb0 + nblk) of the sequence: nbt blocks shared by nsplit
-  const int bq = nbt / nsplit, brem = nbt - bq * nsplit;
-  const int nblk = bq + (split < brem ? 1 : 0);
-  const int jb0 = split * bq + min(split, brem);
-  const int t0 = jb0 * kBlock;
-  const int ntok = min(ctx - t0, nblk * kBlock);
+  const Span sp = split_span(it, ctx);
+  const int nblk = sp.nblk, jb0 = sp.jb0, ntok = sp.ntok;
   const int Hkv = a.num_kv_heads;
-  const int nvalid = nsplit;
 
   if (tid < nblk) {
     int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + tid];
@@ -534,149 +388,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     }
   }
 
-  // ---- sum the eight token groups: a row step, then two reduce-scatter
-  // steps on the row/half swaps.  Lane l keeps M/4 sums: value k is
-  // accumulator k + (M/2)*(row of l is odd) + (M/4)*(l in upper half).
-#pragma unroll
-  for (int k = 0; k < M; ++k) acc[k] += dpp_f<kDppRowRor8>(acc[k]);
-#pragma unroll
-  for (int k = 0; k < M / 2; ++k) {
-    float x, y;
-    swap16_pair(acc[k], acc[k + M / 2], x, y);
-    acc[k] = x + y;
-  }
-#pragma unroll
-  for (int k = 0; k < M / 4; ++k) {
-    float x, y;
-    swap32_pair(acc[k], acc[k + M / 4], x, y);
-    acc[k] = x + y;
-  }
-  if ((lane & 8) == 0) {               // the two groups of a row agree
-    const int off = (M / 2) * ((lane >> 4) & 1) + (M / 4) * (lane >> 5);
-#pragma unroll
-    for (int k = 0; k < M / 4; ++k) {
-      const int idx = k + off;
-      s_fin[(wave * G + idx / CPL) * D + chunk * CPL + idx % CPL] = acc[k];
-    }
-  }
+  groups_to_lds<G, CPL, D>(acc, s_fin, wave, lane, chunk);
   __syncthreads();
-
-  // ---- normalise; write the output or this split's partial ----------------
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int h = e / D, c = e % D;
-    float s = s_fin[h * D + c];
-    float Mh = s_red[h], Lh = s_red[kWaves * G + h], Ph = s_red[2 * kWaves * G + h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      s += s_fin[(w * G + h) * D + c];
-      Mh = fmaxf(Mh, s_red[w * G + h]);
-      Lh += s_red[kWaves * G + w * G + h];
-      Ph += s_red[2 * kWaves * G + w * G + h];
-    }
-    const float o = (s - kCodeBias * Ph) / Lh;
-    if (nvalid == 1) {
-      a.out[(bh0 + h) * D + c] = o;
-    } else {
-      store_agent(a.o_part + ((bh0 + h) * a.n_split + split) * D + c, o);
-      if (c == 0)
-        store_agent(a.lse_part + (bh0 + h) * a.n_split + split, Mh + __builtin_amdgcn_logf(Lh));
-    }
-  }
-  if (nvalid == 1) return;
-
-  // ---- the last workgroup of (b, g) merges the splits by log-sum-exp ------
-  // Partials travel through agent-scope stores and loads, which write
-  // through / bypass the per-XCD L2, so no cache-wide writeback or
-  // invalidate is needed: each wave waits for its stores to complete before
-  // the barrier, and only then is the split counted.
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {
-    unsigned* cnt = a.counters + (int64_t)b * Hkv + g;
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    const int is_last = prev == (unsigned)(nvalid - 1);
-    if (is_last)                       // leave the counter zero for the next call
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[0] = is_last;
-  }
-  __syncthreads();
-  if (!s_flag[0]) return;
-  // Partials are read in batches of kMergeBatch splits whose loads are all
-  // issued before any is used (one memory round trip per batch), and folded
-  // in by an online log-sum-exp update.
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int h = e / D, c = e % D;
-    const int64_t bh = bh0 + h;
-    const float* lse = a.lse_part + bh * a.n_split;
-    const float* op = a.o_part + bh * a.n_split * D + c;
-    float Mx = kNegInf, num = 0.0f, den = 0.0f;
-    for (int s0 = 0; s0 < nvalid; s0 += kMergeBatch) {
-      float lv[kMergeBatch], ov[kMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = min(s0 + u, nvalid - 1);
-        lv[u] = load_agent(lse + s);
-        ov[u] = load_agent(op + (int64_t)s * D);
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        if (s0 + u < nvalid) {
-          const float mn = fmaxf(Mx, lv[u]);
-          const float wo = __builtin_amdgcn_exp2f(Mx - mn);   // 0 while Mx = -inf
-          const float wn = __builtin_amdgcn_exp2f(lv[u] - mn);
-          num = num * wo + wn * ov[u];
-          den = den * wo + wn;
-          Mx = mn;
-        }
-      }
-    }
-    a.out[bh * D + c] = num / den;
-  }
-}
-
-// Compute units of the current device (cached per device; 0 if unknown).
-int device_cu_count() {
-  static std::atomic<int> cache[64];   // 0 = not queried, -1 = unknown
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int c = cache[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = -1;
-    c = v > 0 ? v : -1;
-    cache[dev].store(c, std::memory_order_relaxed);
-  }
-  return c > 0 ? c : 0;
+  finish_split<G, D, kThreads, kWaves, true>(
+      PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
 template <int D, int G, bool QF32>
 bool launch_split(const SplitArgs& a, int batch, hipStream_t stream) {
   const SmemLayout L = smem_layout(a.split_tokens, G, D);
-  int64_t grid = (int64_t)a.n_split * a.num_kv_heads * batch;
   SplitArgs args = a;
-  args.period = 0;
-  args.snake_rounds = 0;
-  if (batch <= 64) {
-    // resident workgroups per CU for this shared-memory size (cached)
-    // (shared-memory bytes << 32 | workgroups); 0 until first computed
-    static std::atomic<uint64_t> occ_cache{0};
-    uint64_t oc = occ_cache.load(std::memory_order_relaxed);
-    if ((oc >> 32) != (uint64_t)L.total) {
-      int v = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &v, decode_split_kernel<D, G, QF32>, kThreads, L.total) != hipSuccess) v = 0;
-      oc = ((uint64_t)L.total << 32) | (uint32_t)(v > 0 ? v : 0);
-      occ_cache.store(oc, std::memory_order_relaxed);
-    }
-    const int occ = (int)(uint32_t)oc;
-    const int cus = device_cu_count();
-    if (cus > 0 && occ > 0) {
-      args.period = cus;
-      args.snake_rounds = occ;
-      grid = (grid + cus - 1) / cus * cus;
-    }
-  }
+  const int64_t grid = item_grid<decode_split_kernel<D, G, QF32>>(
+      kThreads, L.total, batch, (int64_t)a.n_split * a.num_kv_heads * batch, &args.period,
+      &args.snake_rounds);
   if (grid > 0x7FFFFFFF) return false;
   decode_split_kernel<D, G, QF32><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(args);
   return true;

@@ -34,6 +34,13 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream);
 
+int launch_decode_bf16kv(const void* q, bool q_f32, const uint16_t* k_cache,
+                         const uint16_t* v_cache, int64_t num_blocks,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
+                         int num_kv_heads, int head_dim, float sm_scale, float* out,
+                         void* workspace, const DecodePlan& plan, hipStream_t stream);
+
 int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_q, int max_q_len,
                    const int8_t* k_cache, const int8_t* v_cache, const uint16_t* k_scale,
                    const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,

@@ -297,3 +297,52 @@ def llama70b_layer_device(layer, device, batch=64, seed=4):
     return dict(context_lens=lens.astype(np.int32), block_table=table, num_blocks=nb,
                 outlier_channels=outl, token_seq=seq, token_pos=pos, slot_mapping=slots,
                 k=k.to(torch.bfloat16), v=v.to(torch.bfloat16), q=q.to(torch.bfloat16))
+
+
+def long_context_258k(batch, device, ctx=258 * 1024, seed=7, num_q_heads=32, num_kv_heads=8,
+                      head_dim=128):
+    """Sequences of 258K tokens each for the equal-memory-budget comparison
+    ("KV-Cache 全栈优化系统" README, section 实验效果（摘要）: 258K context,
+    same GPU-memory budget), Llama-3.1-8B attention shape.  The block table
+    (a PCG64(seed) permutation of all blocks) and the key outlier channels
+    come from numpy; the tokens of sequence b are drawn on the device by
+    torch.Generator seeded seed * 1000 + b (K, then V; fp32 N(0, 1), the 4
+    outlier channels of each KV head of K scaled by 10, rounded to bf16), so
+    sequence b holds the same tokens whatever the batch.  Q row b [Hq, d] is
+    drawn N(0, 1) by a generator seeded seed * 1000 + 500 + b, rounded to bf16.
+    Returns a dict: context_lens, block_table, num_blocks, outlier_channels
+    (numpy), q (device bf16), tokens(b) -> (k, v) device bf16 [ctx, Hkv, d],
+    and slots(b) -> device int32 [ctx] physical slots of sequence b."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d, hkv = head_dim, num_kv_heads
+    outl = np.stack([rng.choice(d, size=4, replace=False) for _ in range(hkv)])
+    nbs = -(-ctx // BLOCK_SIZE)
+    nb = batch * nbs
+    table = rng.permutation(nb).astype(np.int32).reshape(batch, nbs)
+    lens = np.full(batch, ctx, np.int32)
+    qs = []
+    for b in range(batch):
+        gq = torch.Generator(device=device)
+        gq.manual_seed(seed * 1000 + 500 + b)
+        qs.append(torch.randn((num_q_heads, d), generator=gq, device=device,
+                              dtype=torch.float32))
+    q = torch.stack(qs).to(torch.bfloat16)
+    outl_t = [torch.from_numpy(outl[h]).to(device) for h in range(hkv)]
+    table_t = torch.from_numpy(table).to(device)
+
+    def tokens(b):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 1000 + b)
+        k = torch.randn((ctx, hkv, d), generator=g, device=device, dtype=torch.float32)
+        v = torch.randn((ctx, hkv, d), generator=g, device=device, dtype=torch.float32)
+        for h in range(hkv):
+            k[:, h, outl_t[h]] *= 10.0
+        return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+    def slots(b):
+        pos = torch.arange(ctx, device=device, dtype=torch.int64)
+        return (table_t[b].long()[pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE).to(torch.int32)
+
+    return dict(context_lens=lens, block_table=table, num_blocks=nb, outlier_channels=outl,
+                q=q, tokens=tokens, slots=slots)

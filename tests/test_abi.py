@@ -105,6 +105,44 @@ def test_decode_validation(kw, expected):
     assert decode(**kw) == expected
 
 
+def decode_bf16kv(**kw):
+    a = dict(q=P, dt=B.KV8_BF16, kc=P, vc=P, nb=100, bt=P, mbs=16, ctx=P, maxctx=256, b=2,
+             hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=P2, wsb=1 << 30, tps=0,
+             stream=None)
+    a.update(kw)
+    return B.load().paged_decode_attn_bf16kv(
+        a["q"], a["dt"], a["kc"], a["vc"], a["nb"], a["bt"], a["mbs"], a["ctx"], a["maxctx"],
+        a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"], a["out"], a["ws"], a["wsb"],
+        a["tps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(q=None), B.KV8_ERR_NULL),
+    (dict(kc=None), B.KV8_ERR_NULL),
+    (dict(vc=None), B.KV8_ERR_NULL),
+    (dict(bt=None), B.KV8_ERR_NULL),
+    (dict(ctx=None), B.KV8_ERR_NULL),
+    (dict(out=None), B.KV8_ERR_NULL),
+    (dict(b=0), B.KV8_ERR_SHAPE),
+    (dict(hq=30), B.KV8_ERR_SHAPE),
+    (dict(maxctx=-1), B.KV8_ERR_SHAPE),
+    (dict(mbs=0), B.KV8_ERR_SHAPE),
+    (dict(nb=0), B.KV8_ERR_SHAPE),
+    (dict(hq=24), B.KV8_ERR_UNSUPPORTED),
+    (dict(d=256), B.KV8_ERR_UNSUPPORTED),
+    (dict(bs=32), B.KV8_ERR_UNSUPPORTED),
+    (dict(dt=7), B.KV8_ERR_UNSUPPORTED),
+    (dict(tps=100), B.KV8_ERR_UNSUPPORTED),
+    (dict(q=MIS), B.KV8_ERR_ALIGN),
+    (dict(vc=MIS), B.KV8_ERR_ALIGN),
+    (dict(out=MIS), B.KV8_ERR_ALIGN),
+    (dict(ws=None), B.KV8_ERR_WORKSPACE),
+    (dict(wsb=16), B.KV8_ERR_WORKSPACE),
+])
+def test_decode_bf16kv_validation(kw, expected):
+    assert decode_bf16kv(**kw) == expected
+
+
 def test_decode_workspace_size():
     ws = B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 512)
     n_split = 8
