@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   // ---- q of the G heads: this lane's d/8 channels as fp16 pairs ----------
   half2_t qh[G][NP];
   half2_t ql[QF32 ? G : 1][QF32 ? NP : 1];
-  float cz[G], qbias[G];
+  float cz[G], nqb[G];          // nqb: minus the code bias of this lane's channels
   {
     const int64_t qrow0 = bh0 * D + chunk * CPL;
 #pragma unroll
@@ -200,34 +200,34 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           qsum += (float)l0 + (float)l1;
         }
       }
-      qsum = group8_sum(qsum);
       cz[h] = ldexpf(a.qk_scale_log2, e);
-      qbias[h] = kCodeBias * qsum;
+      nqb[h] = -kCodeBias * qsum;
     }
   }
   // per-lane constants of the logits this lane stores after the reduction
   const int tk = chunk >> 2;            // token of the pair: slot or slot+8
   int hv[NV];
-  float czl[NV], qbl[NV];
+  float czl[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     hv[j] = rs_head<G>(chunk, j);
     czl[j] = cz[0];
-    qbl[j] = qbias[0];
 #pragma unroll
-    for (int h = 1; h < G; ++h) {
-      czl[j] = hv[j] == h ? cz[h] : czl[j];
-      qbl[j] = hv[j] == h ? qbias[h] : qbl[j];
-    }
+    for (int h = 1; h < G; ++h) czl[j] = hv[j] == h ? cz[h] : czl[j];
   }
   __syncthreads();   // s_blk visible
 
-  // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1.
+  // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1; lane i of
+  // `mine` holds the id of the wave's block i, so a block's base address is
+  // scalar (readlane) and each lane adds its own row and channel offset.
   const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
   const int last = nmine - 1;
-  auto line_of = [&](int i) {
-    return ((int64_t)s_blk[wave + i * kWaves] * Hkv + g) * kBlock + slot;
+  const int mine = lane < nmine ? s_blk[wave + lane * kWaves] : 0;
+  auto row0_of = [&](int i) {       // first cache row of block i (wave-uniform)
+    const int id = __builtin_amdgcn_readlane(mine, i);
+    return ((int64_t)id * Hkv + g) * kBlock;
   };
+  const int lane_row = slot * D + chunk * CPL;   // this lane's byte offset in a block
 
   // ---- pass 1: logits ----------------------------------------------------
   float mloc[NV];
@@ -235,16 +235,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   for (int j = 0; j < NV; ++j) mloc[j] = kNegInf;
   if (nmine > 0) {
     Row r0[kPf], r1[kPf];
-    uint16_t ks0[kPf], ks1[kPf], vs0[kPf], vs1[kPf];
+    uint16_t ksc16[kPf], vsc16[kPf];
+    const int tok_row = slot + 8 * tk;            // the token whose logits this lane stores
     auto issue = [&](int s, int i) {
-      const int64_t line = line_of(i);
-      const int8_t* p = a.k_cache + line * D + chunk * CPL;
+      const int64_t row0 = row0_of(i);
+      const int8_t* p = a.k_cache + row0 * D + lane_row;
       r0[s] = *reinterpret_cast<const Row*>(p);
       r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
-      ks0[s] = a.k_scale[line];
-      ks1[s] = a.k_scale[line + 8];
-      vs0[s] = a.v_scale[line];
-      vs1[s] = a.v_scale[line + 8];
+      ksc16[s] = a.k_scale[row0 + tok_row];
+      vsc16[s] = a.v_scale[row0 + tok_row];
     };
     // Slots past the wave's last block re-read that block (L2 hits) and skip
     // the compute, so every load stays unconditional.
@@ -257,9 +256,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const int i = base + s;
         if (i < nmine) {
           const Row w0 = r0[s], w1 = r1[s];
+          // the sums start at minus the code bias of the lane's channels, so
+          // the 8-lane reduction yields the unbiased dot products
           float S[2 * G];
 #pragma unroll
-          for (int k = 0; k < 2 * G; ++k) S[k] = 0.0f;
+          for (int h = 0; h < G; ++h) S[h] = S[G + h] = nqb[h];
 #pragma unroll
           for (int k = 0; k < NDW; ++k) {
             const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
@@ -283,14 +284,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           reduce_scatter8<G>(S, R, chunk);
           const int tl = (wave + i * kWaves) * kBlock + slot + 8 * tk;
           const bool ok = tl < ntok;
-          const float ksc = fp16_bits_to_f32(tk ? ks1[s] : ks0[s]);
+          const float ksc = fp16_bits_to_f32(ksc16[s]);
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
-            const float z = ok ? (ksc * czl[j]) * (R[j] - qbl[j]) : kNegInf;
+            const float z = ok ? (ksc * czl[j]) * R[j] : kNegInf;
             s_z[tl * G + hv[j]] = z;
             mloc[j] = fmaxf(mloc[j], z);
           }
-          s_vs[tl] = tk ? vs1[s] : vs0[s];
+          s_vs[tl] = vsc16[s];
         }
         issue(s, min(i + kPf, last));
       }
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   // while the workgroup finishes the logits and builds the weights.
   Row r0[kPf], r1[kPf];
   auto issue_v = [&](int s, int i) {
-    const int8_t* p = a.v_cache + line_of(i) * D + chunk * CPL;
+    const int8_t* p = a.v_cache + row0_of(i) * D + lane_row;
     r0[s] = *reinterpret_cast<const Row*>(p);
     r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
   };
