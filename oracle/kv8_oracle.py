@@ -289,3 +289,148 @@ def paged_decode_bf16(q, k_cache_bits, v_cache_bits, block_table, context_lens,
             v = gather_bf16(v_cache_bits, block_table[b], ctx, g, block_size)
             out[b, h] = softmax_attention(q[b, h][None, :], k, v, sm_scale)[0]
     return out
+
+
+# --------------------------------------------------------------------------
+# FP8 (e4m3) KV cache.  "KV Cache 优化全景解析" section 7.4: the KV cache kept
+# as FP8, e4m3 (4 exponent bits, 3 mantissa bits, the more precise of the two
+# formats) with quantisation scales; section 11.3: about half the bytes of a
+# 16-bit cache.  Readings (listed in the design notes): the OCP e4m3 format
+# (bias 7, subnormals, largest finite 448, no infinity); one fp16 scale per
+# (token, KV head) as for INT8, s = fp16_rne(fp32_rne(absmax / 448));
+# codes = e4m3 round-to-nearest-even of the fp32 quotient x / s, saturated
+# to +-448; all-zero codes when s == 0; x_hat = e4m3 value * s.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes):
+    """fp64 value of e4m3 codes (uint8): sign bit 7, exponent bits 6..3
+    (bias 7), mantissa bits 2..0; exponent 0 holds the subnormals
+    m * 2^-9; the two all-ones patterns 0x7F / 0xFF are NaN."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e.astype(np.float64) - 10))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x):
+    """e4m3 codes of fp32 values x: round to nearest, ties to even, on the
+    exact grid (spacing 2^(e-3) for |x| in [2^e, 2^(e+1)), e >= -6; spacing
+    2^-9 below 2^-6), then saturate to +-448.  Zero keeps its sign."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    ulp = np.exp2(e - 3)
+    r = np.rint(a / ulp) * ulp                 # exact: power-of-two scaling, RNE
+    r = np.minimum(r, E4M3_MAX)
+    # code of the rounded magnitude r (a grid point or 448)
+    sub = r < 2.0 ** -6
+    ee = np.where(sub, 0, np.floor(np.log2(np.where(sub, 1.0, r))) + 7).astype(np.int64)
+    mm = np.where(sub, np.rint(r / 2.0 ** -9),
+                  np.rint(r / np.exp2(ee.astype(np.float64) - 7) * 8) - 8).astype(np.int64)
+    code = (ee << 3) | mm
+    return (np.where(np.signbit(x), 0x80, 0) | code).astype(np.uint8)
+
+
+def row_scale_fp8(x):
+    """fp16 scale of each row for FP8 codes: absmax / 448 rounded to fp32
+    then fp16 (nearest even, gradual underflow), saturated to 65504."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    s32 = a / np.float32(E4M3_MAX)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(FP16_MAX), s16).astype(np.float16)
+
+
+def codes_fp8_for_scale(x, s):
+    """e4m3 codes of rows x under fp16 scales s: IEEE fp32 quotient, then
+    e4m3_encode; rows with a zero scale give all-zero codes."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 / np.where(zero, np.float32(1), s32)
+    codes = e4m3_encode(quot)
+    return np.where(zero, np.uint8(0), codes).astype(np.uint8)
+
+
+def quantize_rows_fp8(x):
+    s = row_scale_fp8(x)
+    return codes_fp8_for_scale(x, s), s
+
+
+def dequantize_rows_fp8(codes, scales):
+    """x_hat = e4m3 value * scale, exact in fp64."""
+    return e4m3_value(codes) * np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+def quant_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                     block_size=BLOCK_SIZE):
+    """As quant_append, with e4m3 codes (uint8 caches)."""
+    kc, ks = quantize_rows_fp8(k_new)
+    vc, vs = quantize_rows_fp8(v_new)
+    for n, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        blk, off = slot_to_block(slot, block_size)
+        k_cache[blk, :, off, :] = kc[n]
+        v_cache[blk, :, off, :] = vc[n]
+        k_scale[blk, :, off] = ks[n]
+        v_scale[blk, :, off] = vs[n]
+
+
+def gather_dequant_fp8(codes, scales, block_table_row, ctx, kv_head, block_size=BLOCK_SIZE):
+    t = np.arange(ctx)
+    blk, off = logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return dequantize_rows_fp8(codes[blk, kv_head, off, :], scales[blk, kv_head, off])
+
+
+def paged_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                     sm_scale=None, block_size=BLOCK_SIZE):
+    """paged_decode over an e4m3 cache.  Returns fp64 [B, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    G = Hq // k_cache.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        if ctx <= 0:
+            continue
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant_fp8(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant_fp8(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[b, h] = softmax_attention(q[b, h][None, :], k, v, sm_scale)[0]
+    return out
+
+
+def paged_prefill_chunk_fp8(q, q_start_loc, k_cache, v_cache, k_scale, v_scale,
+                            block_table, context_lens, sm_scale=None, block_size=BLOCK_SIZE):
+    """paged_prefill_chunk over an e4m3 cache.  Returns fp64 [Tq, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    Tq, Hq, d = q.shape
+    G = Hq // k_cache.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((Tq, Hq, d), np.float64)
+    for b in range(len(context_lens)):
+        r0, r1 = int(q_start_loc[b]), int(q_start_loc[b + 1])
+        lc, ctx = r1 - r0, int(context_lens[b])
+        if lc <= 0 or ctx <= 0:
+            continue
+        visible = causal_visibility(ctx, lc)
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant_fp8(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant_fp8(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[r0:r1, h] = softmax_attention(q[r0:r1, h], k, v, sm_scale, visible)
+    return out

@@ -35,6 +35,11 @@ def _battery():
         ("bf16_sdpa", P.test_bf16_decode_matches_sdpa_fp64),
         ("bf16_closed_forms", P.test_bf16_decode_closed_forms_and_permutation),
         ("bf16_vs_int8", P.test_bf16_decode_equals_int8_decode_on_exact_values),
+        ("fp8_decode_codes", P.test_fp8_decode_every_code_vs_torch),
+        ("fp8_encode", P.test_fp8_encode_every_bf16_vs_torch_and_saturation),
+        ("fp8_quantiser", P.test_fp8_quantiser_invariants),
+        ("fp8_decode", P.test_fp8_decode_brute_force_and_sdpa),
+        ("fp8_prefill", P.test_fp8_prefill_equals_sdpa_causal),
     ]
     for name, fn in checks:
         try:
@@ -138,6 +143,36 @@ def _gather_bf16_head0(cache_bits, block_table_row, ctx, kv_head, block_size=16)
     return O.bf16_bits_to_f64(cache_bits[blk, 0, off, :])
 
 
+def _e4m3_truncate(x):
+    x = np.asarray(x, np.float32).astype(np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6.0)
+    ulp = np.exp2(e - 3)
+    r = np.minimum(np.floor(a / ulp) * ulp, 448.0)
+    sub = r < 2.0 ** -6
+    ee = np.where(sub, 0, np.floor(np.log2(np.where(sub, 1.0, r))) + 7).astype(np.int64)
+    mm = np.where(sub, np.rint(r / 2.0 ** -9),
+                  np.rint(r / np.exp2(ee.astype(np.float64) - 7) * 8) - 8).astype(np.int64)
+    return (np.where(np.signbit(x), 0x80, 0) | (ee << 3) | mm).astype(np.uint8)
+
+
+def _e4m3_value_bias8(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -10, (8 + m) * np.exp2(e.astype(np.float64) - 11))
+    return sign * np.where((c & 0x7F) == 0x7F, np.nan, mag)
+
+
+def _row_scale_fp8_127(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = (a / np.float32(127)).astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
 MUTANTS = {
     "head_map_mod": ("kv_head_of", lambda h, group: h % group),
     "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
@@ -160,6 +195,9 @@ MUTANTS = {
     "bf16_read_as_fp16": ("bf16_bits_to_f64", _bf16_as_fp16),
     "bf16_wrong_shift": ("bf16_bits_to_f64", _bf16_low_half),
     "bf16_gather_head0": ("gather_bf16", _gather_bf16_head0),
+    "fp8_encode_truncates": ("e4m3_encode", _e4m3_truncate),
+    "fp8_value_bias8": ("e4m3_value", _e4m3_value_bias8),
+    "fp8_scale_127": ("row_scale_fp8", _row_scale_fp8_127),
 }
 
 

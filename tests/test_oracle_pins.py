@@ -516,3 +516,119 @@ def test_bf16_decode_equals_int8_decode_on_exact_values():
     assert np.array_equal(W.bf16_bits_to_f32(kb), kc.astype(np.float32) / 64)   # exact
     out = O.paged_decode_bf16(case.q, kb, vb, case.block_table, case.context_lens)
     assert np.allclose(out, ref, rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) cache ("KV Cache 优化全景解析" section 7.4).  torch's
+# float8_e4m3fn is an independent implementation of the OCP e4m3 format: it
+# decodes every code and rounds to nearest even below the saturation point
+# (464 and above it gives NaN, where the quantiser saturates to 448).
+# ---------------------------------------------------------------------------
+def torch_e4m3(x32):
+    return torch.from_numpy(np.asarray(x32, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_fp8_decode_every_code_vs_torch():
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_value(c)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_fp8_encode_every_bf16_vs_torch_and_saturation():
+    x = W.bf16_bits_to_f32(np.arange(0x10000, dtype=np.uint32).astype(np.uint16))
+    x = x[np.isfinite(x)]
+    got = O.e4m3_encode(x)
+    inr = np.abs(x) < 464
+    assert np.array_equal(got[inr], torch_e4m3(x[inr]))
+    sat = ~inr
+    assert np.all(got[sat] == np.where(x[sat] < 0, 0xFE, 0x7E))
+    assert not np.any((got & 0x7F) == 0x7F)           # never NaN
+
+
+def test_fp8_encode_random_fp32_and_ties_vs_torch():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([
+        rng.uniform(-463.9, 463.9, 200000), rng.uniform(-1, 1, 200000) * 2.0 ** -5,
+        rng.standard_normal(200000) * 2.0 ** rng.integers(-12, 9, 200000),
+    ]).astype(np.float32)
+    # exact midpoints between neighbouring codes (ties go to the even code)
+    vals = O.e4m3_value(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids])
+    got = O.e4m3_encode(x)
+    inr = np.abs(x) < 464
+    assert np.array_equal(got[inr], torch_e4m3(x[inr]))
+    assert np.all(got[~inr] == np.where(x[~inr] < 0, 0xFE, 0x7E))
+
+
+def test_fp8_quantiser_invariants():
+    rng = np.random.default_rng(22)
+    rows = rng.standard_normal((2000, 64)).astype(np.float32) * \
+        np.exp2(rng.integers(-20, 12, 2000)).astype(np.float32)[:, None]
+    _, rows = W.to_bf16(rows)
+    rows = W.bf16_bits_to_f32(rows)
+    codes, s = O.quantize_rows_fp8(rows)
+    s64 = s.astype(np.float64)
+    i = np.argmax(np.abs(rows), axis=1)
+    top = codes[np.arange(len(rows)), i]
+    normal = s64 >= 2.0 ** -14                        # scale not subnormal
+    assert np.all((top[normal] & 0x7F) == 0x7E)       # the absmax lands on +-448
+    xhat = O.dequantize_rows_fp8(codes, s)
+    err = np.abs(xhat - rows)
+    # half an e4m3 step: 2^-4 relative above 2^-6 * s, 2^-10 * s below
+    bound = np.maximum(np.abs(rows) * 2.0 ** -4, 2.0 ** -10 * s64[:, None])
+    assert np.all(err[normal] <= bound[normal] * (1 + 1e-12))
+    z, sz = O.quantize_rows_fp8(np.zeros((3, 16), np.float32))
+    assert np.all(z == 0) and np.all(sz == 0)
+    neg, _ = O.quantize_rows_fp8(-rows)
+    assert np.array_equal(neg ^ 0x80, codes)           # symmetric, signed zero kept
+
+
+def build_cache_fp8(case):
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, case.num_kv_heads, case.head_dim)
+    kc, vc = kc.view(np.uint8), vc.view(np.uint8)
+    O.quant_append_fp8(case.k, case.v, case.slot_mapping, kc, vc, ks, vs)
+    return kc, vc, ks, vs
+
+
+def test_fp8_decode_brute_force_and_sdpa():
+    case = W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=16,
+                             context_lens=[1, 37, 130], q_dtype="f32", k_outliers=True, seed=23)
+    kc, vc, ks, vs = build_cache_fp8(case)
+    out = O.paged_decode_fp8(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    for b in range(3):
+        rk = case.k[case.token_seq == b]
+        rv = case.v[case.token_seq == b]
+        K = O.dequantize_rows_fp8(*O.quantize_rows_fp8(rk))
+        V = O.dequantize_rows_fp8(*O.quantize_rows_fp8(rv))
+        for h in range(8):
+            ref = brute_attention(case.q[b, h], K[:, h // 4], V[:, h // 4], 1 / math.sqrt(16))
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13)
+    v0 = O.gather_dequant_fp8(vc, vs, case.block_table[0], 1, 0)[0]
+    assert np.array_equal(out[0, 0], v0)              # single token: its V
+
+
+def test_fp8_prefill_equals_sdpa_causal():
+    case = W.prefill_case([0, 9], [21, 40], num_q_heads=4, num_kv_heads=2, head_dim=16, seed=24)
+    kc, vc, ks, vs = build_cache_fp8(case)
+    out = O.paged_prefill_chunk_fp8(case.q, case.extra["q_start_loc"], kc, vc, ks, vs,
+                                    case.block_table, case.context_lens)
+    qsl = case.extra["q_start_loc"]
+    for b in range(2):
+        ctx = int(case.context_lens[b])
+        K = np.stack([O.gather_dequant_fp8(kc, ks, case.block_table[b], ctx, g) for g in range(2)])
+        V = np.stack([O.gather_dequant_fp8(vc, vs, case.block_table[b], ctx, g) for g in range(2)])
+        lc = qsl[b + 1] - qsl[b]
+        q = torch.from_numpy(case.q[qsl[b]:qsl[b + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        Kt = torch.from_numpy(K).repeat_interleave(2, dim=0)[None]
+        Vt = torch.from_numpy(V).repeat_interleave(2, dim=0)[None]
+        pos = ctx - lc + np.arange(lc)
+        mask = torch.from_numpy(np.arange(ctx)[None, :] <= pos[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt, attn_mask=mask)
+        assert np.allclose(out[qsl[b]:qsl[b + 1]], ref[0].permute(1, 0, 2).numpy(),
+                           rtol=1e-11, atol=1e-12)
