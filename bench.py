@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=4)
     p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--fp8-steps", type=int, default=1,
+                   help="0 skips the FP8 (e4m3) cache lines")
     p.add_argument("--budget-steps", type=int, default=10,
                    help="decode calls timed per side of the 258K equal-budget comparison "
                         "(0 skips it)")
@@ -234,6 +236,10 @@ def main():
     torch.cuda.empty_cache()
     if args.prefill_steps > 0:
         result["prefill"] = bench_prefill(args, dev)
+    if args.fp8_steps > 0:
+        result["fp8_kv"] = {"decode": bench_fp8_decode(args, dev, case, d_bytes)}
+        if args.prefill_steps > 0:
+            result["fp8_kv"]["prefill"] = bench_prefill(args, dev, fp8=True)
     if args.budget_steps > 0:
         result["equal_budget_258k"] = bench_equal_budget(args, dev)
     if not args.no_cpu_baseline:
@@ -241,10 +247,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_prefill(args, dev):
-    """Chunked prefill over the INT8 cache (batch 8, 32/8 heads, d=128,
-    2048..8192 earlier tokens + a 512-row causal chunk): per step, append the
-    chunk's own K/V (4096 tokens), then paged_prefill_chunk_attn_kv8.  HIP
+def bench_prefill(args, dev, fp8=False):
+    """Chunked prefill over the INT8 (or FP8) cache (batch 8, 32/8 heads,
+    d=128, 2048..8192 earlier tokens + a 512-row causal chunk): per step,
+    append the chunk's own K/V (4096 tokens), then the prefill call.  HIP
     events on the stream the library launches on."""
     import torch
     from paged_int8_kv_amd import binding as B
@@ -256,8 +262,10 @@ def bench_prefill(args, dev):
     mask = case.extra["chunk_mask"]
     k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    cache = B.alloc_cache(case.num_blocks, hkv, d, dev)
-    B.kv8_quant_append(k_all, v_all, torch.from_numpy(case.slot_mapping).to(dev), *cache)
+    append = B.kv8_quant_append_fp8 if fp8 else B.kv8_quant_append
+    prefill = B.paged_prefill_chunk_attn_fp8kv if fp8 else B.paged_prefill_chunk_attn_kv8
+    cache = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=fp8)
+    append(k_all, v_all, torch.from_numpy(case.slot_mapping).to(dev), *cache)
     sel = torch.from_numpy(np.nonzero(mask)[0]).to(dev)
     k_new = k_all.index_select(0, sel).contiguous()
     v_new = v_all.index_select(0, sel).contiguous()
@@ -273,10 +281,10 @@ def bench_prefill(args, dev):
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        B.kv8_quant_append(k_new, v_new, s_new, *cache)
+        append(k_new, v_new, s_new, *cache)
         if ev is not None:
             ev[1].record()
-        B.paged_prefill_chunk_attn_kv8(q, qsl, chunk, *cache, table, lens, max_ctx, out)
+        prefill(q, qsl, chunk, *cache, table, lens, max_ctx, out)
         if ev is not None:
             ev[2].record()
 
@@ -293,7 +301,7 @@ def bench_prefill(args, dev):
     flops = prefill_flops(ctx, np.full(len(ctx), chunk), hq, d)
     tf = flops / (float(pre.mean()) * 1e-3) / 1e12
     return {"workload": "chunked prefill: B=8, Hq=32, Hkv=8, d=128, ctx_prev~U[2048,8192] + "
-                        "512-row causal chunk, bf16 Q, int8 KV cache",
+                        f"512-row causal chunk, bf16 Q, {'fp8 e4m3' if fp8 else 'int8'} KV cache",
             "steps": args.prefill_steps,
             "prefill_us": {"mean": round(float(pre.mean()) * 1e3, 2),
                            "p50": round(float(np.percentile(pre, 50)) * 1e3, 2)},
@@ -301,8 +309,51 @@ def bench_prefill(args, dev):
             "flops_per_call": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("prefill"),
-                         "kernel": "paged_prefill_chunk_attn_kv8 (fp16 MFMA 32x32x16)"}}
+                         "traffic": None if fp8 else measured_traffic("prefill"),
+                         "kernel": ("paged_prefill_chunk_attn_fp8kv" if fp8 else
+                                    "paged_prefill_chunk_attn_kv8") + " (fp16 MFMA 32x32x16)"}}
+
+
+def bench_fp8_decode(args, dev, case, d_bytes):
+    """paged_decode_attn_fp8kv on the same decode workload, cache written by
+    kv8_quant_append_fp8, launches back to back over rotated replicas."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    bsz, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
+    max_ctx = int(case.context_lens.max())
+    k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    caches = []
+    for _ in range(args.replicas):
+        c = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=True)
+        B.kv8_quant_append_fp8(k_all, v_all, slots, *c)
+        caches.append(c)
+    del k_all, v_all
+    q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    table = torch.from_numpy(case.block_table).to(dev)
+    lens = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx), dtype=torch.uint8,
+                     device=dev)
+    n = max(args.steps, 50)
+    for i in range(10):
+        B.paged_decode_attn_fp8kv(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        B.paged_decode_attn_fp8kv(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / n * 1e3
+    del caches, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": "the decode layer above over an FP8 (e4m3) cache, decode launches back "
+                        "to back", "decode_us": round(us, 2),
+            "kv_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
+            "kv_tokens_per_s": round(float(case.context_lens.sum()) / (us * 1e-6), 1)}
 
 
 def bench_equal_budget(args, dev):

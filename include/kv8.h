@@ -235,6 +235,55 @@ int paged_prefill_chunk_attn_kv8(const uint16_t* q, const int32_t* q_start_loc,
                                  float* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/*
+ * FP8 (e4m3) cache.  The KV cache kept as FP8 e4m3 with quantisation
+ * scales ("KV Cache 优化全景解析", section 7.4; about half the bytes of a
+ * 16-bit cache, section 11.3).  Same layout as the INT8 cache: one byte per
+ * element, codes [num_blocks, Hkv, 16, d] and one fp16 scale per (token
+ * slot, KV head) for K and for V.  Codes are OCP e4m3 (bias 7, subnormals,
+ * largest finite 448, no infinity):
+ *   s    = fp16_rne(fp32_rne(absmax / 448)), saturated to 65504;
+ *   code = e4m3 round-to-nearest-even of the fp32 quotient x / s, saturated
+ *          to +-448 (never NaN), the sign of a zero kept; all-zero codes
+ *          when s == 0;
+ *   x_hat = e4m3 value(code) * s.
+ * kv8_quant_append_fp8, paged_decode_attn_fp8kv and
+ * paged_prefill_chunk_attn_fp8kv take the same arguments, with the same
+ * meaning, ownership and errors, as their INT8 counterparts above (the
+ * decode workspace is sized by kv8_decode_workspace_size); only the code
+ * format of the cache differs.
+ */
+int kv8_quant_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* slot_mapping, int64_t n_tokens,
+                         int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks,
+                         uint8_t* k_cache, uint8_t* v_cache,
+                         uint16_t* k_scale, uint16_t* v_scale,
+                         void* stream);
+
+int paged_decode_attn_fp8kv(const void* q, int q_dtype,
+                            const uint8_t* k_cache, const uint8_t* v_cache,
+                            const uint16_t* k_scale, const uint16_t* v_scale,
+                            int64_t num_blocks,
+                            const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* context_lens, int max_context_len,
+                            int batch, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, float sm_scale,
+                            float* out, void* workspace, size_t workspace_bytes,
+                            int tokens_per_split, void* stream);
+
+int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc,
+                                   int64_t total_q, int max_q_len,
+                                   const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const uint16_t* k_scale, const uint16_t* v_scale,
+                                   int64_t num_blocks,
+                                   const int32_t* block_table, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int max_context_len,
+                                   int batch, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int block_size, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

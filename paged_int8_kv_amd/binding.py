@@ -26,7 +26,8 @@ BLOCK_SIZE = 16
 EXPORTED = (
     "kv8_status_string", "kv8_version", "kv8_quant_append", "kv8_decode_workspace_size",
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
-    "paged_prefill_chunk_attn_kv8",
+    "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
+    "paged_prefill_chunk_attn_fp8kv",
 )
 
 _lib = None
@@ -59,11 +60,15 @@ def load():
     lib.kv8_version.argtypes = []
     lib.kv8_quant_append.restype = i32
     lib.kv8_quant_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.kv8_quant_append_fp8.restype = i32
+    lib.kv8_quant_append_fp8.argtypes = lib.kv8_quant_append.argtypes
     lib.kv8_decode_workspace_size.restype = sz
     lib.kv8_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_decode_attn_kv8.restype = i32
     lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
+    lib.paged_decode_attn_fp8kv.restype = i32
+    lib.paged_decode_attn_fp8kv.argtypes = lib.paged_decode_attn_kv8.argtypes
     lib.paged_decode_attn_bf16kv.restype = i32
     lib.paged_decode_attn_bf16kv.argtypes = [vp, i32, vp, vp, i64, vp, i32, vp, i32,
                                              i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
@@ -73,6 +78,8 @@ def load():
     lib.paged_prefill_chunk_attn_kv8.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp, i64, vp,
                                                  i32, vp, i32, i32, i32, i32, i32, i32, f32,
                                                  vp, vp, sz, vp]
+    lib.paged_prefill_chunk_attn_fp8kv.restype = i32
+    lib.paged_prefill_chunk_attn_fp8kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
     _lib = lib
     return lib
 
@@ -99,16 +106,28 @@ def _check(status, where):
 # ---------------------------------------------------------------------------
 # torch-facing wrappers (same names as the C entry points)
 # ---------------------------------------------------------------------------
+def _append(name, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream):
+    n, hkv, d = k_new.shape
+    nb = k_cache.shape[0]
+    st = getattr(load(), name)(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n, hkv, d,
+                               BLOCK_SIZE, nb, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                               _ptr(v_scale), _stream(stream))
+    _check(st, name)
+
+
 def kv8_quant_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
                      stream=None):
     """k_new/v_new: bf16 [N, Hkv, d]; slot_mapping int32 [N]; caches as in
     include/kv8.h.  Enqueues on the current (or given) stream."""
-    n, hkv, d = k_new.shape
-    nb = k_cache.shape[0]
-    st = load().kv8_quant_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n, hkv, d,
-                                 BLOCK_SIZE, nb, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-                                 _ptr(v_scale), _stream(stream))
-    _check(st, "kv8_quant_append")
+    _append("kv8_quant_append", k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+            stream)
+
+
+def kv8_quant_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                         stream=None):
+    """As kv8_quant_append, into an FP8 (e4m3) cache (uint8 codes)."""
+    _append("kv8_quant_append_fp8", k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
+            v_scale, stream)
 
 
 def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
@@ -117,24 +136,38 @@ def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_co
                                                 max_context_len, tokens_per_split))
 
 
-def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
-                          max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
-                          stream=None):
-    """q: fp32 or bf16 [B, Hq, d]; out fp32 [B, Hq, d]; workspace uint8 of at
-    least kv8_decode_workspace_size() bytes."""
+def _decode(name, q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+            max_context_len, out, workspace, sm_scale, tokens_per_split, stream):
     import torch
     b, hq, d = q.shape
     nb, hkv = k_cache.shape[0], k_cache.shape[1]
     dt = KV8_BF16 if q.dtype == torch.bfloat16 else KV8_F32
     if sm_scale is None:
         sm_scale = d ** -0.5
-    st = load().paged_decode_attn_kv8(
+    st = getattr(load(), name)(
         _ptr(q), dt, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nb,
         _ptr(block_table), block_table.shape[1], _ptr(context_lens), int(max_context_len),
         b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         int(tokens_per_split), _stream(stream))
-    _check(st, "paged_decode_attn_kv8")
+    _check(st, name)
+
+
+def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                          max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
+                          stream=None):
+    """q: fp32 or bf16 [B, Hq, d]; out fp32 [B, Hq, d]; workspace uint8 of at
+    least kv8_decode_workspace_size() bytes."""
+    _decode("paged_decode_attn_kv8", q, k_cache, v_cache, k_scale, v_scale, block_table,
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+
+
+def paged_decode_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                            max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
+                            stream=None):
+    """As paged_decode_attn_kv8, over an FP8 (e4m3) cache."""
+    _decode("paged_decode_attn_fp8kv", q, k_cache, v_cache, k_scale, v_scale, block_table,
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
 
 
 def paged_decode_attn_bf16kv(q, k_cache, v_cache, block_table, context_lens, max_context_len,
@@ -163,32 +196,49 @@ def kv8_prefill_workspace_size(batch, num_q_heads, head_dim, max_q_len, max_cont
                                                  max_context_len))
 
 
-def paged_prefill_chunk_attn_kv8(q, q_start_loc, max_q_len, k_cache, v_cache, k_scale, v_scale,
-                                 block_table, context_lens, max_context_len, out,
-                                 workspace=None, sm_scale=None, stream=None):
-    """q: bf16 [total_q, Hq, d]; q_start_loc int32 [B+1]; out fp32
-    [total_q, Hq, d]."""
+def _prefill(name, q, q_start_loc, max_q_len, k_cache, v_cache, k_scale, v_scale, block_table,
+             context_lens, max_context_len, out, workspace, sm_scale, stream):
     tq, hq, d = q.shape
     nb, hkv = k_cache.shape[0], k_cache.shape[1]
     b = context_lens.shape[0]
     if sm_scale is None:
         sm_scale = d ** -0.5
-    st = load().paged_prefill_chunk_attn_kv8(
+    st = getattr(load(), name)(
         _ptr(q), _ptr(q_start_loc), tq, int(max_q_len), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), nb, _ptr(block_table), block_table.shape[1],
         _ptr(context_lens), int(max_context_len), b, hq, hkv, d, BLOCK_SIZE, float(sm_scale),
         _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream))
-    _check(st, "paged_prefill_chunk_attn_kv8")
+    _check(st, name)
 
 
-def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda"):
-    """Zeroed paged cache tensors: codes int8 [NB, Hkv, 16, d] and fp16
-    scales [NB, Hkv, 16] (stored as int16 bit patterns), for K and V."""
+def paged_prefill_chunk_attn_kv8(q, q_start_loc, max_q_len, k_cache, v_cache, k_scale, v_scale,
+                                 block_table, context_lens, max_context_len, out,
+                                 workspace=None, sm_scale=None, stream=None):
+    """q: bf16 [total_q, Hq, d]; q_start_loc int32 [B+1]; out fp32
+    [total_q, Hq, d]."""
+    _prefill("paged_prefill_chunk_attn_kv8", q, q_start_loc, max_q_len, k_cache, v_cache,
+             k_scale, v_scale, block_table, context_lens, max_context_len, out, workspace,
+             sm_scale, stream)
+
+
+def paged_prefill_chunk_attn_fp8kv(q, q_start_loc, max_q_len, k_cache, v_cache, k_scale,
+                                   v_scale, block_table, context_lens, max_context_len, out,
+                                   workspace=None, sm_scale=None, stream=None):
+    """As paged_prefill_chunk_attn_kv8, over an FP8 (e4m3) cache."""
+    _prefill("paged_prefill_chunk_attn_fp8kv", q, q_start_loc, max_q_len, k_cache, v_cache,
+             k_scale, v_scale, block_table, context_lens, max_context_len, out, workspace,
+             sm_scale, stream)
+
+
+def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False):
+    """Zeroed paged cache tensors: codes int8 (uint8 for the FP8 cache)
+    [NB, Hkv, 16, d] and fp16 scales [NB, Hkv, 16] (stored as int16 bit
+    patterns), for K and V."""
     import torch
-    kc = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), dtype=torch.int8,
-                     device=device)
+    kc = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim),
+                     dtype=torch.uint8 if fp8 else torch.int8, device=device)
     vc = torch.zeros_like(kc)
     ks = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.int16, device=device)
     vs = torch.zeros_like(ks)

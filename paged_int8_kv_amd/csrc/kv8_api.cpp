@@ -32,29 +32,10 @@ int check_cache(const int8_t* kc, const int8_t* vc, const uint16_t* ks, const ui
   return KV8_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kv8_status_string(int status) {
-  switch (status) {
-    case KV8_OK: return "KV8_OK";
-    case KV8_ERR_NULL: return "KV8_ERR_NULL: a required pointer is NULL";
-    case KV8_ERR_SHAPE: return "KV8_ERR_SHAPE: invalid or inconsistent size";
-    case KV8_ERR_UNSUPPORTED: return "KV8_ERR_UNSUPPORTED: unsupported shape or dtype";
-    case KV8_ERR_ALIGN: return "KV8_ERR_ALIGN: pointer not 16-byte aligned";
-    case KV8_ERR_WORKSPACE: return "KV8_ERR_WORKSPACE: workspace missing or too small";
-    case KV8_ERR_HIP: return "KV8_ERR_HIP: HIP launch error";
-    default: return "unknown kv8 status";
-  }
-}
-
-int kv8_version(void) { return kVersion; }
-
-int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
-                     const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+int append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
+                 int64_t n_tokens, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,
-                     int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
+                     int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, bool fp8, void* stream) {
   if (n_tokens < 0 || num_kv_heads <= 0) return KV8_ERR_SHAPE;
   if (!supported_dim(head_dim)) return KV8_ERR_UNSUPPORTED;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
@@ -65,28 +46,18 @@ int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
   if (n_tokens * num_kv_heads * (head_dim / 8) / 256 >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;
   const int r = kv8::launch_quant_append(k_new, v_new, slot_mapping, n_tokens, num_kv_heads,
                                          head_dim, num_blocks, k_cache, v_cache, k_scale,
-                                         v_scale, static_cast<hipStream_t>(stream));
+                                         v_scale, fp8, static_cast<hipStream_t>(stream));
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
 }
 
-size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_context_len, int tokens_per_split) {
-  if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
-  kv8::DecodePlan plan;
-  if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        tokens_per_split, &plan))
-    return 0;
-  return plan.total_bytes;
-}
-
-int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
+int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                           const int8_t* v_cache, const uint16_t* k_scale,
                           const uint16_t* v_scale, int64_t num_blocks,
                           const int32_t* block_table, int max_blocks_per_seq,
                           const int32_t* context_lens, int max_context_len, int batch,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, void* stream) {
+                          int tokens_per_split, bool fp8, void* stream) {
   if (!q || !block_table || !context_lens || !out) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
   if (rc != KV8_OK) return rc;
@@ -111,10 +82,120 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
   const int r = kv8::launch_decode(q, q_dtype == KV8_F32, k_cache, v_cache, k_scale, v_scale,
                                    num_blocks, block_table, max_blocks_per_seq, context_lens,
                                    ctx_cap, batch, num_q_heads, num_kv_heads, head_dim,
-                                   sm_scale, out, workspace, plan,
+                                   sm_scale, out, workspace, plan, fp8,
                                    static_cast<hipStream_t>(stream));
   if (r == -2) return KV8_ERR_UNSUPPORTED;
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
+}
+
+int prefill_impl(const uint16_t* q, const int32_t* q_start_loc,
+                                 int64_t total_q, int max_q_len, const int8_t* k_cache,
+                                 const int8_t* v_cache, const uint16_t* k_scale,
+                                 const uint16_t* v_scale, int64_t num_blocks,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, int batch,
+                                 int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, float sm_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, bool fp8, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (!q_start_loc || !block_table || !context_lens) return KV8_ERR_NULL;
+  const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
+  if (rc != KV8_OK) return rc;
+  if (batch <= 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return KV8_ERR_SHAPE;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return KV8_ERR_SHAPE;
+  if (batch > 65535 || num_q_heads > 65535) return KV8_ERR_SHAPE;
+  if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
+    return KV8_ERR_UNSUPPORTED;
+  if (total_q == 0 || max_q_len == 0) return KV8_OK;
+  if (!q || !out) return KV8_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return KV8_ERR_ALIGN;
+  const long long cap_blocks = (long long)max_blocks_per_seq * KV8_BLOCK_SIZE;
+  const int ctx_cap = (int)(cap_blocks < max_context_len ? cap_blocks : max_context_len);
+  const int r = kv8::launch_prefill(q, q_start_loc, total_q, max_q_len, k_cache, v_cache,
+                                    k_scale, v_scale, num_blocks, block_table,
+                                    max_blocks_per_seq, context_lens, ctx_cap, batch,
+                                    num_q_heads, num_kv_heads, head_dim, sm_scale, out, fp8,
+                                    static_cast<hipStream_t>(stream));
+  if (r == -2) return KV8_ERR_UNSUPPORTED;
+  return r == 0 ? KV8_OK : KV8_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv8_status_string(int status) {
+  switch (status) {
+    case KV8_OK: return "KV8_OK";
+    case KV8_ERR_NULL: return "KV8_ERR_NULL: a required pointer is NULL";
+    case KV8_ERR_SHAPE: return "KV8_ERR_SHAPE: invalid or inconsistent size";
+    case KV8_ERR_UNSUPPORTED: return "KV8_ERR_UNSUPPORTED: unsupported shape or dtype";
+    case KV8_ERR_ALIGN: return "KV8_ERR_ALIGN: pointer not 16-byte aligned";
+    case KV8_ERR_WORKSPACE: return "KV8_ERR_WORKSPACE: workspace missing or too small";
+    case KV8_ERR_HIP: return "KV8_ERR_HIP: HIP launch error";
+    default: return "unknown kv8 status";
+  }
+}
+
+int kv8_version(void) { return kVersion; }
+
+int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                     int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,
+                     int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
+  return append_impl(k_new, v_new, slot_mapping, n_tokens, num_kv_heads, head_dim, block_size,
+                     num_blocks, k_cache, v_cache, k_scale, v_scale, false, stream);
+}
+
+int kv8_quant_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int64_t num_blocks, uint8_t* k_cache,
+                         uint8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
+  return append_impl(k_new, v_new, slot_mapping, n_tokens, num_kv_heads, head_dim, block_size,
+                     num_blocks, reinterpret_cast<int8_t*>(k_cache),
+                     reinterpret_cast<int8_t*>(v_cache), k_scale, v_scale, true, stream);
+}
+
+size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int tokens_per_split) {
+  if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
+  kv8::DecodePlan plan;
+  if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        tokens_per_split, &plan))
+    return 0;
+  return plan.total_bytes;
+}
+
+int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
+                          const int8_t* v_cache, const uint16_t* k_scale,
+                          const uint16_t* v_scale, int64_t num_blocks,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* context_lens, int max_context_len, int batch,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                          int tokens_per_split, void* stream) {
+  return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                     workspace_bytes, tokens_per_split, false, stream);
+}
+
+int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
+                            const uint8_t* v_cache, const uint16_t* k_scale,
+                            const uint16_t* v_scale, int64_t num_blocks,
+                            const int32_t* block_table, int max_blocks_per_seq,
+                            const int32_t* context_lens, int max_context_len, int batch,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                            int tokens_per_split, void* stream) {
+  return decode_impl(q, q_dtype, reinterpret_cast<const int8_t*>(k_cache),
+                     reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
+                     block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                     workspace_bytes, tokens_per_split, true, stream);
 }
 
 int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache,
@@ -170,30 +251,27 @@ int paged_prefill_chunk_attn_kv8(const uint16_t* q, const int32_t* q_start_loc,
                                  int num_q_heads, int num_kv_heads, int head_dim,
                                  int block_size, float sm_scale, float* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes;
-  if (!q_start_loc || !block_table || !context_lens) return KV8_ERR_NULL;
-  const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
-  if (rc != KV8_OK) return rc;
-  if (batch <= 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0)
-    return KV8_ERR_SHAPE;
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return KV8_ERR_SHAPE;
-  if (batch > 65535 || num_q_heads > 65535) return KV8_ERR_SHAPE;
-  if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
-    return KV8_ERR_UNSUPPORTED;
-  if (total_q == 0 || max_q_len == 0) return KV8_OK;
-  if (!q || !out) return KV8_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out)) return KV8_ERR_ALIGN;
-  const long long cap_blocks = (long long)max_blocks_per_seq * KV8_BLOCK_SIZE;
-  const int ctx_cap = (int)(cap_blocks < max_context_len ? cap_blocks : max_context_len);
-  const int r = kv8::launch_prefill(q, q_start_loc, total_q, max_q_len, k_cache, v_cache,
-                                    k_scale, v_scale, num_blocks, block_table,
-                                    max_blocks_per_seq, context_lens, ctx_cap, batch,
-                                    num_q_heads, num_kv_heads, head_dim, sm_scale, out,
-                                    static_cast<hipStream_t>(stream));
-  if (r == -2) return KV8_ERR_UNSUPPORTED;
-  return r == 0 ? KV8_OK : KV8_ERR_HIP;
+  return prefill_impl(q, q_start_loc, total_q, max_q_len, k_cache, v_cache, k_scale, v_scale,
+                      num_blocks, block_table, max_blocks_per_seq, context_lens,
+                      max_context_len, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                      sm_scale, out, workspace, workspace_bytes, false, stream);
+}
+
+int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc,
+                                   int64_t total_q, int max_q_len, const uint8_t* k_cache,
+                                   const uint8_t* v_cache, const uint16_t* k_scale,
+                                   const uint16_t* v_scale, int64_t num_blocks,
+                                   const int32_t* block_table, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int max_context_len, int batch,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, float sm_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, q_start_loc, total_q, max_q_len,
+                      reinterpret_cast<const int8_t*>(k_cache),
+                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
+                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
+                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                      workspace_bytes, true, stream);
 }
 
 }  // extern "C"

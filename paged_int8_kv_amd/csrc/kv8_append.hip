@@ -1,5 +1,6 @@
-// kv8_quant_append kernel: per-token, per-KV-head INT8 quantisation of new
-// K/V rows and their scatter into 16-token physical blocks.
+// kv8_quant_append kernel: per-token, per-KV-head quantisation of new K/V
+// rows to INT8 (or to FP8 e4m3 for the FP8 cache) and their scatter into
+// 16-token physical blocks.
 //
 // The method keeps K/V as INT8 produced by dynamic per-token quantisation
 // ("KV-Cache 全栈优化系统" README, section 主要特性); slots address physical
@@ -10,8 +11,9 @@
 // K and the same 8 of V.  The absmax is reduced across the LPR lanes with
 // DPP; the fp32 scale is divided with IEEE-correct division (hipcc's
 // default), rounded to fp16 (round-to-nearest-even, subnormals kept) and
-// saturated to 65504; codes use IEEE division, v_rndne (ties to even) and a
-// symmetric clamp.  Each lane stores its 8 codes (8 bytes) so that the LPR
+// saturated to 65504; codes use IEEE division, then v_rndne (ties to even)
+// and a symmetric clamp for INT8, or round-to-nearest-even on the e4m3 grid
+// with saturation for FP8 (the code formats are described in kv8_device.h).  Each lane stores its 8 codes (8 bytes) so that the LPR
 // lanes write one contiguous d-byte row of the block.
 #include "kv8_device.h"
 #include "kv8_launch.h"
@@ -27,26 +29,22 @@ __device__ __forceinline__ float row_absmax(float a) {
   else return group16_max(a);
 }
 
+template <class C>
 __device__ __forceinline__ float fp16_scale(float absmax) {
-  const float s32 = absmax / 127.0f;                 // IEEE divide, RNE
+  const float s32 = absmax / C::kQmax;               // IEEE divide, RNE
   _Float16 s16 = (_Float16)s32;                       // RNE, gradual underflow
   if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
   return (float)s16;
 }
 
-__device__ __forceinline__ uint32_t code_byte(float x, float s) {
-  float q = __builtin_rintf(x / s);                   // IEEE divide, ties to even
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (uint32_t)((int32_t)q) & 0xFFu;
-}
-
+template <class C>
 __device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
   uint32_t w0 = 0, w1 = 0;
   if (s != 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w0 |= code_byte(x[i], s) << (8 * i);
+    for (int i = 0; i < 4; ++i) w0 |= C::code(x[i], s) << (8 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w1 |= code_byte(x[4 + i], s) << (8 * i);
+    for (int i = 0; i < 4; ++i) w1 |= C::code(x[4 + i], s) << (8 * i);
   }
   return make_uint2(w0, w1);
 }
@@ -62,7 +60,7 @@ __device__ __forceinline__ void unpack8(uint4 raw, float (&x)[8], float& amax) {
   }
 }
 
-template <int D>
+template <int D, class C>
 __global__ __launch_bounds__(256) void quant_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ slot_mapping, int64_t n_rows, int num_kv_heads,
@@ -89,10 +87,10 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
   va = row_absmax<LPR>(va);
   if (!keep) return;
 
-  const float ks = fp16_scale(ka);
-  const float vs = fp16_scale(va);
-  const uint2 kc = quantise8(kx, ks);
-  const uint2 vc = quantise8(vx, vs);
+  const float ks = fp16_scale<C>(ka);
+  const float vs = fp16_scale<C>(va);
+  const uint2 kc = quantise8<C>(kx, ks);
+  const uint2 vc = quantise8<C>(vx, vs);
 
   const int64_t blk = slot / kBlock;
   const int off = (int)(slot % kBlock);
@@ -107,23 +105,38 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
 
 }  // namespace
 
-int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
-                        const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
-                        int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
-                        uint16_t* k_scale, uint16_t* v_scale, hipStream_t stream) {
-  const int64_t n_rows = n_tokens * num_kv_heads;
+namespace {
+template <class C>
+void launch_append_fmt(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
+                       int64_t n_rows, int num_kv_heads, int head_dim, int64_t num_slots,
+                       int8_t* k_cache, int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
+                       hipStream_t stream) {
   const int64_t threads = n_rows * (head_dim / 8);
   const int64_t grid = (threads + 255) / 256;
-  const int64_t num_slots = num_blocks * kBlock;
   if (head_dim == 128) {
-    quant_append_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+    quant_append_kernel<128, C><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
         k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
         k_scale, v_scale);
   } else {
-    quant_append_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+    quant_append_kernel<64, C><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
         k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
         k_scale, v_scale);
   }
+}
+}  // namespace
+
+int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                        const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                        int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
+                        uint16_t* k_scale, uint16_t* v_scale, bool fp8, hipStream_t stream) {
+  const int64_t n_rows = n_tokens * num_kv_heads;
+  const int64_t num_slots = num_blocks * kBlock;
+  if (fp8)
+    launch_append_fmt<CodesFp8>(k_new, v_new, slot_mapping, n_rows, num_kv_heads, head_dim,
+                                num_slots, k_cache, v_cache, k_scale, v_scale, stream);
+  else
+    launch_append_fmt<CodesInt8>(k_new, v_new, slot_mapping, n_rows, num_kv_heads, head_dim,
+                                 num_slots, k_cache, v_cache, k_scale, v_scale, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -1,5 +1,5 @@
-// paged_decode_attn_kv8 kernel: split-K flash-decoding over the paged INT8
-// cache for gfx950.
+// paged_decode_attn_kv8 / paged_decode_attn_fp8kv kernel: split-K
+// flash-decoding over the paged INT8 (or FP8 e4m3) cache for gfx950.
 //
 // Attention softmax(q K^T * sm_scale) V ("KV Cache 优化全景解析", section 2.1)
 // per GQA group (section 3.3) over K/V restored on the fly from INT8 codes
@@ -26,10 +26,13 @@
 // Because the exact split max is known before pass 2, no accumulator is
 // ever rescaled and the largest weight of the split is exact.
 //
-// Dot products use v_dot2_f32_f16 on fp16 pairs.  A code c enters as the
-// fp16 value c + 1152 built by one byte permute (see kv8_device.h); the
-// bias is removed once per token (pass 1: 1152 * sum q_h) and once per
-// output (pass 2: 1152 * sum w).  q enters as fp16 after an exact
+// Dot products use v_dot2_f32_f16 on fp16 pairs.  An INT8 code c enters as
+// the fp16 value c + 1152 built by one byte permute (see kv8_device.h); the
+// bias is removed once per token (pass 1: the sums start at minus 1152 *
+// sum q_h) and once per output (pass 2: 1152 * sum w).  The same kernel
+// serves the FP8 (e4m3) cache ("KV Cache 优化全景解析", section 7.4), whose
+// codes become exact fp16 pairs by one hardware convert and carry no bias.
+// q enters as fp16 after an exact
 // per-head power-of-two rescale (bf16 q is exact in fp16 then); an fp32 q
 // is split into a high and a low fp16 part.
 //
@@ -106,7 +109,7 @@ __device__ __forceinline__ uint32_t dword(const uint4& r, int k) {
 }
 __device__ __forceinline__ uint32_t dword(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
 
-template <int D, int G, bool QF32>
+template <int D, int G, bool QF32, class C>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   constexpr int CPL = D / 8;    // channels (= code bytes) per lane per token
   constexpr int NDW = CPL / 4;  // dwords per lane per token
@@ -260,12 +263,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           // the 8-lane reduction yields the unbiased dot products
           float S[2 * G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) S[h] = S[G + h] = nqb[h];
+          for (int h = 0; h < G; ++h) S[h] = S[G + h] = C::kBiased ? nqb[h] : 0.0f;
 #pragma unroll
           for (int k = 0; k < NDW; ++k) {
-            const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
-            const half2_t a0 = biased_pair_lo(x0), b0 = biased_pair_hi(x0);
-            const half2_t a1 = biased_pair_lo(x1), b1 = biased_pair_hi(x1);
+            const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
+            const half2_t a0 = C::lo(x0), b0 = C::hi(x0);
+            const half2_t a1 = C::lo(x1), b1 = C::hi(x1);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               S[h] = fdot2(qh[h][2 * k], a0, S[h]);
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const float p = __builtin_amdgcn_exp2f(z - Mh);
         p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
         lsum += p;
-        psum += (float)p16;
+        if constexpr (C::kBiased) psum += (float)p16;
       }
       const int jj = t / kBlock, r = t % kBlock;
       pph[((jj * 8 + (r & 7)) * G + h) * 2 + (r >> 3)] = p16;
@@ -372,10 +375,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         for (int h = 0; h < G; ++h) wp[h] = __builtin_bit_cast(half2_t, src[h]);
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
-          const uint32_t x0 = dword(w0, k) ^ kXor80, x1 = dword(w1, k) ^ kXor80;
+          const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
           const uint32_t i01 = interleave_lo(x0, x1), i23 = interleave_hi(x0, x1);
-          const half2_t f0 = biased_pair_lo(i01), f1 = biased_pair_hi(i01);
-          const half2_t f2 = biased_pair_lo(i23), f3 = biased_pair_hi(i23);
+          const half2_t f0 = C::lo(i01), f1 = C::hi(i01);
+          const half2_t f2 = C::lo(i23), f3 = C::hi(i23);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             acc[h * CPL + 4 * k] = fdot2(wp[h], f0, acc[h * CPL + 4 * k]);
@@ -391,32 +394,41 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 
   groups_to_lds<G, CPL, D>(acc, s_fin, wave, lane, chunk);
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, true>(
+  finish_split<G, D, kThreads, kWaves, C::kBiased>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
       bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
-template <int D, int G, bool QF32>
+template <int D, int G, bool QF32, class C>
 bool launch_split(const SplitArgs& a, int batch, hipStream_t stream) {
   const SmemLayout L = smem_layout(a.split_tokens, G, D);
   SplitArgs args = a;
-  const int64_t grid = item_grid<decode_split_kernel<D, G, QF32>>(
+  const int64_t grid = item_grid<decode_split_kernel<D, G, QF32, C>>(
       kThreads, L.total, batch, (int64_t)a.n_split * a.num_kv_heads * batch, &args.period,
       &args.snake_rounds);
   if (grid > 0x7FFFFFFF) return false;
-  decode_split_kernel<D, G, QF32><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(args);
+  decode_split_kernel<D, G, QF32, C><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(
+      args);
   return true;
 }
 
-template <int D, bool QF32>
+template <int D, bool QF32, class C>
 bool dispatch_g(int G, const SplitArgs& a, int batch, hipStream_t s) {
   switch (G) {
-    case 1: return launch_split<D, 1, QF32>(a, batch, s);
-    case 2: return launch_split<D, 2, QF32>(a, batch, s);
-    case 4: return launch_split<D, 4, QF32>(a, batch, s);
-    case 8: return launch_split<D, 8, QF32>(a, batch, s);
+    case 1: return launch_split<D, 1, QF32, C>(a, batch, s);
+    case 2: return launch_split<D, 2, QF32, C>(a, batch, s);
+    case 4: return launch_split<D, 4, QF32, C>(a, batch, s);
+    case 8: return launch_split<D, 8, QF32, C>(a, batch, s);
     default: return false;
   }
+}
+
+template <class C>
+bool dispatch_fmt(int head_dim, bool q_f32, int G, const SplitArgs& a, int batch,
+                  hipStream_t s) {
+  if (head_dim == 128) return q_f32 ? dispatch_g<128, true, C>(G, a, batch, s)
+                                    : dispatch_g<128, false, C>(G, a, batch, s);
+  return q_f32 ? dispatch_g<64, true, C>(G, a, batch, s) : dispatch_g<64, false, C>(G, a, batch, s);
 }
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -461,7 +473,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, hipStream_t stream) {
+                  void* workspace, const DecodePlan& plan, bool fp8, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs a;
   a.q = q;
@@ -486,10 +498,8 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.qk_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   bool ok;
-  if (head_dim == 128) ok = q_f32 ? dispatch_g<128, true>(G, a, batch, stream)
-                                  : dispatch_g<128, false>(G, a, batch, stream);
-  else ok = q_f32 ? dispatch_g<64, true>(G, a, batch, stream)
-                  : dispatch_g<64, false>(G, a, batch, stream);
+  if (fp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
+  else ok = dispatch_fmt<CodesInt8>(head_dim, q_f32, G, a, batch, stream);
   if (!ok) return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -128,6 +128,64 @@ __device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// ---------------------------------------------------------------------------
+// Code formats of the quantised cache.  Each holds one code per byte, a
+// per-(token, KV head) fp16 scale and the quantiser's largest code value:
+//   CodesInt8  symmetric INT8, codes -127..127 (the KV8 method);
+//   CodesFp8   OCP e4m3 ("KV Cache 优化全景解析", section 7.4), largest 448.
+// pre() + lo()/hi() turn a dword of 4 codes into two fp16 pairs (bytes 0,1
+// and 2,3).  For INT8 the pairs carry the +1152 bias described above
+// (kBiased); exact() removes it.  e4m3 values are all exact in fp16, so the
+// FP8 pairs come from one hardware convert each and need no bias.
+// code() quantises one value: the fp32 quotient x / s (IEEE division), then
+// INT8: round half to even and clamp to +-127; FP8: round to nearest even
+// on the e4m3 grid and saturate to +-448, the sign of a zero kept.
+// ---------------------------------------------------------------------------
+struct CodesInt8 {
+  static constexpr bool kBiased = true;
+  static constexpr float kQmax = 127.0f;
+  __device__ static uint32_t pre(uint32_t u) { return u ^ kXor80; }
+  __device__ static half2_t lo(uint32_t x) { return biased_pair_lo(x); }
+  __device__ static half2_t hi(uint32_t x) { return biased_pair_hi(x); }
+  __device__ static half2_t exact(half2_t p) {
+    const half2_t bias = {(_Float16)kCodeBias, (_Float16)kCodeBias};
+    return p - bias;
+  }
+  __device__ static uint32_t code(float x, float s) {
+    float q = __builtin_rintf(x / s);                 // IEEE divide, ties to even
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (uint32_t)((int32_t)q) & 0xFFu;
+  }
+};
+
+struct CodesFp8 {
+  static constexpr bool kBiased = false;
+  static constexpr float kQmax = 448.0f;
+  __device__ static uint32_t pre(uint32_t u) { return u; }
+  __device__ static half2_t lo(uint32_t x) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  }
+  __device__ static half2_t hi(uint32_t x) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  }
+  __device__ static half2_t exact(half2_t p) { return p; }
+  __device__ static uint32_t code(float x, float s) {
+    const float q = x / s;                            // IEEE divide
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 24) & 0x80u;
+    const float a = fabsf(q);
+    uint32_t c;
+    if (a >= 448.0f) {
+      c = 0x7Eu;                                      // 448; beyond it saturates
+    } else if (a < 0.015625f) {                       // below 2^-6: steps of 2^-9
+      c = (uint32_t)__builtin_rintf(a * 512.0f);      // exact scaling, ties to even
+    } else {                                          // 3 mantissa bits, ties to even
+      const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+      c = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+    }
+    return sign | c;
+  }
+};
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }

@@ -1,6 +1,7 @@
 // Internal launchers of libkv8: called by the C ABI layer (kv8_api.cpp)
-// after host validation.  Each returns 0 on success and -1 when the HIP
-// runtime reports a launch error.
+// after host validation.  `fp8` selects the FP8 (e4m3) code format of the
+// cache instead of INT8; caches are passed as bytes either way.  Each
+// returns 0 on success and -1 when the HIP runtime reports a launch error.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,7 +13,7 @@ namespace kv8 {
 int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                         const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
                         int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
-                        uint16_t* k_scale, uint16_t* v_scale, hipStream_t stream);
+                        uint16_t* k_scale, uint16_t* v_scale, bool fp8, hipStream_t stream);
 
 struct DecodePlan {
   int split_tokens;      // tokens per workgroup (multiple of 64)
@@ -32,7 +33,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, hipStream_t stream);
+                  void* workspace, const DecodePlan& plan, bool fp8, hipStream_t stream);
 
 int launch_decode_bf16kv(const void* q, bool q_f32, const uint16_t* k_cache,
                          const uint16_t* v_cache, int64_t num_blocks,
@@ -46,6 +47,6 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,
                    int max_blocks_per_seq, const int32_t* context_lens, int ctx_cap, int batch,
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
-                   hipStream_t stream);
+                   bool fp8, hipStream_t stream);
 
 }  // namespace kv8

@@ -26,9 +26,11 @@
 //      feeds to the PV product are 16 contiguous bytes;
 //   scales as fp32, k_scale premultiplied by sm_scale * log2(e); keys past
 //      the workgroup's key range get scale 0.
-// Codes become fp16 without a convert per code: u = c xor 0x80 under the
-// fp16 high byte 0x64 is the value c + 1152, and one packed fp16 subtract
-// of 1152 leaves c exactly.
+// INT8 codes become fp16 without a convert per code: u = c xor 0x80 under
+// the fp16 high byte 0x64 is the value c + 1152, and one packed fp16
+// subtract of 1152 leaves c exactly.  The same kernel serves the FP8 (e4m3)
+// cache ("KV Cache 优化全景解析", section 7.4): its codes become exact fp16
+// pairs by one hardware convert.
 //
 // Per wave and key tile (v_mfma_f32_32x32x16_f16, fp32 accumulate):
 //   S^T[key][query] = K_code . Q^T, with Q scaled by one power of two 2^e
@@ -116,12 +118,12 @@ __device__ __forceinline__ int vt_swizzle(int row) {
 
 __device__ __forceinline__ half8_t as_half8(uint4 u) { return __builtin_bit_cast(half8_t, u); }
 
-// Four int8 codes (one dword) -> two exact fp16 pairs.
+// Four codes (one dword) -> two exact fp16 pairs.
+template <class C>
 __device__ __forceinline__ void codes_to_f16(uint32_t u, half2_t& lo, half2_t& hi) {
-  const uint32_t x = u ^ kXor80;
-  const half2_t bias = {(_Float16)kCodeBias, (_Float16)kCodeBias};
-  lo = biased_pair_lo(x) - bias;
-  hi = biased_pair_hi(x) - bias;
+  const uint32_t x = C::pre(u);
+  lo = C::exact(C::lo(x));
+  hi = C::exact(C::hi(x));
 }
 
 __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -194,7 +196,7 @@ __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* 
   }
 }
 
-template <int D>
+template <int D, class C>
 __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_keys, int tid,
                                             float k_mult, const Stage<D>& st) {
   {
@@ -203,7 +205,7 @@ __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_
 #pragma unroll
     for (int j = 0; j < Stage<D>::kKBytes / 4; ++j) {
       half2_t lo, hi;
-      codes_to_f16(st.k[j], lo, hi);
+      codes_to_f16<C>(st.k[j], lo, hi);
       o[2 * j] = h2_bits(lo);
       o[2 * j + 1] = h2_bits(hi);
     }
@@ -217,16 +219,15 @@ __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_
     const int grp = kq >> 2, sub = kq & 3;
     const int a4 = sub >> 1, hh = sub & 1;
     // 4 rows x 4 channel bytes -> per channel the 4 rows' codes
-    const uint32_t t01l = interleave_lo(st.v[0], st.v[1]) ^ kXor80;   // [r0c0 r1c0 r0c1 r1c1]
-    const uint32_t t01h = interleave_hi(st.v[0], st.v[1]) ^ kXor80;   // [r0c2 r1c2 r0c3 r1c3]
-    const uint32_t t23l = interleave_lo(st.v[2], st.v[3]) ^ kXor80;
-    const uint32_t t23h = interleave_hi(st.v[2], st.v[3]) ^ kXor80;
-    const half2_t bias = {(_Float16)kCodeBias, (_Float16)kCodeBias};
+    const uint32_t t01l = C::pre(interleave_lo(st.v[0], st.v[1]));   // [r0c0 r1c0 r0c1 r1c1]
+    const uint32_t t01h = C::pre(interleave_hi(st.v[0], st.v[1]));   // [r0c2 r1c2 r0c3 r1c3]
+    const uint32_t t23l = C::pre(interleave_lo(st.v[2], st.v[3]));
+    const uint32_t t23h = C::pre(interleave_hi(st.v[2], st.v[3]));
 #pragma unroll
     for (int ci = 0; ci < 4; ++ci) {
       const uint32_t x01 = ci < 2 ? t01l : t01h, x23 = ci < 2 ? t23l : t23h;
-      const half2_t p01 = ((ci & 1) ? biased_pair_hi(x01) : biased_pair_lo(x01)) - bias;
-      const half2_t p23 = ((ci & 1) ? biased_pair_hi(x23) : biased_pair_lo(x23)) - bias;
+      const half2_t p01 = C::exact((ci & 1) ? C::hi(x01) : C::lo(x01));
+      const half2_t p23 = C::exact((ci & 1) ? C::hi(x23) : C::lo(x23));
       const int row = cq * 4 + ci;
       *reinterpret_cast<uint2*>(
           &lds.v[buf][row][8 * ((grp * 2 + hh) ^ vt_swizzle(row)) + 4 * a4]) =
@@ -346,7 +347,7 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&sc)[2], const float* ks,
   lrun += lsum;
 }
 
-template <int D, int G>
+template <int D, int G, class C>
 __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   constexpr int KS = D / 16;        // k-steps of the QK^T product
   constexpr int CB = D / 32;        // 32-channel blocks of the output
@@ -483,7 +484,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       }
     }
   }
-  if (nkt > 0) stage_store<D>(lds, 0, 0, n_keys, tid, k_mult, st);
+  if (nkt > 0) stage_store<D, C>(lds, 0, 0, n_keys, tid, k_mult, st);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -545,7 +546,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (more) stage_store<D>(lds, buf ^ 1, kt + 1, n_keys, tid, k_mult, st);
+    if (more) stage_store<D, C>(lds, buf ^ 1, kt + 1, n_keys, tid, k_mult, st);
     __syncthreads();
   }
 
@@ -566,25 +567,25 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, class C>
 int launch_dg(PrefillArgs a, int batch, int max_q_len, hipStream_t stream) {
   const int64_t tiles = ((int64_t)max_q_len * G + kQueriesPerGroup - 1) / kQueriesPerGroup;
   const int64_t pairs8 = ((int64_t)batch * a.num_kv_heads + 7) / 8 * 8;
   if (tiles * pairs8 > 0x7FFFFFFF) return -2;
   a.tiles_per_pair = (int)tiles;
   a.batch = batch;
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)(tiles * pairs8)), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, C>), dim3((unsigned)(tiles * pairs8)), dim3(kThreads),
+                     0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int D>
+template <int D, class C>
 int launch_d(const PrefillArgs& a, int G, int batch, int max_q_len, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_dg<D, 1>(a, batch, max_q_len, stream);
-    case 2: return launch_dg<D, 2>(a, batch, max_q_len, stream);
-    case 4: return launch_dg<D, 4>(a, batch, max_q_len, stream);
-    case 8: return launch_dg<D, 8>(a, batch, max_q_len, stream);
+    case 1: return launch_dg<D, 1, C>(a, batch, max_q_len, stream);
+    case 2: return launch_dg<D, 2, C>(a, batch, max_q_len, stream);
+    case 4: return launch_dg<D, 4, C>(a, batch, max_q_len, stream);
+    case 8: return launch_dg<D, 8, C>(a, batch, max_q_len, stream);
     default: return -2;
   }
 }
@@ -596,7 +597,7 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,
                    int max_blocks_per_seq, const int32_t* context_lens, int ctx_cap, int batch,
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
-                   hipStream_t stream) {
+                   bool fp8, hipStream_t stream) {
   PrefillArgs a;
   a.q = q;
   a.q_start_loc = q_start_loc;
@@ -615,8 +616,10 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
   a.num_kv_heads = num_kv_heads;
   a.sm_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
-  if (head_dim == 128) return launch_d<128>(a, G, batch, max_q_len, stream);
-  if (head_dim == 64) return launch_d<64>(a, G, batch, max_q_len, stream);
+  if (head_dim == 128) return fp8 ? launch_d<128, CodesFp8>(a, G, batch, max_q_len, stream)
+                                  : launch_d<128, CodesInt8>(a, G, batch, max_q_len, stream);
+  if (head_dim == 64) return fp8 ? launch_d<64, CodesFp8>(a, G, batch, max_q_len, stream)
+                                 : launch_d<64, CodesInt8>(a, G, batch, max_q_len, stream);
   return -2;
 }
 

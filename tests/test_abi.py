@@ -40,11 +40,11 @@ def test_status_strings_and_version():
     assert B.load().kv8_version() >= 100
 
 
-def append(**kw):
+def append(fn="kv8_quant_append", **kw):
     a = dict(k_new=P, v_new=P, slots=P, n=4, hkv=8, d=128, bs=16, nb=10,
              kc=P, vc=P, ks=P, vs=P, stream=None)
     a.update(kw)
-    return B.load().kv8_quant_append(a["k_new"], a["v_new"], a["slots"], a["n"], a["hkv"],
+    return getattr(B.load(), fn)(a["k_new"], a["v_new"], a["slots"], a["n"], a["hkv"],
                                      a["d"], a["bs"], a["nb"], a["kc"], a["vc"], a["ks"],
                                      a["vs"], a["stream"])
 
@@ -67,12 +67,12 @@ def test_append_validation(kw, expected):
     assert append(**kw) == expected
 
 
-def decode(**kw):
+def decode(fn="paged_decode_attn_kv8", **kw):
     a = dict(q=P, dt=B.KV8_BF16, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
              maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=P2,
              wsb=1 << 30, tps=0, stream=None)
     a.update(kw)
-    return B.load().paged_decode_attn_kv8(
+    return getattr(B.load(), fn)(
         a["q"], a["dt"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"], a["bt"], a["mbs"],
         a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"],
         a["out"], a["ws"], a["wsb"], a["tps"], a["stream"])
@@ -157,12 +157,12 @@ def test_decode_workspace_size():
         B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 1024)
 
 
-def prefill(**kw):
+def prefill(fn="paged_prefill_chunk_attn_kv8", **kw):
     a = dict(q=P, qsl=P, tq=64, mq=32, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
              maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=None,
              wsb=0, stream=None)
     a.update(kw)
-    return B.load().paged_prefill_chunk_attn_kv8(
+    return getattr(B.load(), fn)(
         a["q"], a["qsl"], a["tq"], a["mq"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"],
         a["bt"], a["mbs"], a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"],
         a["scale"], a["out"], a["ws"], a["wsb"], a["stream"])
@@ -185,3 +185,27 @@ def prefill(**kw):
 ])
 def test_prefill_validation(kw, expected):
     assert prefill(**kw) == expected
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k_new=None), dict(kc=None), dict(vs=None), dict(n=-1), dict(nb=0), dict(d=96),
+    dict(bs=32), dict(kc=MIS), dict(n=0),
+])
+def test_fp8_append_validation_matches_int8(kw):
+    assert append(fn="kv8_quant_append_fp8", **kw) == append(**kw)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(ks=None), dict(b=0), dict(hq=30), dict(hq=24), dict(d=256), dict(dt=7),
+    dict(tps=100), dict(kc=MIS), dict(ws=None), dict(wsb=16),
+])
+def test_fp8_decode_validation_matches_int8(kw):
+    assert decode(fn="paged_decode_attn_fp8kv", **kw) == decode(**kw)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qsl=None), dict(vc=None), dict(b=0), dict(tq=-1), dict(hq=31), dict(d=96),
+    dict(q=MIS), dict(tq=0),
+])
+def test_fp8_prefill_validation_matches_int8(kw):
+    assert prefill(fn="paged_prefill_chunk_attn_fp8kv", **kw) == prefill(**kw)
