@@ -434,3 +434,39 @@ def paged_prefill_chunk_fp8(q, q_start_loc, k_cache, v_cache, k_scale, v_scale,
             v = gather_dequant_fp8(v_cache, v_scale, block_table[b], ctx, g, block_size)
             out[r0:r1, h] = softmax_attention(q[r0:r1, h], k, v, sm_scale, visible)
     return out
+
+
+# --------------------------------------------------------------------------
+# RoPE fused into the append.  "KV-Cache 全栈优化系统" README, section
+# 系统架构概览: on the cache-operator plane K is written to the cache after
+# RoPE, then quantised.  The pages give no RoPE formula; the reading taken is
+# the standard rotary embedding in the rotate-half (Llama) convention over
+# the whole head: for j < d/2, with (c, s) = table[pos, j], table[pos, d/2+j],
+#   x'_j       = x_j * c - x_{j+d/2} * s
+#   x'_{j+d/2} = x_{j+d/2} * c + x_j * s
+# in fp32, each product and the sum rounded to fp32 (no fused multiply-add),
+# so the quantiser sees fp32 values.  The cos/sin table [max_pos, d] is an
+# input, as in serving engines.  V is not rotated.
+# --------------------------------------------------------------------------
+def rope_rotate_half(x, positions, cos_sin):
+    """x [N, H, d] (fp32 values), positions [N] int, cos_sin [P, d] fp32.
+    Returns the rotated rows as fp32."""
+    x = np.asarray(x, np.float32)
+    d = x.shape[-1]
+    half = d // 2
+    tab = np.asarray(cos_sin, np.float32)[np.asarray(positions)]     # [N, d]
+    c = tab[:, None, :half]
+    s = tab[:, None, half:]
+    lo, hi = x[..., :half], x[..., half:]
+    out = np.empty_like(x)
+    out[..., :half] = (lo * c) - (hi * s)          # numpy float32: each op rounded
+    out[..., half:] = (hi * c) + (lo * s)
+    return out
+
+
+def rope_quant_append(k_pre, v_new, positions, cos_sin, slot_mapping, k_cache, v_cache,
+                      k_scale, v_scale, block_size=BLOCK_SIZE):
+    """Rotate K (pre-RoPE bf16 values) at its positions, then quant_append
+    the rotated K and the unrotated V."""
+    k_rot = rope_rotate_half(k_pre, positions, cos_sin)
+    quant_append(k_rot, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size)

@@ -40,6 +40,9 @@ def _battery():
         ("fp8_quantiser", P.test_fp8_quantiser_invariants),
         ("fp8_decode", P.test_fp8_decode_brute_force_and_sdpa),
         ("fp8_prefill", P.test_fp8_prefill_equals_sdpa_causal),
+        ("rope_library", P.test_rope_matches_transformers_and_fp64),
+        ("rope_props", P.test_rope_identity_at_zero_and_relative_position),
+        ("rope_append", P.test_rope_quant_append_is_rotate_then_quantise),
     ]
     for name, fn in checks:
         try:
@@ -173,6 +176,36 @@ def _row_scale_fp8_127(x):
     return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
 
 
+def _rope_sign(x, positions, cos_sin):
+    x = np.asarray(x, np.float32)
+    half = x.shape[-1] // 2
+    tab = np.asarray(cos_sin, np.float32)[np.asarray(positions)]
+    c, s_ = tab[:, None, :half], tab[:, None, half:]
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c + hi * s_, hi * c - lo * s_], axis=-1)
+
+
+def _rope_cos_sin_swapped(x, positions, cos_sin):
+    x = np.asarray(x, np.float32)
+    half = x.shape[-1] // 2
+    tab = np.asarray(cos_sin, np.float32)[np.asarray(positions)]
+    s_, c = tab[:, None, :half], tab[:, None, half:]
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s_, hi * c + lo * s_], axis=-1)
+
+
+def _rope_interleaved(x, positions, cos_sin):
+    x = np.asarray(x, np.float32)
+    half = x.shape[-1] // 2
+    tab = np.asarray(cos_sin, np.float32)[np.asarray(positions)]
+    c, s_ = tab[:, None, :half], tab[:, None, half:]
+    ev, od = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = ev * c - od * s_
+    out[..., 1::2] = od * c + ev * s_
+    return out
+
+
 MUTANTS = {
     "head_map_mod": ("kv_head_of", lambda h, group: h % group),
     "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
@@ -198,6 +231,9 @@ MUTANTS = {
     "fp8_encode_truncates": ("e4m3_encode", _e4m3_truncate),
     "fp8_value_bias8": ("e4m3_value", _e4m3_value_bias8),
     "fp8_scale_127": ("row_scale_fp8", _row_scale_fp8_127),
+    "rope_sign": ("rope_rotate_half", _rope_sign),
+    "rope_cos_sin_swapped": ("rope_rotate_half", _rope_cos_sin_swapped),
+    "rope_interleaved": ("rope_rotate_half", _rope_interleaved),
 }
 
 

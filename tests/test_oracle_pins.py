@@ -634,3 +634,72 @@ def test_fp8_prefill_equals_sdpa_causal():
         ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt, attn_mask=mask)
         assert np.allclose(out[qsl[b]:qsl[b + 1]], ref[0].permute(1, 0, 2).numpy(),
                            rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# RoPE fused into the append (README section 系统架构概览; rotate-half
+# reading).  transformers' apply_rotary_pos_emb is an independent
+# implementation of the same convention.
+# ---------------------------------------------------------------------------
+def rope_table(max_pos, d, base=500000.0):
+    inv = 1.0 / base ** (np.arange(0, d, 2, dtype=np.float64) / d)
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def test_rope_matches_transformers_and_fp64():
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    rng = np.random.default_rng(41)
+    n, h, d = 300, 4, 128
+    tab = rope_table(70000, d)
+    pos = rng.integers(0, 70000, n)
+    x = W.bf16_bits_to_f32(W.to_bf16(rng.standard_normal((n, h, d)).astype(np.float32) * 3)[1])
+    got = O.rope_rotate_half(x, pos, tab)
+    c = torch.from_numpy(np.concatenate([tab[pos, :d // 2]] * 2, axis=1))      # [n, d]
+    s = torch.from_numpy(np.concatenate([tab[pos, d // 2:]] * 2, axis=1))
+    xt = torch.from_numpy(x)
+    ref, _ = apply_rotary_pos_emb(xt, xt, c, s, unsqueeze_dim=1)
+    ulp = np.spacing(np.abs(ref.numpy()).astype(np.float32))
+    assert np.all(np.abs(got - ref.numpy()) <= ulp)        # same rounded ops, at most 1 ulp
+    # against the exact rotation with the same table (fp64): within 2 fp32 ulps
+    t64 = tab[pos].astype(np.float64)
+    c64, s64 = t64[:, None, :d // 2], t64[:, None, d // 2:]
+    lo, hi = x[..., :d // 2].astype(np.float64), x[..., d // 2:].astype(np.float64)
+    exact = np.concatenate([lo * c64 - hi * s64, hi * c64 + lo * s64], axis=-1)
+    # each fp32 product rounds by half an ulp of itself, the sum by half an ulp of the result
+    sp = lambda v: np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)
+    pa = np.concatenate([lo * c64, hi * c64], axis=-1)
+    pb = np.concatenate([hi * s64, lo * s64], axis=-1)
+    bound = 0.5 * (sp(pa) + sp(pb) + sp(exact)) * (1 + 1e-9)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_rope_identity_at_zero_and_relative_position():
+    rng = np.random.default_rng(42)
+    d = 64
+    tab = rope_table(5000, d, base=10000.0)
+    x = rng.standard_normal((1, 1, d)).astype(np.float32)
+    assert np.array_equal(O.rope_rotate_half(x, [0], tab), x)        # cos 1, sin 0
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, d)).astype(np.float32)
+    dots = []
+    for m, n_ in ((100, 40), (1060, 1000), (60, 0)):
+        dots.append(float(np.dot(O.rope_rotate_half(q, [m], tab).ravel().astype(np.float64),
+                                 O.rope_rotate_half(k, [n_], tab).ravel().astype(np.float64))))
+    assert np.allclose(dots, dots[0], rtol=1e-4, atol=1e-4)          # depends on m - n only
+    norms = np.linalg.norm(O.rope_rotate_half(x, [1234], tab)), np.linalg.norm(x)
+    assert abs(norms[0] - norms[1]) < 1e-5 * norms[1]                 # a rotation
+
+
+def test_rope_quant_append_is_rotate_then_quantise():
+    case = W.make_paged_case(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                             context_lens=[20, 33], seed=43)
+    tab = rope_table(4096, 64)
+    pos = case.token_pos + 7
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, 2, 64)
+    O.rope_quant_append(case.k, case.v, pos, tab, case.slot_mapping, kc, vc, ks, vs)
+    kq, ksc = O.quantize_rows(O.rope_rotate_half(case.k, pos, tab))
+    vq, vsc = O.quantize_rows(case.v)
+    blk, off = case.slot_mapping // 16, case.slot_mapping % 16
+    assert np.array_equal(kc[blk, :, off], kq) and np.array_equal(vc[blk, :, off], vq)
+    assert np.array_equal(ks[blk, :, off], ksc) and np.array_equal(vs[blk, :, off], vsc)
