@@ -187,6 +187,29 @@ def main():
     torch.cuda.synchronize()
     dec_b2b_us = b0.elapsed_time(b1) / n_b2b * 1e3
 
+    # the append alone, back to back: plain, and with RoPE fused in front of
+    # the quantiser (positions of the newest tokens, Llama-3 table)
+    table = torch.from_numpy(W.rope_cos_sin(8192, d)).to(dev)
+    pos_new = torch.from_numpy((ctx - 1).astype(np.int32)).to(dev)
+
+    def b2b(fn, n=50):
+        for _ in range(5):
+            fn(0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    app_plain_us = b2b(lambda i: B.kv8_quant_append(k_new, v_new, slots_new,
+                                                    *caches[i % len(caches)]))
+    app_rope_us = b2b(lambda i: B.kv8_rope_quant_append(k_new, v_new, slots_new, pos_new, table,
+                                                        *caches[i % len(caches)]))
+
     step_ms = total_ms / args.steps
     d_bytes = decode_bytes(ctx, hkv, d, hq, 2)
     a_bytes = append_bytes(bsz, hkv, d)
@@ -225,6 +248,8 @@ def main():
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "decode_back_to_back_us": round(dec_b2b_us, 2),
         "append_us": {"mean": round(float(app_ms.mean()) * 1e3, 2)},
+        "append_back_to_back_us": {"plain": round(app_plain_us, 2),
+                                   "rope_fused": round(app_rope_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode"),

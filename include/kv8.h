@@ -117,6 +117,35 @@ int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                      void* stream);
 
 /*
+ * kv8_rope_quant_append - kv8_quant_append with the rotary position
+ * embedding of K fused in front of the quantiser: K goes into the cache
+ * after RoPE, then quantised, as on the cache-operator plane of the
+ * "KV-Cache 全栈优化系统" README (section 系统架构概览).  Rotate-half
+ * convention over the whole head: for j < d/2, with c = cos_sin[pos][j] and
+ * s = cos_sin[pos][d/2 + j],
+ *   k'_j = k_j c - k_{j+d/2} s,   k'_{j+d/2} = k_{j+d/2} c + k_j s,
+ * each product and sum rounded to fp32; the rotated fp32 row is quantised
+ * exactly as kv8_quant_append quantises a row.  V is appended unrotated.
+ *
+ *   k_new         device bf16 [n_tokens, Hkv, d], K before RoPE
+ *   positions     device int32 [n_tokens], the token positions; values
+ *                 outside [0, max_position) are clamped into it
+ *   cos_sin       device fp32 [max_position, d], 16-byte aligned: row p
+ *                 holds cos(p * theta_j) for j < d/2, then sin(p * theta_j)
+ *   all other arguments as for kv8_quant_append
+ * Returns KV8_OK, KV8_ERR_NULL, KV8_ERR_SHAPE (max_position <= 0 with
+ * tokens to append), KV8_ERR_UNSUPPORTED, KV8_ERR_ALIGN or KV8_ERR_HIP.
+ */
+int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* slot_mapping, const int32_t* positions,
+                          const float* cos_sin, int max_position, int64_t n_tokens,
+                          int num_kv_heads, int head_dim, int block_size,
+                          int64_t num_blocks,
+                          int8_t* k_cache, int8_t* v_cache,
+                          uint16_t* k_scale, uint16_t* v_scale,
+                          void* stream);
+
+/*
  * kv8_decode_workspace_size - bytes of workspace paged_decode_attn_kv8
  * needs for these sizes.  tokens_per_split: most tokens one workgroup covers
  * (a multiple of 64 in [64, 2048]), or <= 0 for the library's choice,

@@ -27,7 +27,7 @@ EXPORTED = (
     "kv8_status_string", "kv8_version", "kv8_quant_append", "kv8_decode_workspace_size",
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
-    "paged_prefill_chunk_attn_fp8kv",
+    "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append",
 )
 
 _lib = None
@@ -60,6 +60,9 @@ def load():
     lib.kv8_version.argtypes = []
     lib.kv8_quant_append.restype = i32
     lib.kv8_quant_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+    lib.kv8_rope_quant_append.restype = i32
+    lib.kv8_rope_quant_append.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i64,
+                                          vp, vp, vp, vp, vp]
     lib.kv8_quant_append_fp8.restype = i32
     lib.kv8_quant_append_fp8.argtypes = lib.kv8_quant_append.argtypes
     lib.kv8_decode_workspace_size.restype = sz
@@ -128,6 +131,18 @@ def kv8_quant_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, 
     """As kv8_quant_append, into an FP8 (e4m3) cache (uint8 codes)."""
     _append("kv8_quant_append_fp8", k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
             v_scale, stream)
+
+
+def kv8_rope_quant_append(k_new, v_new, slot_mapping, positions, cos_sin, k_cache, v_cache,
+                          k_scale, v_scale, stream=None):
+    """k_new (before RoPE) / v_new: bf16 [N, Hkv, d]; slot_mapping and
+    positions int32 [N]; cos_sin fp32 [max_position, d]."""
+    n, hkv, d = k_new.shape
+    st = load().kv8_rope_quant_append(
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], n, hkv, d, BLOCK_SIZE, k_cache.shape[0], _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream))
+    _check(st, "kv8_rope_quant_append")
 
 
 def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,

@@ -159,6 +159,28 @@ int kv8_quant_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
                      reinterpret_cast<int8_t*>(v_cache), k_scale, v_scale, true, stream);
 }
 
+int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* slot_mapping, const int32_t* positions,
+                          const float* cos_sin, int max_position, int64_t n_tokens,
+                          int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                          int8_t* k_cache, int8_t* v_cache, uint16_t* k_scale,
+                          uint16_t* v_scale, void* stream) {
+  if (n_tokens < 0 || num_kv_heads <= 0) return KV8_ERR_SHAPE;
+  if (!supported_dim(head_dim)) return KV8_ERR_UNSUPPORTED;
+  const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
+  if (rc != KV8_OK) return rc;
+  if (n_tokens == 0) return KV8_OK;
+  if (!k_new || !v_new || !slot_mapping || !positions || !cos_sin) return KV8_ERR_NULL;
+  if (max_position <= 0) return KV8_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_sin)) return KV8_ERR_ALIGN;
+  if (n_tokens * num_kv_heads * (head_dim / 8) / 256 >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;
+  const int r = kv8::launch_rope_quant_append(k_new, v_new, slot_mapping, positions, cos_sin,
+                                              max_position, n_tokens, num_kv_heads, head_dim,
+                                              num_blocks, k_cache, v_cache, k_scale, v_scale,
+                                              static_cast<hipStream_t>(stream));
+  return r == 0 ? KV8_OK : KV8_ERR_HIP;
+}
+
 size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int tokens_per_split) {
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;

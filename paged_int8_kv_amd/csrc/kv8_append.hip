@@ -60,12 +60,44 @@ __device__ __forceinline__ void unpack8(uint4 raw, float (&x)[8], float& amax) {
   }
 }
 
-template <int D, class C>
+// Rotary embedding of K (rotate-half convention over the whole head): for
+// j < d/2 with (c, s) = cos_sin[pos][j], cos_sin[pos][d/2 + j],
+//   x'_j = x_j c - x_{j+d/2} s,   x'_{j+d/2} = x_{j+d/2} c + x_j s,
+// each product and the sum rounded to fp32 (contraction off), so the
+// quantiser sees the same fp32 values as any plain implementation.  The
+// lane holding channels j and the lane holding j + d/2 are LPR/2 apart in
+// the row, so one lane exchange per value brings the partner over.
+template <int LPR>
+__device__ __forceinline__ void rope8(float (&x)[8], int part, const float* __restrict__ cs,
+                                      int half) {
+#pragma clang fp contract(off)
+  const bool upper = part >= LPR / 2;
+  const int j0 = (part % (LPR / 2)) * 8;            // first channel index within the half
+  const float4 c0 = *reinterpret_cast<const float4*>(cs + j0);
+  const float4 c1 = *reinterpret_cast<const float4*>(cs + j0 + 4);
+  const float4 s0 = *reinterpret_cast<const float4*>(cs + half + j0);
+  const float4 s1 = *reinterpret_cast<const float4*>(cs + half + j0 + 4);
+  const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __shfl_xor(x[i], LPR / 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = x[i] * c[i];
+    const float b = p[i] * sn[i];
+    x[i] = upper ? a + b : a - b;
+  }
+}
+
+template <int D, class C, bool ROPE>
 __global__ __launch_bounds__(256) void quant_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ slot_mapping, int64_t n_rows, int num_kv_heads,
     int64_t num_slots, int8_t* __restrict__ k_cache, int8_t* __restrict__ v_cache,
-    uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale) {
+    uint16_t* __restrict__ k_scale, uint16_t* __restrict__ v_scale,
+    const int32_t* __restrict__ positions, const float* __restrict__ cos_sin,
+    int max_position) {
   constexpr int LPR = D / 8;
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gtid / LPR;          // (token, head) row
@@ -81,6 +113,14 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
   float kx[8], vx[8], ka, va;
   unpack8(kraw, kx, ka);
   unpack8(vraw, vx, va);
+  if constexpr (ROPE) {
+    int pos = positions[n];
+    pos = pos < 0 ? 0 : (pos >= max_position ? max_position - 1 : pos);
+    rope8<LPR>(kx, part, cos_sin + (int64_t)pos * D, D / 2);
+    ka = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ka = fmaxf(ka, fabsf(kx[i]));
+  }
   // Every lane of the row takes part in the reductions (rows never straddle
   // an exit), so the DPP partners are always active.
   ka = row_absmax<LPR>(ka);
@@ -106,21 +146,22 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
 }  // namespace
 
 namespace {
-template <class C>
+template <class C, bool ROPE>
 void launch_append_fmt(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
                        int64_t n_rows, int num_kv_heads, int head_dim, int64_t num_slots,
                        int8_t* k_cache, int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
+                       const int32_t* positions, const float* cos_sin, int max_position,
                        hipStream_t stream) {
   const int64_t threads = n_rows * (head_dim / 8);
   const int64_t grid = (threads + 255) / 256;
   if (head_dim == 128) {
-    quant_append_kernel<128, C><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+    quant_append_kernel<128, C, ROPE><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
         k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
-        k_scale, v_scale);
+        k_scale, v_scale, positions, cos_sin, max_position);
   } else {
-    quant_append_kernel<64, C><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+    quant_append_kernel<64, C, ROPE><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
         k_new, v_new, slot_mapping, n_rows, num_kv_heads, num_slots, k_cache, v_cache,
-        k_scale, v_scale);
+        k_scale, v_scale, positions, cos_sin, max_position);
   }
 }
 }  // namespace
@@ -132,11 +173,26 @@ int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
   const int64_t n_rows = n_tokens * num_kv_heads;
   const int64_t num_slots = num_blocks * kBlock;
   if (fp8)
-    launch_append_fmt<CodesFp8>(k_new, v_new, slot_mapping, n_rows, num_kv_heads, head_dim,
-                                num_slots, k_cache, v_cache, k_scale, v_scale, stream);
+    launch_append_fmt<CodesFp8, false>(k_new, v_new, slot_mapping, n_rows, num_kv_heads,
+                                       head_dim, num_slots, k_cache, v_cache, k_scale, v_scale,
+                                       nullptr, nullptr, 0, stream);
   else
-    launch_append_fmt<CodesInt8>(k_new, v_new, slot_mapping, n_rows, num_kv_heads, head_dim,
-                                 num_slots, k_cache, v_cache, k_scale, v_scale, stream);
+    launch_append_fmt<CodesInt8, false>(k_new, v_new, slot_mapping, n_rows, num_kv_heads,
+                                        head_dim, num_slots, k_cache, v_cache, k_scale, v_scale,
+                                        nullptr, nullptr, 0, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* slot_mapping, const int32_t* positions,
+                             const float* cos_sin, int max_position, int64_t n_tokens,
+                             int num_kv_heads, int head_dim, int64_t num_blocks, int8_t* k_cache,
+                             int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
+                             hipStream_t stream) {
+  launch_append_fmt<CodesInt8, true>(k_new, v_new, slot_mapping, n_tokens * num_kv_heads,
+                                     num_kv_heads, head_dim, num_blocks * kBlock, k_cache,
+                                     v_cache, k_scale, v_scale, positions, cos_sin, max_position,
+                                     stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

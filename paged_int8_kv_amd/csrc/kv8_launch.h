@@ -15,6 +15,13 @@ int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                         int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
                         uint16_t* k_scale, uint16_t* v_scale, bool fp8, hipStream_t stream);
 
+int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* slot_mapping, const int32_t* positions,
+                             const float* cos_sin, int max_position, int64_t n_tokens,
+                             int num_kv_heads, int head_dim, int64_t num_blocks, int8_t* k_cache,
+                             int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
+                             hipStream_t stream);
+
 struct DecodePlan {
   int split_tokens;      // tokens per workgroup (multiple of 64)
   int n_split;           // workgroups per (sequence, KV head)

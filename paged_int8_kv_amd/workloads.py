@@ -346,3 +346,13 @@ def long_context_258k(batch, device, ctx=258 * 1024, seed=7, num_q_heads=32, num
 
     return dict(context_lens=lens, block_table=table, num_blocks=nb, outlier_channels=outl,
                 q=q, tokens=tokens, slots=slots)
+
+
+def rope_cos_sin(max_position, head_dim, base=500000.0):
+    """The rotary-embedding table a serving engine keeps: fp32 [max_position,
+    head_dim], row p = cos(p * theta_j) for j < d/2, then sin(p * theta_j),
+    theta_j = base^(-2j/d) (Llama-3's base 500000), computed in fp64 and
+    rounded to fp32."""
+    inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)

@@ -209,3 +209,29 @@ def test_fp8_decode_validation_matches_int8(kw):
 ])
 def test_fp8_prefill_validation_matches_int8(kw):
     assert prefill(fn="paged_prefill_chunk_attn_fp8kv", **kw) == prefill(**kw)
+
+
+def rope_append(**kw):
+    a = dict(k_new=P, v_new=P, slots=P, pos=P, cs=P, maxpos=4096, n=4, hkv=8, d=128, bs=16,
+             nb=10, kc=P, vc=P, ks=P, vs=P, stream=None)
+    a.update(kw)
+    return B.load().kv8_rope_quant_append(
+        a["k_new"], a["v_new"], a["slots"], a["pos"], a["cs"], a["maxpos"], a["n"], a["hkv"],
+        a["d"], a["bs"], a["nb"], a["kc"], a["vc"], a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(pos=None), B.KV8_ERR_NULL),
+    (dict(cs=None), B.KV8_ERR_NULL),
+    (dict(k_new=None), B.KV8_ERR_NULL),
+    (dict(kc=None), B.KV8_ERR_NULL),
+    (dict(maxpos=0), B.KV8_ERR_SHAPE),
+    (dict(n=-1), B.KV8_ERR_SHAPE),
+    (dict(d=96), B.KV8_ERR_UNSUPPORTED),
+    (dict(bs=32), B.KV8_ERR_UNSUPPORTED),
+    (dict(cs=MIS), B.KV8_ERR_ALIGN),
+    (dict(k_new=MIS), B.KV8_ERR_ALIGN),
+    (dict(n=0, pos=None, cs=None), B.KV8_OK),
+])
+def test_rope_append_validation(kw, expected):
+    assert rope_append(**kw) == expected
