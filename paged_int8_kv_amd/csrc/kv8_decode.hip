@@ -253,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 #pragma unroll
     for (int s = 0; s < kPf; ++s) issue(s, min(s, last));
     for (int base = 0; base < nmine; base += kPf) {
+      priority_by_remaining(2 * nmine - base);
 #pragma unroll
       for (int s = 0; s < kPf; ++s) {
         __builtin_amdgcn_sched_barrier(0);
@@ -363,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 #pragma unroll
   for (int k = 0; k < M; ++k) acc[k] = 0.0f;
   for (int base = 0; base < nmine; base += kPf) {
+    priority_by_remaining(nmine - base);
 #pragma unroll
     for (int s = 0; s < kPf; ++s) {
       __builtin_amdgcn_sched_barrier(0);

@@ -81,6 +81,20 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // Wait until every vector memory access of this wave has completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Issue priority of a wave from the blocks (K and V passes together) it
+// still has to stream: more work left, higher priority.  Without it the
+// hardware issues the oldest wave of a CU first, so a CU's first workgroup
+// races ahead and its last one ends the launch streaming alone at a
+// fraction of the CU's share of bandwidth; largest-remaining-first makes the
+// workgroups that share a CU finish closer together.  s_setprio takes an
+// immediate, hence the branches (uniform over the wave).
+__device__ __forceinline__ void priority_by_remaining(int remaining_blocks) {
+  if (remaining_blocks > 24) __builtin_amdgcn_s_setprio(3);
+  else if (remaining_blocks > 16) __builtin_amdgcn_s_setprio(2);
+  else if (remaining_blocks > 8) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 struct Item {
   int b;        // sequence, -1 past the last item
   int g;        // KV head
