@@ -202,6 +202,38 @@ int paged_decode_attn_kv8(const void* q, int q_dtype,
                           int tokens_per_split, void* stream);
 
 /*
+ * paged_decode_attn_kv8_append - one decode step in one launch: append the
+ * newest token of every sequence, then paged_decode_attn_kv8.  The result
+ * (cache contents and output) is that of kv8_quant_append on the new
+ * tokens followed by paged_decode_attn_kv8 ("KV-Cache 全栈优化系统" README,
+ * section 主要特性: K/V quantised as they are written, restored inside
+ * attention).  The token of sequence b goes to position context_lens[b] - 1
+ * (context_lens already count it; values above max_context_len are clamped
+ * first, as in paged_decode_attn_kv8), i.e. to slot
+ * block_table[b][p / 16] * 16 + p % 16; sequences with an empty context
+ * append nothing.  The workgroup that attends over a sequence's last split
+ * quantises the row and stores it before reading it back, so no separate
+ * append kernel and no grid-wide synchronisation is needed.
+ *
+ *   k_new, v_new  device bf16 [B, Hkv, d], 16-byte aligned
+ *   k_cache, v_cache, k_scale, v_scale  as for kv8_quant_append (written)
+ *   all other arguments as for paged_decode_attn_kv8
+ * Returns as paged_decode_attn_kv8, and KV8_ERR_NULL / KV8_ERR_ALIGN for
+ * k_new or v_new.
+ */
+int paged_decode_attn_kv8_append(const void* q, int q_dtype,
+                                 const uint16_t* k_new, const uint16_t* v_new,
+                                 int8_t* k_cache, int8_t* v_cache,
+                                 uint16_t* k_scale, uint16_t* v_scale,
+                                 int64_t num_blocks,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len,
+                                 int batch, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, float sm_scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 int tokens_per_split, void* stream);
+
+/*
  * paged_decode_attn_bf16kv - the same decode attention over a paged cache
  * that holds K and V unquantised, as bf16: the 16-bit reference point that
  * the KV8 method is compared with at an equal memory budget ("KV-Cache

@@ -27,7 +27,7 @@ EXPORTED = (
     "kv8_status_string", "kv8_version", "kv8_quant_append", "kv8_decode_workspace_size",
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
-    "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append",
+    "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
 )
 
 _lib = None
@@ -70,6 +70,10 @@ def load():
     lib.paged_decode_attn_kv8.restype = i32
     lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
+    lib.paged_decode_attn_kv8_append.restype = i32
+    lib.paged_decode_attn_kv8_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, i32,
+                                                 vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                                 sz, i32, vp]
     lib.paged_decode_attn_fp8kv.restype = i32
     lib.paged_decode_attn_fp8kv.argtypes = lib.paged_decode_attn_kv8.argtypes
     lib.paged_decode_attn_bf16kv.restype = i32
@@ -183,6 +187,27 @@ def paged_decode_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, block_table, 
     """As paged_decode_attn_kv8, over an FP8 (e4m3) cache."""
     _decode("paged_decode_attn_fp8kv", q, k_cache, v_cache, k_scale, v_scale, block_table,
             context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+
+
+def paged_decode_attn_kv8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                                 block_table, context_lens, max_context_len, out, workspace,
+                                 sm_scale=None, tokens_per_split=0, stream=None):
+    """One decode step: append k_new/v_new (bf16 [B, Hkv, d], the newest token
+    of each sequence, at position context_lens[b] - 1), then decode."""
+    import torch
+    b, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    dt = KV8_BF16 if q.dtype == torch.bfloat16 else KV8_F32
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    st = load().paged_decode_attn_kv8_append(
+        _ptr(q), dt, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), nb, _ptr(block_table), block_table.shape[1], _ptr(context_lens),
+        int(max_context_len), b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out),
+        _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        int(tokens_per_split), _stream(stream))
+    _check(st, "paged_decode_attn_kv8_append")
 
 
 def paged_decode_attn_bf16kv(q, k_cache, v_cache, block_table, context_lens, max_context_len,

@@ -57,7 +57,8 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                           const int32_t* context_lens, int max_context_len, int batch,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, bool fp8, void* stream) {
+                          int tokens_per_split, bool fp8, const uint16_t* k_new,
+                const uint16_t* v_new, void* stream) {
   if (!q || !block_table || !context_lens || !out) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
   if (rc != KV8_OK) return rc;
@@ -82,7 +83,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
   const int r = kv8::launch_decode(q, q_dtype == KV8_F32, k_cache, v_cache, k_scale, v_scale,
                                    num_blocks, block_table, max_blocks_per_seq, context_lens,
                                    ctx_cap, batch, num_q_heads, num_kv_heads, head_dim,
-                                   sm_scale, out, workspace, plan, fp8,
+                                   sm_scale, out, workspace, plan, fp8, k_new, v_new,
                                    static_cast<hipStream_t>(stream));
   if (r == -2) return KV8_ERR_UNSUPPORTED;
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
@@ -202,7 +203,7 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
   return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, false, stream);
+                     workspace_bytes, tokens_per_split, false, nullptr, nullptr, stream);
 }
 
 int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
@@ -217,7 +218,23 @@ int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, true, stream);
+                     workspace_bytes, tokens_per_split, true, nullptr, nullptr, stream);
+}
+
+int paged_decode_attn_kv8_append(const void* q, int q_dtype, const uint16_t* k_new,
+                                 const uint16_t* v_new, int8_t* k_cache, int8_t* v_cache,
+                                 uint16_t* k_scale, uint16_t* v_scale, int64_t num_blocks,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, int batch,
+                                 int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, float sm_scale, float* out, void* workspace,
+                                 size_t workspace_bytes, int tokens_per_split, void* stream) {
+  if (!k_new || !v_new) return KV8_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KV8_ERR_ALIGN;
+  return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                     workspace_bytes, tokens_per_split, false, k_new, v_new, stream);
 }
 
 int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache,

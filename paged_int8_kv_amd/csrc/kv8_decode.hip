@@ -58,6 +58,8 @@ struct SplitArgs {
   const int8_t* v_cache;
   const uint16_t* k_scale;
   const uint16_t* v_scale;
+  const uint16_t* k_new;   // bf16 [B, Hkv, D] newest token per sequence, or null
+  const uint16_t* v_new;
   const int32_t* block_table;
   const int32_t* context_lens;
   float* out;
@@ -151,6 +153,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + tid];
     id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
     s_blk[tid] = (int)id;
+  }
+
+  // ---- decode step with append: the newest token of the sequence sits at
+  // position ctx - 1, inside the last split, so that split's workgroup
+  // quantises the token's K and V rows of head g (as the append kernel
+  // does) and stores them before its passes read the block back.  Wave 0's
+  // stores complete (vmcnt 0) before the barrier below, and every later load
+  // of the workgroup comes after that barrier on the same CU.
+  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == 0) {
+    constexpr int LPR = D / 8;          // lanes per row, 8 values each
+    if (lane < LPR) {
+      const int p = ctx - 1;
+      int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + p / kBlock];
+      id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+      const int64_t line = (id * Hkv + g) * kBlock + p % kBlock;
+      const int64_t src = ((int64_t)b * Hkv + g) * D + lane * 8;
+      float kx[8], vx[8], ka, va;
+      unpack8(*reinterpret_cast<const uint4*>(a.k_new + src), kx, ka);
+      unpack8(*reinterpret_cast<const uint4*>(a.v_new + src), vx, va);
+      ka = row_absmax<LPR>(ka);
+      va = row_absmax<LPR>(va);
+      const float ks = fp16_scale<C>(ka), vs = fp16_scale<C>(va);
+      *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.k_cache) + line * D + lane * 8) =
+          quantise8<C>(kx, ks);
+      *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.v_cache) + line * D + lane * 8) =
+          quantise8<C>(vx, vs);
+      if (lane == 0) {
+        const_cast<uint16_t*>(a.k_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)ks);
+        const_cast<uint16_t*>(a.v_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)vs);
+      }
+    }
+    wait_vmem();
   }
 
   // ---- q of the G heads: this lane's d/8 channels as fp16 pairs ----------
@@ -475,7 +509,8 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, bool fp8, hipStream_t stream) {
+                  void* workspace, const DecodePlan& plan, bool fp8, const uint16_t* k_new,
+                  const uint16_t* v_new, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs a;
   a.q = q;
@@ -483,6 +518,8 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.v_cache = v_cache;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.out = out;

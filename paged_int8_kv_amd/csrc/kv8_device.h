@@ -186,6 +186,51 @@ struct CodesFp8 {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Row quantiser shared by the append kernel and the decode step that appends
+// its newest token: LPR lanes hold one (token, KV head) row of d = 8 * LPR
+// bf16 values, 8 per lane.  Scale s = fp16_rne(fp32(absmax / kQmax)) with
+// gradual underflow, saturated to 65504; codes by C::code; a zero scale
+// gives all-zero codes.
+// ---------------------------------------------------------------------------
+template <int LPR>
+__device__ __forceinline__ float row_absmax(float a) {
+  static_assert(LPR == 8 || LPR == 16, "row of 64 or 128 channels");
+  if constexpr (LPR == 8) return group8_max(a);
+  else return group16_max(a);
+}
+
+template <class C>
+__device__ __forceinline__ float fp16_scale(float absmax) {
+  const float s32 = absmax / C::kQmax;               // IEEE divide, RNE
+  _Float16 s16 = (_Float16)s32;                       // RNE, gradual underflow
+  if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+  return (float)s16;
+}
+
+template <class C>
+__device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
+  uint32_t w0 = 0, w1 = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w0 |= C::code(x[i], s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w1 |= C::code(x[4 + i], s) << (8 * i);
+  }
+  return make_uint2(w0, w1);
+}
+
+__device__ __forceinline__ void unpack8(uint4 raw, float (&x)[8], float& amax) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }

@@ -1,7 +1,9 @@
 // Internal launchers of libkv8: called by the C ABI layer (kv8_api.cpp)
 // after host validation.  `fp8` selects the FP8 (e4m3) code format of the
-// cache instead of INT8; caches are passed as bytes either way.  Each
-// returns 0 on success and -1 when the HIP runtime reports a launch error.
+// cache instead of INT8; caches are passed as bytes either way.  A
+// non-null k_new/v_new makes launch_decode append each sequence's newest
+// token (position context_lens[b] - 1) before attending.  Each returns 0 on
+// success and -1 when the HIP runtime reports a launch error.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,7 +42,8 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, bool fp8, hipStream_t stream);
+                  void* workspace, const DecodePlan& plan, bool fp8, const uint16_t* k_new,
+                  const uint16_t* v_new, hipStream_t stream);
 
 int launch_decode_bf16kv(const void* q, bool q_f32, const uint16_t* k_cache,
                          const uint16_t* v_cache, int64_t num_blocks,
