@@ -470,3 +470,139 @@ def rope_quant_append(k_pre, v_new, positions, cos_sin, slot_mapping, k_cache, v
     the rotated K and the unrotated V."""
     k_rot = rope_rotate_half(k_pre, positions, cos_sin)
     quant_append(k_rot, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size)
+
+
+# --------------------------------------------------------------------------
+# INT4 KV cache.  "KV Cache 优化全景解析" section 2.3 counts INT4 at 0.5 byte
+# per element in the KV-size formula, and the KV-cache optimisation page of
+# garden.houmin.site (section 2.2.2, directions for optimisation) lists
+# compressing the cache from FP16 to INT8 or INT4.
+# Readings (listed in the design notes): the INT8 recipe with 7 in place of
+# 127, i.e. one fp16 scale per (token, KV head), s = fp16_rne(fp32_rne(
+# absmax / 7)), codes = clamp(round_half_even(fp32(x / s)), -7, 7), all zero
+# when s == 0; two codes per byte as 4-bit two's complement, element 2i in
+# the low nibble of byte i and element 2i+1 in the high nibble; the paged
+# layout of the INT8 cache with d/2 bytes per row.
+# --------------------------------------------------------------------------
+INT4_QMAX = 7
+
+
+def row_scale_int4(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    s32 = a / np.float32(INT4_QMAX)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(FP16_MAX), s16).astype(np.float16)
+
+
+def codes_int4_for_scale(x, s):
+    """Signed codes -7..7 (int8 array, unpacked) under fp16 scales s."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 / np.where(zero, np.float32(1), s32)
+    q = np.clip(np.rint(quot.astype(np.float64)), -INT4_QMAX, INT4_QMAX)
+    return np.where(zero, 0.0, q).astype(np.int8)
+
+
+def pack_int4(codes):
+    """[..., d] signed codes -> [..., d/2] bytes: element 2i in the low
+    nibble of byte i, element 2i+1 in the high nibble."""
+    c = np.asarray(codes, np.int64) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed):
+    """[..., d/2] bytes -> [..., d] signed codes (int8)."""
+    p = np.asarray(packed, np.int64)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.int64)
+    out[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return out.astype(np.int8)
+
+
+def quantize_rows_int4(x):
+    """Rows [..., d] -> (packed codes uint8 [..., d/2], scales fp16 [...])."""
+    s = row_scale_int4(x)
+    return pack_int4(codes_int4_for_scale(x, s)), s
+
+
+def dequantize_rows_int4(packed, scales):
+    return unpack_int4(packed).astype(np.float64) * \
+        np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+def alloc_paged_cache_int4(num_blocks, num_kv_heads, head_dim, block_size=BLOCK_SIZE):
+    kc = np.zeros((num_blocks, num_kv_heads, block_size, head_dim // 2), np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((num_blocks, num_kv_heads, block_size), np.float16)
+    vs = np.zeros_like(ks)
+    return kc, vc, ks, vs
+
+
+def quant_append_int4(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                      block_size=BLOCK_SIZE):
+    """As quant_append, with packed INT4 codes."""
+    kc, ks = quantize_rows_int4(k_new)
+    vc, vs = quantize_rows_int4(v_new)
+    for n, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        blk, off = slot_to_block(slot, block_size)
+        k_cache[blk, :, off, :] = kc[n]
+        v_cache[blk, :, off, :] = vc[n]
+        k_scale[blk, :, off] = ks[n]
+        v_scale[blk, :, off] = vs[n]
+
+
+def gather_dequant_int4(packed, scales, block_table_row, ctx, kv_head, block_size=BLOCK_SIZE):
+    t = np.arange(ctx)
+    blk, off = logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return dequantize_rows_int4(packed[blk, kv_head, off, :], scales[blk, kv_head, off])
+
+
+def paged_decode_int4(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                      sm_scale=None, block_size=BLOCK_SIZE):
+    """paged_decode over a packed INT4 cache.  Returns fp64 [B, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    G = Hq // k_cache.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        if ctx <= 0:
+            continue
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant_int4(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant_int4(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[b, h] = softmax_attention(q[b, h][None, :], k, v, sm_scale)[0]
+    return out
+
+
+def paged_prefill_chunk_int4(q, q_start_loc, k_cache, v_cache, k_scale, v_scale,
+                             block_table, context_lens, sm_scale=None, block_size=BLOCK_SIZE):
+    """paged_prefill_chunk over a packed INT4 cache.  Returns fp64 [Tq, Hq, d]."""
+    q = np.asarray(q, np.float64)
+    Tq, Hq, d = q.shape
+    G = Hq // k_cache.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    out = np.zeros((Tq, Hq, d), np.float64)
+    for b in range(len(context_lens)):
+        r0, r1 = int(q_start_loc[b]), int(q_start_loc[b + 1])
+        lc, ctx = r1 - r0, int(context_lens[b])
+        if lc <= 0 or ctx <= 0:
+            continue
+        visible = causal_visibility(ctx, lc)
+        for h in range(Hq):
+            g = kv_head_of(h, G)
+            k = gather_dequant_int4(k_cache, k_scale, block_table[b], ctx, g, block_size)
+            v = gather_dequant_int4(v_cache, v_scale, block_table[b], ctx, g, block_size)
+            out[r0:r1, h] = softmax_attention(q[r0:r1, h], k, v, sm_scale, visible)
+    return out

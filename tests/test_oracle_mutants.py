@@ -43,6 +43,10 @@ def _battery():
         ("rope_library", P.test_rope_matches_transformers_and_fp64),
         ("rope_props", P.test_rope_identity_at_zero_and_relative_position),
         ("rope_append", P.test_rope_quant_append_is_rotate_then_quantise),
+        ("int4_pack", P.test_int4_packing_worked_example_and_roundtrip),
+        ("int4_invariants", P.test_int4_quantiser_invariants),
+        ("int4_attention", P.test_int4_decode_and_prefill_brute_force),
+        ("int4_codes", lambda: P.test_int4_codes_every_bf16(1.0)),
     ]
     for name, fn in checks:
         try:
@@ -206,6 +210,28 @@ def _rope_interleaved(x, positions, cos_sin):
     return out
 
 
+def _pack_int4_swapped(codes):
+    c = np.asarray(codes, np.int64) & 0xF
+    return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
+
+
+def _row_scale_int4_8(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = (a / np.float32(8)).astype(np.float16)
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
+def _unpack_int4_sign_magnitude(packed):
+    p = np.asarray(packed, np.int64)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.int64)
+    out[..., 0::2] = np.where(lo >= 8, -(lo - 8), lo)
+    out[..., 1::2] = np.where(hi >= 8, -(hi - 8), hi)
+    return out.astype(np.int8)
+
+
 MUTANTS = {
     "head_map_mod": ("kv_head_of", lambda h, group: h % group),
     "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
@@ -234,6 +260,9 @@ MUTANTS = {
     "rope_sign": ("rope_rotate_half", _rope_sign),
     "rope_cos_sin_swapped": ("rope_rotate_half", _rope_cos_sin_swapped),
     "rope_interleaved": ("rope_rotate_half", _rope_interleaved),
+    "int4_nibbles_swapped": ("pack_int4", _pack_int4_swapped),
+    "int4_scale_8": ("row_scale_int4", _row_scale_int4_8),
+    "int4_sign_magnitude": ("unpack_int4", _unpack_int4_sign_magnitude),
 }
 
 

@@ -703,3 +703,98 @@ def test_rope_quant_append_is_rotate_then_quantise():
     blk, off = case.slot_mapping // 16, case.slot_mapping % 16
     assert np.array_equal(kc[blk, :, off], kq) and np.array_equal(vc[blk, :, off], vq)
     assert np.array_equal(ks[blk, :, off], ksc) and np.array_equal(vs[blk, :, off], vsc)
+
+
+# ---------------------------------------------------------------------------
+# INT4 cache (KV-size table of "KV Cache 优化全景解析" section 2.3: INT4 = 0.5 B;
+# reading: the INT8 recipe with 7 in place of 127, two's-complement nibbles)
+# ---------------------------------------------------------------------------
+def exact_codes_q(x, s, qmax):
+    """round_half_even(x / s) clamped to +-qmax by exact rational arithmetic."""
+    if s == 0:
+        return np.zeros(len(x), np.int64)
+    out = []
+    for xv in np.asarray(x, np.float64).tolist():
+        q = round(Fraction(xv) / Fraction(float(s)))
+        out.append(max(-qmax, min(qmax, q)))
+    return np.array(out, np.int64)
+
+
+def test_int4_scale_every_bf16_absmax():
+    a = all_finite_bf16(positive_only=True)
+    got = O.row_scale_int4(a[:, None]).astype(np.float64)
+    pick = np.random.default_rng(51).choice(len(a), 4000, replace=False)
+    for i in pick.tolist():
+        e = fp16_rne_exact(Fraction(float(a[i])) / 7)
+        assert got[i] == (65504.0 if e == math.inf else e)
+
+
+@pytest.mark.parametrize("s", [1.0, 0.0234375, 3 * 2 ** -24, 2.0 ** -14, 9362.0])
+def test_int4_codes_every_bf16(s):
+    x = all_finite_bf16()
+    got = O.codes_int4_for_scale(x[None, :], np.array([s], np.float16))[0].astype(np.int64)
+    # exact rational rounding, on every value whose quotient is within the
+    # clamp (+-7.5) and on a sample beyond it
+    q = np.abs(x.astype(np.float64)) / s
+    near = np.nonzero(q < 16)[0]
+    far = np.nonzero(q >= 16)[0]
+    far = far[np.random.default_rng(52).choice(len(far), min(300, len(far)), replace=False)]
+    for idx in (near, far):
+        assert np.array_equal(got[idx], exact_codes_q(x[idx], np.float16(s), 7))
+
+
+def test_int4_packing_worked_example_and_roundtrip():
+    codes = np.array([[-7, 7, 0, -1, 1, -2, 5, 3]], np.int8)
+    packed = O.pack_int4(codes)
+    # byte i = (code 2i+1 & 0xF) << 4 | (code 2i & 0xF)
+    assert packed.tolist() == [[0x79, 0xF0, 0xE1, 0x35]]
+    assert np.array_equal(O.unpack_int4(packed), codes)
+    rng = np.random.default_rng(53)
+    c = rng.integers(-7, 8, size=(100, 64)).astype(np.int8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(c)), c)
+
+
+def test_int4_quantiser_invariants():
+    rng = np.random.default_rng(54)
+    rows, _ = W.to_bf16(rng.standard_normal((500, 128)).astype(np.float32))
+    p, s = O.quantize_rows_int4(rows)
+    c = O.unpack_int4(p)
+    am = np.argmax(np.abs(rows), axis=1)
+    assert np.all(np.abs(c[np.arange(500), am]) == 7) and c.min() >= -7 and c.max() <= 7
+    err = np.abs(rows - O.dequantize_rows_int4(p, s))
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2)
+    pn, sn = O.quantize_rows_int4(-rows)
+    assert np.array_equal(O.unpack_int4(pn), -c) and np.array_equal(sn, s)
+
+
+def build_cache_int4(case):
+    kc, vc, ks, vs = O.alloc_paged_cache_int4(case.num_blocks, case.num_kv_heads, case.head_dim)
+    O.quant_append_int4(case.k, case.v, case.slot_mapping, kc, vc, ks, vs)
+    return kc, vc, ks, vs
+
+
+def test_int4_decode_and_prefill_brute_force():
+    case = W.make_paged_case(batch=2, num_q_heads=4, num_kv_heads=2, head_dim=16,
+                             context_lens=[5, 37], q_dtype="f32", seed=55)
+    kc, vc, ks, vs = build_cache_int4(case)
+    out = O.paged_decode_int4(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    for b in range(2):
+        K = O.dequantize_rows_int4(*O.quantize_rows_int4(case.k[case.token_seq == b]))
+        V = O.dequantize_rows_int4(*O.quantize_rows_int4(case.v[case.token_seq == b]))
+        for h in range(4):
+            ref = brute_attention(case.q[b, h], K[:, h // 2], V[:, h // 2], 1 / math.sqrt(16))
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13)
+    pc = W.prefill_case([0, 9], [21, 40], num_q_heads=4, num_kv_heads=2, head_dim=16, seed=56)
+    kc, vc, ks, vs = build_cache_int4(pc)
+    pout = O.paged_prefill_chunk_int4(pc.q, pc.extra["q_start_loc"], kc, vc, ks, vs,
+                                      pc.block_table, pc.context_lens)
+    qsl = pc.extra["q_start_loc"]
+    for b in range(2):
+        ctx = int(pc.context_lens[b])
+        K = O.gather_dequant_int4(kc, ks, pc.block_table[b], ctx, 1)
+        V = O.gather_dequant_int4(vc, vs, pc.block_table[b], ctx, 1)
+        lc = qsl[b + 1] - qsl[b]
+        for i in (0, lc - 1):
+            pos = ctx - lc + i
+            ref = brute_attention(pc.q[qsl[b] + i, 3], K[:pos + 1], V[:pos + 1], 1 / math.sqrt(16))
+            assert np.allclose(pout[qsl[b] + i, 3], ref, rtol=1e-12, atol=1e-13)
