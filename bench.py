@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--cpu-steps", type=int, default=4)
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--fp8-steps", type=int, default=1,
-                   help="0 skips the FP8 (e4m3) cache lines")
+                   help="0 skips the FP8 (e4m3) and INT4 cache lines")
     p.add_argument("--budget-steps", type=int, default=10,
                    help="decode calls timed per side of the 258K equal-budget comparison "
                         "(0 skips it)")
@@ -276,9 +276,11 @@ def main():
     if args.prefill_steps > 0:
         result["prefill"] = bench_prefill(args, dev)
     if args.fp8_steps > 0:
-        result["fp8_kv"] = {"decode": bench_fp8_decode(args, dev, case, d_bytes)}
+        result["fp8_kv"] = {"decode": bench_code_decode(args, dev, case, "fp8")}
         if args.prefill_steps > 0:
             result["fp8_kv"]["prefill"] = bench_prefill(args, dev, fp8=True)
+    if args.fp8_steps > 0:
+        result["int4_kv"] = {"decode": bench_code_decode(args, dev, case, "int4")}
     if args.budget_steps > 0:
         result["equal_budget_258k"] = bench_equal_budget(args, dev)
     if not args.no_cpu_baseline:
@@ -353,46 +355,55 @@ def bench_prefill(args, dev, fp8=False):
                                     "paged_prefill_chunk_attn_kv8") + " (fp16 MFMA 32x32x16)"}}
 
 
-def bench_fp8_decode(args, dev, case, d_bytes):
-    """paged_decode_attn_fp8kv on the same decode workload, cache written by
-    kv8_quant_append_fp8, launches back to back over rotated replicas."""
+def bench_code_decode(args, dev, case, fmt):
+    """Decode over an FP8 (e4m3) or INT4 cache on the same decode workload,
+    cache written by the matching append, launches back to back over
+    rotated replicas.  Algorithmic bytes as for INT8 with the code bytes of
+    the format (d for FP8, d/2 for INT4)."""
     import torch
     from paged_int8_kv_amd import binding as B
     bsz, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
-    max_ctx = int(case.context_lens.max())
+    ctx = case.context_lens
+    max_ctx = int(ctx.max())
+    int4 = fmt == "int4"
+    append = B.kv8_quant_append_int4 if int4 else B.kv8_quant_append_fp8
+    decode = B.paged_decode_attn_int4kv if int4 else B.paged_decode_attn_fp8kv
     k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     slots = torch.from_numpy(case.slot_mapping).to(dev)
     caches = []
     for _ in range(args.replicas):
-        c = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=True)
-        B.kv8_quant_append_fp8(k_all, v_all, slots, *c)
+        c = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=not int4, int4=int4)
+        append(k_all, v_all, slots, *c)
         caches.append(c)
     del k_all, v_all
     q = torch.from_numpy(case.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     table = torch.from_numpy(case.block_table).to(dev)
-    lens = torch.from_numpy(case.context_lens).to(dev)
+    lens = torch.from_numpy(ctx).to(dev)
     out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
     ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx), dtype=torch.uint8,
                      device=dev)
     n = max(args.steps, 50)
-    for i in range(10):
-        B.paged_decode_attn_fp8kv(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+    for i in range(200):
+        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
-        B.paged_decode_attn_fp8kv(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
+    code_bytes = d // 2 if int4 else d
+    nbytes = (int(ctx.sum()) * 2 * hkv * (code_bytes + 2) + bsz * hq * d * 2 + bsz * hq * d * 4
+              + 4 * int(np.sum((ctx + 15) // 16)) + 4 * bsz)
     del caches, ws, out
     torch.cuda.empty_cache()
-    return {"workload": "the decode layer above over an FP8 (e4m3) cache, decode launches back "
-                        "to back", "decode_us": round(us, 2),
-            "kv_gbs": round(d_bytes / (us * 1e-6) / 1e9, 1),
-            "kv_tokens_per_s": round(float(case.context_lens.sum()) / (us * 1e-6), 1)}
+    return {"workload": f"the decode layer above over an {'INT4' if int4 else 'FP8 (e4m3)'} "
+                        "cache, decode launches back to back", "decode_us": round(us, 2),
+            "bytes_per_launch": nbytes, "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "kv_tokens_per_s": round(float(ctx.sum()) / (us * 1e-6), 1)}
 
 
 def bench_equal_budget(args, dev):
@@ -427,12 +438,14 @@ def bench_equal_budget(args, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3     # us per call
 
+    per_tok_int4 = 2 * hkv * (d // 2 + 2)
+    b4 = budget // (ctx * per_tok_int4)
     res = {"workload": f"decode, Llama-3.1-8B attention (Hq=32, Hkv=8, d=128), {ctx} tokens per "
                        "sequence, bf16 q, one KV budget per layer",
            "context_tokens": ctx, "budget_bytes": int(budget),
-           "bf16_kv": {"batch": b16}, "int8_kv": {"batch": int(b8)}}
+           "bf16_kv": {"batch": b16}, "int8_kv": {"batch": int(b8)}, "int4_kv": {"batch": int(b4)}}
     outs = {}
-    for kind, batch in (("bf16_kv", b16), ("int8_kv", int(b8))):
+    for kind, batch in (("bf16_kv", b16), ("int8_kv", int(b8)), ("int4_kv", int(b4))):
         w = W.long_context_258k(batch, dev)
         nb = w["num_blocks"]
         table = torch.from_numpy(w["block_table"]).to(dev)
@@ -452,7 +465,7 @@ def bench_equal_budget(args, dev):
             cache = (kc, vc)
             call = lambda: B.paged_decode_attn_bf16kv(w["q"], *cache, table, lens, ctx, out, ws)
             nbytes = batch * ctx * per_tok_bf16
-        else:
+        elif kind == "int8_kv":
             cache = B.alloc_cache(nb, hkv, d, dev)
             for b in range(batch):
                 k, v = w["tokens"](b)
@@ -460,6 +473,14 @@ def bench_equal_budget(args, dev):
                 del k, v
             call = lambda: B.paged_decode_attn_kv8(w["q"], *cache, table, lens, ctx, out, ws)
             nbytes = batch * ctx * per_tok_int8
+        else:
+            cache = B.alloc_cache(nb, hkv, d, dev, int4=True)
+            for b in range(batch):
+                k, v = w["tokens"](b)
+                B.kv8_quant_append_int4(k, v, w["slots"](b), *cache)
+                del k, v
+            call = lambda: B.paged_decode_attn_int4kv(w["q"], *cache, table, lens, ctx, out, ws)
+            nbytes = batch * ctx * per_tok_int4
         torch.cuda.synchronize()
         us = timed(call, args.budget_steps)
         outs[kind] = out.clone()
@@ -471,9 +492,13 @@ def bench_equal_budget(args, dev):
         torch.cuda.empty_cache()
     res["throughput_ratio_int8_over_bf16"] = round(
         res["int8_kv"]["decode_tokens_per_s"] / res["bf16_kv"]["decode_tokens_per_s"], 3)
+    res["throughput_ratio_int4_over_bf16"] = round(
+        res["int4_kv"]["decode_tokens_per_s"] / res["bf16_kv"]["decode_tokens_per_s"], 3)
     n = min(b16, int(b8))
     res["int8_vs_bf16_output_max_abs"] = float(
         (outs["int8_kv"][:n] - outs["bf16_kv"][:n]).abs().max().item())
+    res["int4_vs_bf16_output_max_abs"] = float(
+        (outs["int4_kv"][:n] - outs["bf16_kv"][:n]).abs().max().item())
     res["pages_figure"] = "1.64x KV8 over FA2 at 258K, same memory budget, L40S, system level"
     return res
 

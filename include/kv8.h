@@ -345,6 +345,41 @@ int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc
                                    float* out, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * INT4 cache.  "KV Cache 优化全景解析" counts INT4 at 0.5 byte per element in
+ * its KV-size formula (section 2.3), and the KV-cache optimisation page of
+ * garden.houmin.site (section 2.2.2) lists compressing the cache from FP16
+ * to INT8 or INT4.  Same recipe as INT8 with 7 in place of 127:
+ *   s    = fp16_rne(fp32_rne(absmax / 7)), saturated to 65504;
+ *   code = clamp(round_half_even(fp32(x / s)), -7, 7); all zero if s == 0;
+ *   x_hat = code * s.
+ * Two codes per byte as 4-bit two's complement, element 2i in the low
+ * nibble of byte i: codes [num_blocks, Hkv, 16, d/2] bytes; one fp16 scale
+ * per (token slot, KV head) for K and for V as in the INT8 cache.
+ * kv8_quant_append_int4 and paged_decode_attn_int4kv take the same
+ * arguments, with the same meaning, ownership and errors, as
+ * kv8_quant_append and paged_decode_attn_kv8 (the decode workspace is sized
+ * by kv8_decode_workspace_size).
+ */
+int kv8_quant_append_int4(const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* slot_mapping, int64_t n_tokens,
+                          int num_kv_heads, int head_dim, int block_size,
+                          int64_t num_blocks,
+                          uint8_t* k_cache, uint8_t* v_cache,
+                          uint16_t* k_scale, uint16_t* v_scale,
+                          void* stream);
+
+int paged_decode_attn_int4kv(const void* q, int q_dtype,
+                             const uint8_t* k_cache, const uint8_t* v_cache,
+                             const uint16_t* k_scale, const uint16_t* v_scale,
+                             int64_t num_blocks,
+                             const int32_t* block_table, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int batch, int num_q_heads, int num_kv_heads,
+                             int head_dim, int block_size, float sm_scale,
+                             float* out, void* workspace, size_t workspace_bytes,
+                             int tokens_per_split, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ EXPORTED = (
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
+    "kv8_quant_append_int4", "paged_decode_attn_int4kv",
 )
 
 _lib = None
@@ -65,6 +66,8 @@ def load():
                                           vp, vp, vp, vp, vp]
     lib.kv8_quant_append_fp8.restype = i32
     lib.kv8_quant_append_fp8.argtypes = lib.kv8_quant_append.argtypes
+    lib.kv8_quant_append_int4.restype = i32
+    lib.kv8_quant_append_int4.argtypes = lib.kv8_quant_append.argtypes
     lib.kv8_decode_workspace_size.restype = sz
     lib.kv8_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_decode_attn_kv8.restype = i32
@@ -76,6 +79,8 @@ def load():
                                                  sz, i32, vp]
     lib.paged_decode_attn_fp8kv.restype = i32
     lib.paged_decode_attn_fp8kv.argtypes = lib.paged_decode_attn_kv8.argtypes
+    lib.paged_decode_attn_int4kv.restype = i32
+    lib.paged_decode_attn_int4kv.argtypes = lib.paged_decode_attn_kv8.argtypes
     lib.paged_decode_attn_bf16kv.restype = i32
     lib.paged_decode_attn_bf16kv.argtypes = [vp, i32, vp, vp, i64, vp, i32, vp, i32,
                                              i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
@@ -149,6 +154,14 @@ def kv8_rope_quant_append(k_new, v_new, slot_mapping, positions, cos_sin, k_cach
     _check(st, "kv8_rope_quant_append")
 
 
+def kv8_quant_append_int4(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                          stream=None):
+    """As kv8_quant_append, into an INT4 cache (packed codes uint8
+    [NB, Hkv, 16, d/2])."""
+    _append("kv8_quant_append_int4", k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
+            v_scale, stream)
+
+
 def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                               tokens_per_split=0):
     return int(load().kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
@@ -178,6 +191,14 @@ def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, co
     """q: fp32 or bf16 [B, Hq, d]; out fp32 [B, Hq, d]; workspace uint8 of at
     least kv8_decode_workspace_size() bytes."""
     _decode("paged_decode_attn_kv8", q, k_cache, v_cache, k_scale, v_scale, block_table,
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+
+
+def paged_decode_attn_int4kv(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                             max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
+                             stream=None):
+    """As paged_decode_attn_kv8, over an INT4 cache."""
+    _decode("paged_decode_attn_int4kv", q, k_cache, v_cache, k_scale, v_scale, block_table,
             context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
 
 
@@ -272,13 +293,14 @@ def paged_prefill_chunk_attn_fp8kv(q, q_start_loc, max_q_len, k_cache, v_cache, 
              sm_scale, stream)
 
 
-def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False):
-    """Zeroed paged cache tensors: codes int8 (uint8 for the FP8 cache)
-    [NB, Hkv, 16, d] and fp16 scales [NB, Hkv, 16] (stored as int16 bit
-    patterns), for K and V."""
+def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False, int4=False):
+    """Zeroed paged cache tensors: codes int8 [NB, Hkv, 16, d] (uint8 for the
+    FP8 cache; uint8 [NB, Hkv, 16, d/2] of packed nibbles for the INT4 cache)
+    and fp16 scales [NB, Hkv, 16] (stored as int16 bit patterns), for K and
+    V."""
     import torch
-    kc = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim),
-                     dtype=torch.uint8 if fp8 else torch.int8, device=device)
+    kc = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim // 2 if int4 else head_dim),
+                     dtype=torch.uint8 if (fp8 or int4) else torch.int8, device=device)
     vc = torch.zeros_like(kc)
     ks = torch.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.int16, device=device)
     vs = torch.zeros_like(ks)

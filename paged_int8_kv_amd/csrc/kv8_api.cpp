@@ -35,7 +35,7 @@ int check_cache(const int8_t* kc, const int8_t* vc, const uint16_t* ks, const ui
 int append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
                  int64_t n_tokens, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,
-                     int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, bool fp8, void* stream) {
+                     int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, int fmt, void* stream) {
   if (n_tokens < 0 || num_kv_heads <= 0) return KV8_ERR_SHAPE;
   if (!supported_dim(head_dim)) return KV8_ERR_UNSUPPORTED;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
@@ -46,7 +46,7 @@ int append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slo
   if (n_tokens * num_kv_heads * (head_dim / 8) / 256 >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;
   const int r = kv8::launch_quant_append(k_new, v_new, slot_mapping, n_tokens, num_kv_heads,
                                          head_dim, num_blocks, k_cache, v_cache, k_scale,
-                                         v_scale, fp8, static_cast<hipStream_t>(stream));
+                                         v_scale, fmt, static_cast<hipStream_t>(stream));
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
 }
 
@@ -57,7 +57,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                           const int32_t* context_lens, int max_context_len, int batch,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, bool fp8, const uint16_t* k_new,
+                          int tokens_per_split, int fmt, const uint16_t* k_new,
                 const uint16_t* v_new, void* stream) {
   if (!q || !block_table || !context_lens || !out) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
@@ -83,7 +83,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
   const int r = kv8::launch_decode(q, q_dtype == KV8_F32, k_cache, v_cache, k_scale, v_scale,
                                    num_blocks, block_table, max_blocks_per_seq, context_lens,
                                    ctx_cap, batch, num_q_heads, num_kv_heads, head_dim,
-                                   sm_scale, out, workspace, plan, fp8, k_new, v_new,
+                                   sm_scale, out, workspace, plan, fmt, k_new, v_new,
                                    static_cast<hipStream_t>(stream));
   if (r == -2) return KV8_ERR_UNSUPPORTED;
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
@@ -97,7 +97,7 @@ int prefill_impl(const uint16_t* q, const int32_t* q_start_loc,
                                  const int32_t* context_lens, int max_context_len, int batch,
                                  int num_q_heads, int num_kv_heads, int head_dim,
                                  int block_size, float sm_scale, float* out, void* workspace,
-                                 size_t workspace_bytes, bool fp8, void* stream) {
+                                 size_t workspace_bytes, int fmt, void* stream) {
   (void)workspace; (void)workspace_bytes;
   if (!q_start_loc || !block_table || !context_lens) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
@@ -118,7 +118,7 @@ int prefill_impl(const uint16_t* q, const int32_t* q_start_loc,
   const int r = kv8::launch_prefill(q, q_start_loc, total_q, max_q_len, k_cache, v_cache,
                                     k_scale, v_scale, num_blocks, block_table,
                                     max_blocks_per_seq, context_lens, ctx_cap, batch,
-                                    num_q_heads, num_kv_heads, head_dim, sm_scale, out, fp8,
+                                    num_q_heads, num_kv_heads, head_dim, sm_scale, out, fmt,
                                     static_cast<hipStream_t>(stream));
   if (r == -2) return KV8_ERR_UNSUPPORTED;
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
@@ -148,7 +148,7 @@ int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                      int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,
                      int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
   return append_impl(k_new, v_new, slot_mapping, n_tokens, num_kv_heads, head_dim, block_size,
-                     num_blocks, k_cache, v_cache, k_scale, v_scale, false, stream);
+                     num_blocks, k_cache, v_cache, k_scale, v_scale, kv8::kFmtInt8, stream);
 }
 
 int kv8_quant_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
@@ -157,7 +157,7 @@ int kv8_quant_append_fp8(const uint16_t* k_new, const uint16_t* v_new,
                          uint8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
   return append_impl(k_new, v_new, slot_mapping, n_tokens, num_kv_heads, head_dim, block_size,
                      num_blocks, reinterpret_cast<int8_t*>(k_cache),
-                     reinterpret_cast<int8_t*>(v_cache), k_scale, v_scale, true, stream);
+                     reinterpret_cast<int8_t*>(v_cache), k_scale, v_scale, kv8::kFmtFp8, stream);
 }
 
 int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
@@ -182,6 +182,15 @@ int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
   return r == 0 ? KV8_OK : KV8_ERR_HIP;
 }
 
+int kv8_quant_append_int4(const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int64_t num_blocks, uint8_t* k_cache,
+                          uint8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale, void* stream) {
+  return append_impl(k_new, v_new, slot_mapping, n_tokens, num_kv_heads, head_dim, block_size,
+                     num_blocks, reinterpret_cast<int8_t*>(k_cache),
+                     reinterpret_cast<int8_t*>(v_cache), k_scale, v_scale, kv8::kFmtInt4, stream);
+}
+
 size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int tokens_per_split) {
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
@@ -203,7 +212,7 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
   return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, false, nullptr, nullptr, stream);
+                     workspace_bytes, tokens_per_split, kv8::kFmtInt8, nullptr, nullptr, stream);
 }
 
 int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
@@ -218,7 +227,7 @@ int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, true, nullptr, nullptr, stream);
+                     workspace_bytes, tokens_per_split, kv8::kFmtFp8, nullptr, nullptr, stream);
 }
 
 int paged_decode_attn_kv8_append(const void* q, int q_dtype, const uint16_t* k_new,
@@ -234,7 +243,22 @@ int paged_decode_attn_kv8_append(const void* q, int q_dtype, const uint16_t* k_n
   return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, false, k_new, v_new, stream);
+                     workspace_bytes, tokens_per_split, kv8::kFmtInt8, k_new, v_new, stream);
+}
+
+int paged_decode_attn_int4kv(const void* q, int q_dtype, const uint8_t* k_cache,
+                             const uint8_t* v_cache, const uint16_t* k_scale,
+                             const uint16_t* v_scale, int64_t num_blocks,
+                             const int32_t* block_table, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int batch,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             float sm_scale, float* out, void* workspace,
+                             size_t workspace_bytes, int tokens_per_split, void* stream) {
+  return decode_impl(q, q_dtype, reinterpret_cast<const int8_t*>(k_cache),
+                     reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
+                     block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
+                     num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                     workspace_bytes, tokens_per_split, kv8::kFmtInt4, nullptr, nullptr, stream);
 }
 
 int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache,
@@ -293,7 +317,7 @@ int paged_prefill_chunk_attn_kv8(const uint16_t* q, const int32_t* q_start_loc,
   return prefill_impl(q, q_start_loc, total_q, max_q_len, k_cache, v_cache, k_scale, v_scale,
                       num_blocks, block_table, max_blocks_per_seq, context_lens,
                       max_context_len, batch, num_q_heads, num_kv_heads, head_dim, block_size,
-                      sm_scale, out, workspace, workspace_bytes, false, stream);
+                      sm_scale, out, workspace, workspace_bytes, kv8::kFmtInt8, stream);
 }
 
 int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc,
@@ -310,7 +334,7 @@ int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc
                       reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
                       block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
                       num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                      workspace_bytes, true, stream);
+                      workspace_bytes, kv8::kFmtFp8, stream);
 }
 
 }  // extern "C"

@@ -92,14 +92,18 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
 
   const float ks = fp16_scale<C>(ka);
   const float vs = fp16_scale<C>(va);
-  const uint2 kc = quantise8<C>(kx, ks);
-  const uint2 vc = quantise8<C>(vx, vs);
-
   const int64_t blk = slot / kBlock;
   const int off = (int)(slot % kBlock);
   const int64_t line = (blk * num_kv_heads + h) * kBlock + off;   // (block, head, slot)
-  *reinterpret_cast<uint2*>(k_cache + line * D + part * 8) = kc;
-  *reinterpret_cast<uint2*>(v_cache + line * D + part * 8) = vc;
+  if constexpr (C::kBits == 4) {
+    *reinterpret_cast<uint32_t*>(k_cache + line * (D / 2) + part * 4) =
+        quantise8_nibbles<C>(kx, ks);
+    *reinterpret_cast<uint32_t*>(v_cache + line * (D / 2) + part * 4) =
+        quantise8_nibbles<C>(vx, vs);
+  } else {
+    *reinterpret_cast<uint2*>(k_cache + line * D + part * 8) = quantise8<C>(kx, ks);
+    *reinterpret_cast<uint2*>(v_cache + line * D + part * 8) = quantise8<C>(vx, vs);
+  }
   if (part == 0) {
     k_scale[line] = __builtin_bit_cast(uint16_t, (_Float16)ks);
     v_scale[line] = __builtin_bit_cast(uint16_t, (_Float16)vs);
@@ -132,10 +136,14 @@ void launch_append_fmt(const uint16_t* k_new, const uint16_t* v_new, const int32
 int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                         const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
                         int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
-                        uint16_t* k_scale, uint16_t* v_scale, bool fp8, hipStream_t stream) {
+                        uint16_t* k_scale, uint16_t* v_scale, int fmt, hipStream_t stream) {
   const int64_t n_rows = n_tokens * num_kv_heads;
   const int64_t num_slots = num_blocks * kBlock;
-  if (fp8)
+  if (fmt == kFmtInt4)
+    launch_append_fmt<CodesInt4, false>(k_new, v_new, slot_mapping, n_rows, num_kv_heads,
+                                        head_dim, num_slots, k_cache, v_cache, k_scale, v_scale,
+                                        nullptr, nullptr, 0, stream);
+  else if (fmt == kFmtFp8)
     launch_append_fmt<CodesFp8, false>(k_new, v_new, slot_mapping, n_rows, num_kv_heads,
                                        head_dim, num_slots, k_cache, v_cache, k_scale, v_scale,
                                        nullptr, nullptr, 0, stream);

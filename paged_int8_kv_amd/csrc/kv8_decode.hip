@@ -105,20 +105,26 @@ __host__ __device__ inline SmemLayout smem_layout(int split_tokens, int G, int D
 template <int NDW> struct RowT;
 template <> struct RowT<4> { using type = uint4; };
 template <> struct RowT<2> { using type = uint2; };
+template <> struct RowT<1> { using type = uint32_t; };
 
 __device__ __forceinline__ uint32_t dword(const uint4& r, int k) {
   return k == 0 ? r.x : k == 1 ? r.y : k == 2 ? r.z : r.w;
 }
 __device__ __forceinline__ uint32_t dword(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
+__device__ __forceinline__ uint32_t dword(const uint32_t& r, int) { return r; }
 
 template <int D, int G, bool QF32, class C>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   constexpr int CPL = D / 8;    // channels (= code bytes) per lane per token
-  constexpr int NDW = CPL / 4;  // dwords per lane per token
+  constexpr int NDW = CPL / 4;  // dwords per lane per token of 8-bit codes (and of bf16 q / 2)
   constexpr int NP = CPL / 2;   // fp16 pairs per lane per token
+  constexpr int NIB = C::kBits == 4;              // 4-bit codes: 8 per dword
+  constexpr int NDC = NIB ? CPL / 8 : NDW;        // code dwords per lane per token
+  constexpr int RB = NIB ? D / 2 : D;             // code bytes per cache row
   constexpr int NV = (2 * G >= 8) ? (2 * G) / 8 : 1;   // logits stored per lane
   constexpr int M = G * CPL;    // accumulators per lane
-  using Row = typename RowT<NDW>::type;
+  using QRow = typename RowT<NDW>::type;         // CPL / 2 bf16 q values
+  using Row = typename RowT<NDC>::type;          // the lane's codes of one token
 
   extern __shared__ __align__(16) unsigned char smem[];
   const SmemLayout L = smem_layout(a.split_tokens, G, D);
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   // does) and stores them before its passes read the block back.  Wave 0's
   // stores complete (vmcnt 0) before the barrier below, and every later load
   // of the workgroup comes after that barrier on the same CU.
-  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == 0) {
+  if (C::kBits == 8 && a.k_new != nullptr && split == it.nsplit - 1 && wave == 0) {
     constexpr int LPR = D / 8;          // lanes per row, 8 values each
     if (lane < LPR) {
       const int p = ctx - 1;
@@ -206,9 +212,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         }
       } else {
         // CPL bf16 values = two Rows of NDW dwords
-        const Row* qp = reinterpret_cast<const Row*>(
+        const QRow* qp = reinterpret_cast<const QRow*>(
             static_cast<const uint16_t*>(a.q) + qrow0 + (int64_t)h * D);
-        const Row r = qp[0], r2 = qp[1];
+        const QRow r = qp[0], r2 = qp[1];
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
           const uint32_t w = dword(r, k), w2 = dword(r2, k);
@@ -227,7 +233,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
       float qsum = 0.0f;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const float a0 = ldexpf(x[2 * p], -e), a1 = ldexpf(x[2 * p + 1], -e);
+        // pair p: channels (2p, 2p+1) for byte codes; for 4-bit codes the
+        // channels (j, j+4) of 8-channel group p/4, j = p%4, the pairs the
+        // nibble extraction produces
+        const int c0 = NIB ? 8 * (p / 4) + p % 4 : 2 * p, c1 = NIB ? c0 + 4 : 2 * p + 1;
+        const float a0 = ldexpf(x[c0], -e), a1 = ldexpf(x[c1], -e);
         const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
         qh[h][p] = half2_t{h0, h1};
         qsum += (float)h0 + (float)h1;
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         }
       }
       cz[h] = ldexpf(a.qk_scale_log2, e);
-      nqb[h] = -kCodeBias * qsum;
+      nqb[h] = -C::kBias * qsum;
     }
   }
   // per-lane constants of the logits this lane stores after the reduction
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     const int id = __builtin_amdgcn_readlane(mine, i);
     return ((int64_t)id * Hkv + g) * kBlock;
   };
-  const int lane_row = slot * D + chunk * CPL;   // this lane's byte offset in a block
+  const int lane_row = slot * RB + chunk * (RB / 8);   // this lane's byte offset in a block
 
   // ---- pass 1: logits ----------------------------------------------------
   float mloc[NV];
@@ -276,9 +286,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     const int tok_row = slot + 8 * tk;            // the token whose logits this lane stores
     auto issue = [&](int s, int i) {
       const int64_t row0 = row0_of(i);
-      const int8_t* p = a.k_cache + row0 * D + lane_row;
+      const int8_t* p = a.k_cache + row0 * RB + lane_row;
       r0[s] = *reinterpret_cast<const Row*>(p);
-      r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
+      r1[s] = *reinterpret_cast<const Row*>(p + 8 * RB);
       ksc16[s] = a.k_scale[row0 + tok_row];
       vsc16[s] = a.v_scale[row0 + tok_row];
     };
@@ -299,6 +309,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           float S[2 * G];
 #pragma unroll
           for (int h = 0; h < G; ++h) S[h] = S[G + h] = C::kBiased ? nqb[h] : 0.0f;
+          if constexpr (NIB) {
+#pragma unroll
+            for (int k = 0; k < NDC; ++k) {
+              const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const half2_t a0 = C::nib_pair(x0, j), a1 = C::nib_pair(x1, j);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                  S[h] = fdot2(qh[h][4 * k + j], a0, S[h]);
+                  S[G + h] = fdot2(qh[h][4 * k + j], a1, S[G + h]);
+                  if constexpr (QF32) {
+                    S[h] = fdot2(ql[h][4 * k + j], a0, S[h]);
+                    S[G + h] = fdot2(ql[h][4 * k + j], a1, S[G + h]);
+                  }
+                }
+              }
+            }
+          } else {
 #pragma unroll
           for (int k = 0; k < NDW; ++k) {
             const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
@@ -317,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
                 S[G + h] = fdot2(ql[h][2 * k + 1], b1, S[G + h]);
               }
             }
+          }
           }
           float R[NV];
           reduce_scatter8<G>(S, R, chunk);
@@ -340,9 +370,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   // while the workgroup finishes the logits and builds the weights.
   Row r0[kPf], r1[kPf];
   auto issue_v = [&](int s, int i) {
-    const int8_t* p = a.v_cache + row0_of(i) * D + lane_row;
+    const int8_t* p = a.v_cache + row0_of(i) * RB + lane_row;
     r0[s] = *reinterpret_cast<const Row*>(p);
-    r1[s] = *reinterpret_cast<const Row*>(p + 8 * D);
+    r1[s] = *reinterpret_cast<const Row*>(p + 8 * RB);
   };
   if (nmine > 0) {
 #pragma unroll
@@ -409,6 +439,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const uint32_t* src = s_pp + ((wave + i * kWaves) * 8 + slot) * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) wp[h] = __builtin_bit_cast(half2_t, src[h]);
+        if constexpr (NIB) {
+          // bytes 0,1 (channels 8k..8k+3) and 2,3 (8k+4..8k+7) of the two
+          // tokens side by side, so nibble pairs are (token t, token t+8)
+#pragma unroll
+          for (int k = 0; k < NDC; ++k) {
+            const uint32_t u0 = dword(w0, k), u1 = dword(w1, k);
+            const uint32_t lo = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
+            const uint32_t hi = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const half2_t fl = C::nib_pair(lo, j), fh = C::nib_pair(hi, j);
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                acc[h * CPL + 8 * k + j] = fdot2(wp[h], fl, acc[h * CPL + 8 * k + j]);
+                acc[h * CPL + 8 * k + 4 + j] = fdot2(wp[h], fh, acc[h * CPL + 8 * k + 4 + j]);
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
           const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
@@ -423,6 +472,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
             acc[h * CPL + 4 * k + 3] = fdot2(wp[h], f3, acc[h * CPL + 4 * k + 3]);
           }
         }
+        }
       }
       issue_v(s, min(i + kPf, last));
     }
@@ -432,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   __syncthreads();
   finish_split<G, D, kThreads, kWaves, C::kBiased>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
 }
 
 template <int D, int G, bool QF32, class C>
@@ -509,7 +559,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, bool fp8, const uint16_t* k_new,
+                  void* workspace, const DecodePlan& plan, int fmt, const uint16_t* k_new,
                   const uint16_t* v_new, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   SplitArgs a;
@@ -537,7 +587,8 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.qk_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   bool ok;
-  if (fp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
+  if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
+  else if (fmt == kFmtInt4) ok = dispatch_fmt<CodesInt4>(head_dim, q_f32, G, a, batch, stream);
   else ok = dispatch_fmt<CodesInt8>(head_dim, q_f32, G, a, batch, stream);
   if (!ok) return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

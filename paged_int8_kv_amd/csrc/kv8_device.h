@@ -142,7 +142,9 @@ __device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
 // on the e4m3 grid and saturate to +-448, the sign of a zero kept.
 // ---------------------------------------------------------------------------
 struct CodesInt8 {
+  static constexpr int kBits = 8;
   static constexpr bool kBiased = true;
+  static constexpr float kBias = kCodeBias;
   static constexpr float kQmax = 127.0f;
   __device__ static uint32_t pre(uint32_t u) { return u ^ kXor80; }
   __device__ static half2_t lo(uint32_t x) { return biased_pair_lo(x); }
@@ -159,7 +161,9 @@ struct CodesInt8 {
 };
 
 struct CodesFp8 {
+  static constexpr int kBits = 8;
   static constexpr bool kBiased = false;
+  static constexpr float kBias = 0.0f;
   static constexpr float kQmax = 448.0f;
   __device__ static uint32_t pre(uint32_t u) { return u; }
   __device__ static half2_t lo(uint32_t x) {
@@ -183,6 +187,32 @@ struct CodesFp8 {
       c = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
     }
     return sign | c;
+  }
+};
+
+// INT4: symmetric codes -7..7 (the INT8 recipe with 7 in place of 127), two
+// per byte as 4-bit two's complement, element 2i in the low nibble of byte
+// i.  A dword holds 8 codes.  Flipping each nibble's sign bit (xor 0x8)
+// gives u = c + 8, and u under the fp16 pattern 0x6400 is the value
+// 1024 + u = c + 1032 exactly.  nib_pair(x, j) makes the fp16 pair of
+// nibbles j and j + 4 of the (already flipped) dword x.
+struct CodesInt4 {
+  static constexpr int kBits = 4;
+  static constexpr bool kBiased = true;
+  static constexpr float kBias = 1032.0f;
+  static constexpr float kQmax = 7.0f;
+  __device__ static uint32_t pre(uint32_t u) { return u ^ 0x88888888u; }
+  __device__ static half2_t nib_pair(uint32_t x, int j) {
+    return __builtin_bit_cast(half2_t, ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
+  }
+  __device__ static half2_t exact(half2_t p) {
+    const half2_t bias = {(_Float16)kBias, (_Float16)kBias};
+    return p - bias;
+  }
+  __device__ static uint32_t code(float x, float s) {
+    float q = __builtin_rintf(x / s);                 // IEEE divide, ties to even
+    q = fminf(fmaxf(q, -7.0f), 7.0f);
+    return (uint32_t)((int32_t)q) & 0xFu;
   }
 };
 
@@ -218,6 +248,17 @@ __device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
     for (int i = 0; i < 4; ++i) w1 |= C::code(x[4 + i], s) << (8 * i);
   }
   return make_uint2(w0, w1);
+}
+
+// Eight 4-bit codes of one lane, packed: code i in bits 4i .. 4i+3.
+template <class C>
+__device__ __forceinline__ uint32_t quantise8_nibbles(const float (&x)[8], float s) {
+  uint32_t w = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= C::code(x[i], s) << (4 * i);
+  }
+  return w;
 }
 
 __device__ __forceinline__ void unpack8(uint4 raw, float (&x)[8], float& amax) {

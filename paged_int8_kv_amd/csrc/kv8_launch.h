@@ -1,6 +1,7 @@
 // Internal launchers of libkv8: called by the C ABI layer (kv8_api.cpp)
-// after host validation.  `fp8` selects the FP8 (e4m3) code format of the
-// cache instead of INT8; caches are passed as bytes either way.  A
+// after host validation.  `fmt` selects the code format of the cache
+// (kFmtInt8, kFmtFp8 = e4m3, kFmtInt4 = packed nibbles); caches are passed
+// as bytes either way.  A
 // non-null k_new/v_new makes launch_decode append each sequence's newest
 // token (position context_lens[b] - 1) before attending.  Each returns 0 on
 // success and -1 when the HIP runtime reports a launch error.
@@ -12,10 +13,12 @@
 
 namespace kv8 {
 
+enum : int { kFmtInt8 = 0, kFmtFp8 = 1, kFmtInt4 = 2 };
+
 int launch_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                         const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
                         int head_dim, int64_t num_blocks, int8_t* k_cache, int8_t* v_cache,
-                        uint16_t* k_scale, uint16_t* v_scale, bool fp8, hipStream_t stream);
+                        uint16_t* k_scale, uint16_t* v_scale, int fmt, hipStream_t stream);
 
 int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                              const int32_t* slot_mapping, const int32_t* positions,
@@ -42,7 +45,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
                   const int32_t* block_table, int max_blocks_per_seq,
                   const int32_t* context_lens, int ctx_cap, int batch, int num_q_heads,
                   int num_kv_heads, int head_dim, float sm_scale, float* out,
-                  void* workspace, const DecodePlan& plan, bool fp8, const uint16_t* k_new,
+                  void* workspace, const DecodePlan& plan, int fmt, const uint16_t* k_new,
                   const uint16_t* v_new, hipStream_t stream);
 
 int launch_decode_bf16kv(const void* q, bool q_f32, const uint16_t* k_cache,
@@ -57,6 +60,6 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,
                    int max_blocks_per_seq, const int32_t* context_lens, int ctx_cap, int batch,
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
-                   bool fp8, hipStream_t stream);
+                   int fmt, hipStream_t stream);
 
 }  // namespace kv8

@@ -597,7 +597,7 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    const uint16_t* v_scale, int64_t num_blocks, const int32_t* block_table,
                    int max_blocks_per_seq, const int32_t* context_lens, int ctx_cap, int batch,
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
-                   bool fp8, hipStream_t stream) {
+                   int fmt, hipStream_t stream) {
   PrefillArgs a;
   a.q = q;
   a.q_start_loc = q_start_loc;
@@ -616,6 +616,8 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
   a.num_kv_heads = num_kv_heads;
   a.sm_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
+  if (fmt == kFmtInt4) return -2;
+  const bool fp8 = fmt == kFmtFp8;
   if (head_dim == 128) return fp8 ? launch_d<128, CodesFp8>(a, G, batch, max_q_len, stream)
                                   : launch_d<128, CodesInt8>(a, G, batch, max_q_len, stream);
   if (head_dim == 64) return fp8 ? launch_d<64, CodesFp8>(a, G, batch, max_q_len, stream)

@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(Bf16Args a) {
   __syncthreads();
   finish_split<G, D, kThreads, kWaves, false>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, 0.0f);
 }
 
 template <int D, int G, bool QF32>

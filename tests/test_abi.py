@@ -235,3 +235,19 @@ def rope_append(**kw):
 ])
 def test_rope_append_validation(kw, expected):
     assert rope_append(**kw) == expected
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k_new=None), dict(kc=None), dict(vs=None), dict(n=-1), dict(nb=0), dict(d=96),
+    dict(bs=32), dict(kc=MIS), dict(n=0),
+])
+def test_int4_append_validation_matches_int8(kw):
+    assert append(fn="kv8_quant_append_int4", **kw) == append(**kw)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(ks=None), dict(b=0), dict(hq=30), dict(hq=24), dict(d=256), dict(dt=7),
+    dict(tps=100), dict(kc=MIS), dict(ws=None), dict(wsb=16),
+])
+def test_int4_decode_validation_matches_int8(kw):
+    assert decode(fn="paged_decode_attn_int4kv", **kw) == decode(**kw)
