@@ -99,8 +99,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or KV head with no exchange; see the "
-              "design notes)", file=sys.stderr)
+              "(this build runs on one GPU; the decode path would shard by sequence or by "
+              "KV head, with no exchange inside attention)", file=sys.stderr)
         sys.exit(2)
     import torch
     from paged_int8_kv_amd import binding as B

@@ -25,7 +25,7 @@ Sources are the pages collected for this method:
   FP16/INT8 while attention accumulates in FP32.
 
 The pages do not spell out the quantiser's arithmetic.  The readings taken
-here (all listed with reasons in the design notes of the repository):
+here:
 
 1. one scale per (token, KV head), separately for K and V;
 2. scale s = fp16_rne(fp32_rne(absmax / 127)), gradual underflow, an fp16
@@ -295,7 +295,7 @@ def paged_decode_bf16(q, k_cache_bits, v_cache_bits, block_table, context_lens,
 # FP8 (e4m3) KV cache.  "KV Cache 优化全景解析" section 7.4: the KV cache kept
 # as FP8, e4m3 (4 exponent bits, 3 mantissa bits, the more precise of the two
 # formats) with quantisation scales; section 11.3: about half the bytes of a
-# 16-bit cache.  Readings (listed in the design notes): the OCP e4m3 format
+# 16-bit cache.  Readings taken: the OCP e4m3 format
 # (bias 7, subnormals, largest finite 448, no infinity); one fp16 scale per
 # (token, KV head) as for INT8, s = fp16_rne(fp32_rne(absmax / 448));
 # codes = e4m3 round-to-nearest-even of the fp32 quotient x / s, saturated
@@ -477,7 +477,7 @@ def rope_quant_append(k_pre, v_new, positions, cos_sin, slot_mapping, k_cache, v
 # per element in the KV-size formula, and the KV-cache optimisation page of
 # garden.houmin.site (section 2.2.2, directions for optimisation) lists
 # compressing the cache from FP16 to INT8 or INT4.
-# Readings (listed in the design notes): the INT8 recipe with 7 in place of
+# Readings taken: the INT8 recipe with 7 in place of
 # 127, i.e. one fp16 scale per (token, KV head), s = fp16_rne(fp32_rne(
 # absmax / 7)), codes = clamp(round_half_even(fp32(x / s)), -7, 7), all zero
 # when s == 0; two codes per byte as 4-bit two's complement, element 2i in

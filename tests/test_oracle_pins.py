@@ -6,7 +6,7 @@ brute force on tiny inputs, against torch's scaled_dot_product_attention in
 fp64 (the dense, non-paged, MHA special case), against closed forms
 (single token, identical keys) and against invariants (block permutation,
 batch order, causal locality).  The KV-size closed form reproduces the
-numbers the survey page prints.
+numbers the overview page ("KV Cache 优化全景解析") prints.
 """
 import json
 import math
@@ -112,7 +112,7 @@ def dense_dequant(case, b, which):
 
 
 # ---------------------------------------------------------------------------
-# KV-size closed form (survey page, sections 2.3 / 3.3 / 11.4)
+# KV-size closed form ("KV Cache 优化全景解析", sections 2.3 / 3.3 / 11.4)
 # ---------------------------------------------------------------------------
 def test_kv_size_printed_tables():
     g = json.load(open(os.path.join(GOLDEN, "kv_size_tables.json")))
