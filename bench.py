@@ -36,7 +36,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--tokens-per-split", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-steps", type=int, default=4)
+    p.add_argument("--cpu-steps", type=int, default=24,
+                   help="oracle steps timed on the host (about 0.5 s each on 16 cores)")
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--fp8-steps", type=int, default=1,
                    help="0 skips the FP8 (e4m3) and INT4 cache lines")
