@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=20)
     p.add_argument("--fp8-steps", type=int, default=1,
                    help="0 skips the FP8 (e4m3) and INT4 cache lines")
+    p.add_argument("--sweep-layers", type=int, default=80,
+                   help="layers of the Llama-3-70B-shaped decode sweep (0 skips it)")
     p.add_argument("--budget-steps", type=int, default=10,
                    help="decode calls timed per side of the 258K equal-budget comparison "
                         "(0 skips it)")
@@ -282,6 +284,8 @@ def main():
             result["fp8_kv"]["prefill"] = bench_prefill(args, dev, fp8=True)
     if args.fp8_steps > 0:
         result["int4_kv"] = {"decode": bench_code_decode(args, dev, case, "int4")}
+    if args.sweep_layers > 0:
+        result["llama70b_sweep"] = bench_sweep70b(args, dev)
     if args.budget_steps > 0:
         result["equal_budget_258k"] = bench_equal_budget(args, dev)
     if not args.no_cpu_baseline:
@@ -405,6 +409,63 @@ def bench_code_decode(args, dev, case, fmt):
                         "cache, decode launches back to back", "decode_us": round(us, 2),
             "bytes_per_launch": nbytes, "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "kv_tokens_per_s": round(float(ctx.sum()) / (us * 1e-6), 1)}
+
+
+def bench_sweep70b(args, dev):
+    """The Llama-3-70B-shaped decode sweep: one decode call per layer, all
+    layers back to back as one model step launches them (64 sequences of
+    512..16384 tokens per layer, 64 query heads over 8 KV heads, d=128,
+    K/V drawn on the device and quantised by the append kernel; about 49 GB
+    of cache for 80 layers, far beyond the last-level cache)."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    from paged_int8_kv_amd import workloads as W
+    layers = []
+    kv_bytes = 0
+    tokens = 0
+    for layer in range(args.sweep_layers):
+        g = W.llama70b_layer_device(layer, dev)
+        cache = B.alloc_cache(g["num_blocks"], 8, 128, dev)
+        B.kv8_quant_append(g["k"], g["v"], torch.from_numpy(g["slot_mapping"]).to(dev), *cache)
+        lens = g["context_lens"]
+        layers.append((g["q"], cache, torch.from_numpy(g["block_table"]).to(dev),
+                       torch.from_numpy(lens).to(dev), int(lens.max())))
+        kv_bytes += decode_bytes(lens, 8, 128, 64, 2)
+        tokens += int(lens.astype(np.int64).sum())
+        del g
+    torch.cuda.synchronize()
+    max_ctx = max(x[4] for x in layers)
+    ws = torch.zeros(B.kv8_decode_workspace_size(64, 64, 8, 128, max_ctx), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((64, 64, 128), dtype=torch.float32, device=dev)
+
+    def sweep():
+        for q, cache, table, lens, m in layers:
+            B.paged_decode_attn_kv8(q, *cache, table, lens, m, out, ws)
+
+    for _ in range(3):
+        sweep()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sweep()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    del layers, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": f"Llama-3-70B-shaped decode sweep: {args.sweep_layers} layers back to "
+                        "back, B=64, Hq=64, Hkv=8, d=128, ctx ~ log-U[512,16384] per layer",
+            "ms_per_step": round(ms, 3),
+            "us_per_layer": round(ms * 1e3 / args.sweep_layers, 1),
+            "bytes_per_step": int(kv_bytes), "kv_gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "kv_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
 
 
 def bench_equal_budget(args, dev):
