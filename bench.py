@@ -35,6 +35,8 @@ def parse():
                    help="untimed steps first (the GPU clocks settle over ~100 ms)")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--tokens-per-split", type=int, default=0)
+    p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma"], default="auto",
+                   help="form of the INT8/FP8 decode kernel (auto: by group size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=24,
                    help="oracle steps timed on the host (about 0.5 s each on 16 cores)")
@@ -111,6 +113,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    B.kv8_set_decode_kernel({"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT,
+                             "mfma": B.DECODE_MFMA}[args.decode_kernel])
     if args.calibrate_copy:
         calibrate_copy(dev)
         return

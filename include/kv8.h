@@ -93,6 +93,25 @@ const char* kv8_status_string(int status);
 int kv8_version(void);
 
 /*
+ * kv8_set_decode_kernel - choose the form of the INT8 / FP8 decode kernel
+ * used by paged_decode_attn_kv8, paged_decode_attn_kv8_append and
+ * paged_decode_attn_fp8kv, for this process (all threads, all devices).
+ *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv;
+ *          KV8_DECODE_DOT  (1): the v_dot2 kernel;
+ *          KV8_DECODE_MFMA (2): the matrix-core kernel (logits and values
+ *          as 16x16 MFMA tiles over all G heads of a group at once).
+ * Both forms compute the same attention (same softmax algebra, same work
+ * split and merge); results agree within the attention tolerance, not
+ * bitwise.  The INT4 decode always uses the v_dot2 kernel.  Takes effect for
+ * launches issued after the call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED
+ * for another value (the setting is then unchanged).
+ */
+#define KV8_DECODE_AUTO 0
+#define KV8_DECODE_DOT 1
+#define KV8_DECODE_MFMA 2
+int kv8_set_decode_kernel(int which);
+
+/*
  * kv8_quant_append - quantise N new tokens' K and V and scatter them into
  * the paged cache (the quantise-on-write half of the KV8 method: "KV-Cache
  * 全栈优化系统" README, section 主要特性; slot addressing per the block

@@ -59,6 +59,8 @@ def load():
     lib.kv8_status_string.argtypes = [i32]
     lib.kv8_version.restype = i32
     lib.kv8_version.argtypes = []
+    lib.kv8_set_decode_kernel.restype = i32
+    lib.kv8_set_decode_kernel.argtypes = [i32]
     lib.kv8_quant_append.restype = i32
     lib.kv8_quant_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
     lib.kv8_rope_quant_append.restype = i32
@@ -94,6 +96,15 @@ def load():
     lib.paged_prefill_chunk_attn_fp8kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
     _lib = lib
     return lib
+
+
+DECODE_AUTO, DECODE_DOT, DECODE_MFMA = 0, 1, 2
+
+
+def kv8_set_decode_kernel(which):
+    """Choose the INT8/FP8 decode kernel form for this process:
+    DECODE_AUTO (by group size), DECODE_DOT (v_dot2) or DECODE_MFMA."""
+    _check(load().kv8_set_decode_kernel(int(which)), "kv8_set_decode_kernel")
 
 
 def status_string(status):

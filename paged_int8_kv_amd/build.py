@@ -22,7 +22,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libkv8.so")
 
 ARCH = "gfx950"
-SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_prefill.hip",
+SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_decode_mfma.hip",
+           "kv8_prefill.hip",
            "kvbf16_decode.hip"]
 
 # Packed fp32 VALU instructions are kept out of the code object: the
@@ -35,11 +36,14 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
+# Per-source extra flags.  The MFMA kernels keep their accumulators in
 # ordinary VGPRs: with the accumulator-register form the compiler copied all
-# 128 accumulators between register files on every key tile.
+# 128 prefill accumulators between register files on every key tile, and the
+# matrix-core decode needs 96 VGPRs in one file (5 waves per SIMD) against
+# 96 + 36 split over two (3 waves).
 EXTRA_FLAGS = {
     "kv8_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kv8_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 
 

@@ -143,6 +143,15 @@ const char* kv8_status_string(int status) {
 
 int kv8_version(void) { return kVersion; }
 
+int kv8_set_decode_kernel(int which) {
+  if (which != KV8_DECODE_AUTO && which != KV8_DECODE_DOT && which != KV8_DECODE_MFMA)
+    return KV8_ERR_UNSUPPORTED;
+  kv8::set_decode_kernel(which == KV8_DECODE_DOT    ? kv8::kDecodeKernelDot
+                         : which == KV8_DECODE_MFMA ? kv8::kDecodeKernelMfma
+                                                    : kv8::kDecodeKernelAuto);
+  return KV8_OK;
+}
+
 int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                      const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,

@@ -52,32 +52,7 @@ constexpr int kWaves = 4;
 constexpr int kPf = 4;        // blocks in flight per wave and pass
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct SplitArgs {
-  const void* q;
-  const int8_t* k_cache;
-  const int8_t* v_cache;
-  const uint16_t* k_scale;
-  const uint16_t* v_scale;
-  const uint16_t* k_new;   // bf16 [B, Hkv, D] newest token per sequence, or null
-  const uint16_t* v_new;
-  const int32_t* block_table;
-  const int32_t* context_lens;
-  float* out;
-  float* o_part;
-  float* lse_part;
-  unsigned* counters;
-  int64_t num_blocks;
-  int max_blocks_per_seq;
-  int ctx_cap;
-  int num_q_heads;
-  int num_kv_heads;
-  int split_tokens;
-  int n_split;
-  int batch;
-  int period;        // workgroups per dispatch round (the CU count)
-  int snake_rounds;  // rounds resident at once (workgroups per CU)
-  float qk_scale_log2;
-};
+
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
@@ -161,37 +136,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     s_blk[tid] = (int)id;
   }
 
-  // ---- decode step with append: the newest token of the sequence sits at
-  // position ctx - 1, inside the last split, so that split's workgroup
-  // quantises the token's K and V rows of head g (as the append kernel
-  // does) and stores them before its passes read the block back.  Wave 0's
-  // stores complete (vmcnt 0) before the barrier below, and every later load
-  // of the workgroup comes after that barrier on the same CU.
-  if (C::kBits == 8 && a.k_new != nullptr && split == it.nsplit - 1 && wave == 0) {
-    constexpr int LPR = D / 8;          // lanes per row, 8 values each
-    if (lane < LPR) {
-      const int p = ctx - 1;
-      int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + p / kBlock];
-      id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-      const int64_t line = (id * Hkv + g) * kBlock + p % kBlock;
-      const int64_t src = ((int64_t)b * Hkv + g) * D + lane * 8;
-      float kx[8], vx[8], ka, va;
-      unpack8(*reinterpret_cast<const uint4*>(a.k_new + src), kx, ka);
-      unpack8(*reinterpret_cast<const uint4*>(a.v_new + src), vx, va);
-      ka = row_absmax<LPR>(ka);
-      va = row_absmax<LPR>(va);
-      const float ks = fp16_scale<C>(ka), vs = fp16_scale<C>(va);
-      *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.k_cache) + line * D + lane * 8) =
-          quantise8<C>(kx, ks);
-      *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.v_cache) + line * D + lane * 8) =
-          quantise8<C>(vx, vs);
-      if (lane == 0) {
-        const_cast<uint16_t*>(a.k_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)ks);
-        const_cast<uint16_t*>(a.v_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)vs);
-      }
-    }
-    wait_vmem();
-  }
+  // ---- decode step with append (the newest token, in the last split) ----
+  if (C::kBits == 8 && a.k_new != nullptr && split == it.nsplit - 1 && wave == 0)
+    append_newest<D, C>(a, b, g, ctx, lane);
 
   // ---- q of the G heads: this lane's d/8 channels as fp16 pairs ----------
   half2_t qh[G][NP];
@@ -519,7 +466,21 @@ bool dispatch_fmt(int head_dim, bool q_f32, int G, const SplitArgs& a, int batch
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+std::atomic<int> g_decode_kernel{kDecodeKernelAuto};
+
+// Automatic choice: the matrix-core kernel from four query heads per KV
+// head up, where the dot-product kernel's vector work per cache byte (G/2
+// v_dot2 issues per lane) outgrows the memory stream.
+bool use_mfma_decode(int G) {
+  const int k = g_decode_kernel.load(std::memory_order_relaxed);
+  if (k == kDecodeKernelDot) return false;
+  if (k == kDecodeKernelMfma) return true;
+  return G >= 4;
+}
+
 }  // namespace
+
+void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_order_relaxed); }
 
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                  int max_context_len, int tokens_per_split, DecodePlan* plan) {
@@ -587,7 +548,10 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.qk_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   bool ok;
-  if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
+  if (fmt != kFmtInt4 && use_mfma_decode(G)) {
+    a.period = a.snake_rounds = 0;
+    ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, stream);
+  } else if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
   else if (fmt == kFmtInt4) ok = dispatch_fmt<CodesInt4>(head_dim, q_f32, G, a, batch, stream);
   else ok = dispatch_fmt<CodesInt8>(head_dim, q_f32, G, a, batch, stream);
   if (!ok) return -2;

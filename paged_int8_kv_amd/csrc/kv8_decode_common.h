@@ -95,6 +95,76 @@ __device__ __forceinline__ void priority_by_remaining(int remaining_blocks) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
+// Arguments of the INT8 / FP8 / INT4 decode kernels (both the dot-product
+// and the matrix-core form).
+struct SplitArgs {
+  const void* q;
+  const int8_t* k_cache;
+  const int8_t* v_cache;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+  const uint16_t* k_new;   // bf16 [B, Hkv, D] newest token per sequence, or null
+  const uint16_t* v_new;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* out;
+  float* o_part;
+  float* lse_part;
+  unsigned* counters;
+  int64_t num_blocks;
+  int max_blocks_per_seq;
+  int ctx_cap;
+  int num_q_heads;
+  int num_kv_heads;
+  int split_tokens;
+  int n_split;
+  int batch;
+  int period;        // workgroups per dispatch round (the CU count)
+  int snake_rounds;  // rounds resident at once (workgroups per CU)
+  float qk_scale_log2;
+};
+
+// Decode step with append: the newest token of sequence b sits at position
+// ctx - 1, inside the sequence's last split, so that split's workgroup
+// quantises the token's K and V rows of KV head g (as the append kernel
+// does) and stores them before its passes read the block back.  Called by
+// one whole wave; the stores complete (vmcnt 0) before it returns, so every
+// load the workgroup issues after its next barrier sees the new codes.
+template <int D, class C>
+__device__ __forceinline__ void append_newest(const SplitArgs& a, int b, int g, int ctx,
+                                              int lane) {
+  constexpr int LPR = D / 8;          // lanes per row, 8 values each
+  if (lane < LPR) {
+    const int p = ctx - 1;
+    const int Hkv = a.num_kv_heads;
+    int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + p / kBlock];
+    id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+    const int64_t line = (id * Hkv + g) * kBlock + p % kBlock;
+    const int64_t src = ((int64_t)b * Hkv + g) * D + lane * 8;
+    float kx[8], vx[8], ka, va;
+    unpack8(*reinterpret_cast<const uint4*>(a.k_new + src), kx, ka);
+    unpack8(*reinterpret_cast<const uint4*>(a.v_new + src), vx, va);
+    ka = row_absmax<LPR>(ka);
+    va = row_absmax<LPR>(va);
+    const float ks = fp16_scale<C>(ka), vs = fp16_scale<C>(va);
+    *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.k_cache) + line * D + lane * 8) =
+        quantise8<C>(kx, ks);
+    *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.v_cache) + line * D + lane * 8) =
+        quantise8<C>(vx, vs);
+    if (lane == 0) {
+      const_cast<uint16_t*>(a.k_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)ks);
+      const_cast<uint16_t*>(a.v_scale)[line] = __builtin_bit_cast(uint16_t, (_Float16)vs);
+    }
+  }
+  wait_vmem();
+}
+
+// Matrix-core form of the INT8 / FP8 decode (kv8_decode_mfma.hip): launches
+// the split kernel for head dim D in {64, 128}, group size G in {1, 2, 4, 8}
+// and the given code format; false for a shape it does not serve.
+bool launch_decode_mfma(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
+                        hipStream_t stream);
+
 struct Item {
   int b;        // sequence, -1 past the last item
   int g;        // KV head

@@ -1,0 +1,415 @@
+// Matrix-core form of paged_decode_attn_kv8 / paged_decode_attn_fp8kv:
+// split-K flash-decoding over the paged INT8 (or FP8 e4m3) cache on gfx950,
+// with both contractions of a block on MFMA.
+//
+// Attention softmax(q K^T * sm_scale) V ("KV Cache 优化全景解析", section 2.1)
+// per GQA group (section 3.3) over K/V restored from INT8 codes and
+// per-token fp16 scales ("KV-Cache 全栈优化系统" README, section 主要特性),
+// fp32 softmax and accumulation ("大模型推理加速：KV Cache与vLLM技术解析",
+// section 4.1).  Work items, split spans, the two-pass softmax and the
+// in-launch log-sum-exp merge are those of the dot-product kernel
+// (kv8_decode.hip); only the per-block arithmetic differs.
+//
+// Why matrix cores here.  With G query heads per KV head, a 16-token block
+// is a [16 x d] x [d x G] product (logits) and a [G x 16] x [16 x d] product
+// (values).  As v_dot2 work every cache byte costs G/2 multiply-add issues
+// per lane, so at G = 8 the vector unit, not HBM, sets the pace.  One
+// 16x16 MFMA tile holds all G <= 16 heads at once: the columns past G are
+// idle, which costs nothing that the memory stream would notice.
+//
+// Pass 1 (logits), per block, v_mfma_f32_16x16x32_f16 with
+//   A = codes [token = lane % 16][8 channels of the lane's k group]
+//   B = q     [same 8 channels][head = lane % 16]   (zero past G)
+//   D[token 4*(lane/16) + r][head lane % 16], r = 0..3.
+// Lane l loads 16-byte pieces of the row of token l % 16 at channel
+// offsets 64u + 16*(l/16); MFMA j uses the 8 channels 64(j/2) + 16(l/16) +
+// 8(j%2) ... + 7 on both sides, so A and B agree on every k slot.
+//
+// Pass 2 (values), per block, v_mfma_f32_16x16x16_f16 with
+//   A = codes [channel row m = lane % 16][tokens 4*(lane/16) .. + 3]
+//   B = w     [tokens 4*(lane/16) .. + 3][head = lane % 16]
+//   tile j (j < d/16) holds channel (d/16)*m + j, so lane l reads d/16
+//   contiguous bytes of each of the 4 token rows 4*(l/16) .. + 3 (one wave
+//   load instruction covers 4 whole 128-byte rows).
+//   D[row 4*(lane/16) + r][head lane % 16] = O[head][(d/16)(4(l/16)+r) + j].
+//
+// INT8 codes enter as the biased fp16 values c + 1152 (one byte permute per
+// pair, kv8_device.h); the bias is removed from the logits by starting the
+// accumulator at minus 1152 * sum(q_h) and from the outputs by 1152 * the sum
+// of the fp16 weights.  FP8 codes become exact fp16 by one hardware convert
+// per pair.  q enters as fp16 after an exact per-head power-of-two rescale;
+// an fp32 q is split into a high and a low fp16 part (two MFMAs).
+#include "kv8_decode_common.h"
+#include "kv8_device.h"
+#include "kv8_launch.h"
+
+namespace kv8 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kPf = 4;        // blocks in flight per wave and pass
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__host__ __device__ constexpr int align16m(int x) { return (x + 15) & ~15; }
+
+struct MSmem {
+  int blk_off, z_off, vs_off, w_off, red_off, flag_off, total;
+};
+
+// LDS of one workgroup: block ids, logits [token][G] (reused for the
+// cross-wave output sum [kWaves][G][D]), v scales per token, fp16 weights
+// [block][G][16 tokens], per-head scalars, the last-workgroup flag.
+__host__ __device__ inline MSmem msmem_layout(int split_tokens, int G, int D) {
+  MSmem L{};
+  const int zbytes = split_tokens * G * 4;
+  const int finbytes = kWaves * G * D * 4;
+  L.blk_off = 0;
+  L.z_off = align16m((split_tokens / kBlock) * 4);
+  L.vs_off = L.z_off + align16m(zbytes > finbytes ? zbytes : finbytes);
+  L.w_off = L.vs_off + align16m(split_tokens * 2);
+  L.red_off = L.w_off + align16m(split_tokens * G * 2);
+  L.flag_off = L.red_off + align16m(3 * kWaves * G * 4);
+  L.total = L.flag_off + 16;
+  return L;
+}
+
+__device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
+  const half4_t lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const half4_t hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ half4_t cat4(half2_t a, half2_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3);
+}
+__device__ __forceinline__ uint32_t dw(const uint4& r, int k) {
+  return k == 0 ? r.x : k == 1 ? r.y : k == 2 ? r.z : r.w;
+}
+
+template <int NDW> struct VRowT;
+template <> struct VRowT<2> { using type = uint2; };
+template <> struct VRowT<1> { using type = uint32_t; };
+__device__ __forceinline__ uint32_t dw(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
+__device__ __forceinline__ uint32_t dw(const uint32_t& r, int) { return r; }
+
+template <int D, int G, bool QF32, class C>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
+  static_assert(C::kBits == 8, "byte codes");
+  static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
+  constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block
+  constexpr int NKM = D / 32;     // logit MFMAs per block (per q part)
+  constexpr int NVT = D / 16;     // value tiles per block (= bytes per V row piece)
+  constexpr int NVD = NVT / 4;    // dwords of a lane's V row piece
+  using VRow = typename VRowT<NVD>::type;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const MSmem L = msmem_layout(a.split_tokens, G, D);
+  int* s_blk = reinterpret_cast<int*>(smem + L.blk_off);
+  float* s_z = reinterpret_cast<float*>(smem + L.z_off);
+  float* s_fin = s_z;
+  uint16_t* s_vs = reinterpret_cast<uint16_t*>(smem + L.vs_off);
+  _Float16* s_w = reinterpret_cast<_Float16*>(smem + L.w_off);
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const Item it = locate_item(a.context_lens, a.batch, a.ctx_cap, a.num_kv_heads,
+                              a.split_tokens, a.period, a.snake_rounds, lane);
+  const int b = it.b, g = it.g, split = it.split;
+  if (b < 0) return;                           // uniform: past the item list
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15;                    // token (pass 1 A) / head (B, D) / channel row
+  const int q4 = lane >> 4;                    // k group
+  const int64_t bh0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
+
+  int ctx = a.context_lens[b];
+  ctx = min(max(ctx, 0), a.ctx_cap);
+  if (ctx == 0) {                              // uniform: empty context, zero output
+    for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
+    return;
+  }
+  const Span sp = split_span(it, ctx);
+  const int nblk = sp.nblk, jb0 = sp.jb0, ntok = sp.ntok;
+  const int Hkv = a.num_kv_heads;
+
+  if (tid < nblk) {
+    int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + tid];
+    id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+    s_blk[tid] = (int)id;
+  }
+  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == 0)
+    append_newest<D, C>(a, b, g, ctx, lane);
+
+  // ---- q of head hl as the B operand of the logit MFMAs ------------------
+  half8_t qb[NKM], qlo[QF32 ? NKM : 1];
+  float cz, nqb;
+  {
+    const bool live = hl < G;
+    const int64_t qrow = (bh0 + (live ? hl : 0)) * D;
+    float x[NKM][8];
+#pragma unroll
+    for (int j = 0; j < NKM; ++j) {
+      const int c0 = 64 * (j / 2) + 16 * q4 + 8 * (j % 2);
+      if constexpr (QF32) {
+        const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + c0);
+        const float4 u = qp[0], v = qp[1];
+        x[j][0] = u.x; x[j][1] = u.y; x[j][2] = u.z; x[j][3] = u.w;
+        x[j][4] = v.x; x[j][5] = v.y; x[j][6] = v.z; x[j][7] = v.w;
+      } else {
+        const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow + c0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = dw(r, k);
+          x[j][2 * k] = __builtin_bit_cast(float, w << 16);
+          x[j][2 * k + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[j][i] = live ? x[j][i] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NKM; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[j][i]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    // power-of-two shift bringing the head's largest |q| into [2^14, 2^15)
+    const int e = m > 0.0f ? ilogbf(m) - 14 : 0;
+    float qsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NKM; ++j) {
+      _Float16 hv[8], lv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s = ldexpf(x[j][i], -e);
+        hv[i] = (_Float16)s;
+        qsum += (float)hv[i];
+        if constexpr (QF32) {
+          lv[i] = (_Float16)(s - (float)hv[i]);
+          qsum += (float)lv[i];
+        }
+      }
+      qb[j] = half8_t{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+      if constexpr (QF32) qlo[j] = half8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
+    }
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+    cz = ldexpf(a.qk_scale_log2, e);
+    nqb = -C::kBias * qsum;
+  }
+  __syncthreads();   // s_blk visible
+
+  // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1; lane i of
+  // `mine` holds the id of the wave's block i.
+  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int last = nmine - 1;
+  const int mine = lane < nmine ? s_blk[wave + lane * kWaves] : 0;
+  auto row0_of = [&](int i) {       // first cache row of block i (wave-uniform)
+    const int id = __builtin_amdgcn_readlane(mine, i);
+    return ((int64_t)id * Hkv + g) * kBlock;
+  };
+
+  // ---- pass 1: logits ----------------------------------------------------
+  float mloc = kNegInf;
+  if (nmine > 0) {
+    uint4 rk[kPf][NCH];
+    uint2 ksc[kPf], vsc[kPf];
+    auto issue = [&](int s, int i) {
+      const int64_t row0 = row0_of(i);
+      const int8_t* p = a.k_cache + (row0 + hl) * D + 16 * q4;
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) rk[s][u] = *reinterpret_cast<const uint4*>(p + 64 * u);
+      ksc[s] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + 4 * q4);
+      vsc[s] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + 4 * q4);
+    };
+    // Slots past the wave's last block re-read that block (L2 hits) and skip
+    // the compute, so every load stays unconditional.
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) issue(s, min(s, last));
+    for (int base = 0; base < nmine; base += kPf) {
+      priority_by_remaining(2 * nmine - base);
+#pragma unroll
+      for (int s = 0; s < kPf; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = base + s;
+        if (i < nmine) {
+          float4_t acc = {nqb, nqb, nqb, nqb};
+#pragma unroll
+          for (int j = 0; j < NKM; ++j) {
+            const uint4 r = rk[s][j / 2];
+            const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
+            const half8_t av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j], acc, 0, 0, 0);
+            if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[j], acc, 0, 0, 0);
+          }
+          const int tb = (wave + i * kWaves) * kBlock + 4 * q4;   // first of the lane's 4 tokens
+          const float k0 = fp16_bits_to_f32((uint16_t)ksc[s].x);
+          const float k1 = fp16_bits_to_f32((uint16_t)(ksc[s].x >> 16));
+          const float k2 = fp16_bits_to_f32((uint16_t)ksc[s].y);
+          const float k3 = fp16_bits_to_f32((uint16_t)(ksc[s].y >> 16));
+          const float kk[4] = {k0, k1, k2, k3};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = tb + r < ntok ? (kk[r] * cz) * acc[r] : kNegInf;
+            if (hl < G) {
+              s_z[(tb + r) * G + hl] = z;
+              mloc = fmaxf(mloc, z);
+            }
+          }
+          if (hl == 0) *reinterpret_cast<uint2*>(s_vs + tb) = vsc[s];
+        }
+        issue(s, min(i + kPf, last));
+      }
+    }
+  }
+
+  // V rows of the first kPf blocks are requested now, so that they arrive
+  // while the workgroup finishes the logits and builds the weights.
+  VRow rv[kPf][4];
+  auto issue_v = [&](int s, int i) {
+    const int8_t* p = a.v_cache + (row0_of(i) + 4 * q4) * D + hl * NVT;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(p + t * D);
+  };
+  if (nmine > 0) {
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) issue_v(s, min(s, last));
+  }
+
+  // max per head over the four k groups of lanes
+  {
+    float m = fmaxf(mloc, __shfl_xor(mloc, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (lane < G) s_red[wave * G + lane] = m;
+  }
+  __syncthreads();
+
+  // ---- middle: weights ----------------------------------------------------
+  {
+    const int h = tid % G;
+    float Mh = s_red[h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_red[w * G + h]);
+    float lsum = 0.0f, psum = 0.0f;
+    const int total = nblk * kBlock * G;
+    for (int e = tid; e < total; e += kThreads) {
+      const int t = e / G;
+      const float z = s_z[e];
+      _Float16 p16 = (_Float16)0.0f;
+      if (z != kNegInf) {
+        const float p = __builtin_amdgcn_exp2f(z - Mh);
+        p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
+        lsum += p;
+        if constexpr (C::kBiased) psum += (float)p16;
+      }
+      const int jj = t / kBlock, r = t % kBlock;
+      s_w[(jj * G + h) * kBlock + r] = p16;
+    }
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1) {
+      lsum += __shfl_xor(lsum, off);
+      psum += __shfl_xor(psum, off);
+    }
+    if (lane < G) {
+      s_red[kWaves * G + wave * G + lane] = lsum;
+      s_red[2 * kWaves * G + wave * G + lane] = psum;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: weighted sum of V codes ------------------------------------
+  float4_t acc[NVT];
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = 0; base < nmine; base += kPf) {
+    priority_by_remaining(nmine - base);
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = base + s;
+      if (i < nmine) {
+        half4_t wb = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+        if (hl < G)
+          wb = *reinterpret_cast<const half4_t*>(
+              s_w + ((wave + i * kWaves) * G + hl) * kBlock + 4 * q4);
+#pragma unroll
+        for (int k = 0; k < NVD; ++k) {
+          const uint32_t x0 = C::pre(dw(rv[s][0], k)), x1 = C::pre(dw(rv[s][1], k));
+          const uint32_t x2 = C::pre(dw(rv[s][2], k)), x3 = C::pre(dw(rv[s][3], k));
+          const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
+          const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
+          const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
+          const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
+          const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
+          const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
+          acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
+          acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
+          acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
+          acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
+        }
+      }
+      issue_v(s, min(i + kPf, last));
+    }
+  }
+
+  // this wave's [G][D] result to LDS (the logits are no longer needed)
+  if (hl < G) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* dst = s_fin + (wave * G + hl) * D + NVT * (4 * q4 + r);
+#pragma unroll
+      for (int j = 0; j < NVT; ++j) dst[j] = acc[j][r];
+    }
+  }
+  __syncthreads();
+  finish_split<G, D, kThreads, kWaves, C::kBiased>(
+      PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
+}
+
+template <int D, int G, bool QF32, class C>
+bool launch_one(const SplitArgs& a, hipStream_t stream) {
+  const MSmem L = msmem_layout(a.split_tokens, G, D);
+  SplitArgs args = a;
+  const int64_t grid = item_grid<decode_mfma_kernel<D, G, QF32, C>>(
+      kThreads, L.total, a.batch, (int64_t)a.n_split * a.num_kv_heads * a.batch, &args.period,
+      &args.snake_rounds);
+  if (grid > 0x7FFFFFFF) return false;
+  decode_mfma_kernel<D, G, QF32, C><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(
+      args);
+  return true;
+}
+
+template <int D, bool QF32, class C>
+bool by_group(int G, const SplitArgs& a, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_one<D, 1, QF32, C>(a, s);
+    case 2: return launch_one<D, 2, QF32, C>(a, s);
+    case 4: return launch_one<D, 4, QF32, C>(a, s);
+    case 8: return launch_one<D, 8, QF32, C>(a, s);
+    default: return false;
+  }
+}
+
+template <class C>
+bool by_dim(int head_dim, bool q_f32, int G, const SplitArgs& a, hipStream_t s) {
+  if (head_dim == 128) return q_f32 ? by_group<128, true, C>(G, a, s) : by_group<128, false, C>(G, a, s);
+  if (head_dim == 64) return q_f32 ? by_group<64, true, C>(G, a, s) : by_group<64, false, C>(G, a, s);
+  return false;
+}
+
+}  // namespace
+
+bool launch_decode_mfma(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
+                        hipStream_t stream) {
+  if (fmt == kFmtFp8) return by_dim<CodesFp8>(head_dim, q_f32, G, a, stream);
+  if (fmt == kFmtInt8) return by_dim<CodesInt8>(head_dim, q_f32, G, a, stream);
+  return false;
+}
+
+}  // namespace kv8

@@ -27,6 +27,11 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                              int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
                              hipStream_t stream);
 
+// Which form of the INT8 / FP8 decode kernel launches: automatic (by group
+// size), the v_dot2 kernel, or the matrix-core kernel.  Process-wide.
+enum : int { kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2 };
+void set_decode_kernel(int which);
+
 struct DecodePlan {
   int split_tokens;      // tokens per workgroup (multiple of 64)
   int n_split;           // workgroups per (sequence, KV head)

@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(params=["dot", "mfma"])
+def decode_kernel(request):
+    """Run a test under each form of the INT8/FP8 decode kernel (v_dot2 and
+    matrix-core), restoring the automatic choice afterwards."""
+    from paged_int8_kv_amd import binding as B
+    B.kv8_set_decode_kernel(B.DECODE_DOT if request.param == "dot" else B.DECODE_MFMA)
+    yield request.param
+    B.kv8_set_decode_kernel(B.DECODE_AUTO)

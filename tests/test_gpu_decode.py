@@ -11,7 +11,7 @@ from paged_int8_kv_amd import workloads as W
 from tests.kv8_testutil import (check_close, dev, gpu_append, gpu_decode, needs_gpu,
                                 oracle_cache, upload_cache)
 
-pytestmark = [pytest.mark.gpu, needs_gpu]
+pytestmark = [pytest.mark.gpu, needs_gpu, pytest.mark.usefixtures("decode_kernel")]
 
 
 def run_parity(case, tokens_per_split=0, cache_from="oracle"):

@@ -16,7 +16,7 @@ from tests.kv8_testutil import (bits_tensor, check_close, dev, download_cache, n
                                 oracle_cache, q_tensor, upload_cache)
 from tests.test_gpu_append import assert_cache_equal
 
-pytestmark = [pytest.mark.gpu, needs_gpu]
+pytestmark = [pytest.mark.gpu, needs_gpu, pytest.mark.usefixtures("decode_kernel")]
 
 
 def newest_rows(case):

@@ -16,7 +16,7 @@ from tests.kv8_testutil import (bits_tensor, check_close, dev, f16_to_i16, needs
                                 q_tensor)
 from tests.test_gpu_append import assert_cache_equal, rows_case
 
-pytestmark = [pytest.mark.gpu, needs_gpu]
+pytestmark = [pytest.mark.gpu, needs_gpu, pytest.mark.usefixtures("decode_kernel")]
 
 
 def oracle_cache_fp8(case):
