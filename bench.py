@@ -35,7 +35,7 @@ def parse():
                    help="untimed steps first (the GPU clocks settle over ~100 ms)")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--tokens-per-split", type=int, default=0)
-    p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma"], default="auto",
+    p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma", "mfma1"], default="auto",
                    help="form of the INT8/FP8 decode kernel (auto: by group size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-steps", type=int, default=24,
@@ -113,8 +113,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B.kv8_set_decode_kernel({"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT,
-                             "mfma": B.DECODE_MFMA}[args.decode_kernel])
+    B.kv8_set_decode_kernel({"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
+                             "mfma1": B.DECODE_MFMA_ONEPASS}[args.decode_kernel])
     if args.calibrate_copy:
         calibrate_copy(dev)
         return
@@ -439,13 +439,14 @@ def bench_sweep70b(args, dev):
         del g
     torch.cuda.synchronize()
     max_ctx = max(x[4] for x in layers)
-    ws = torch.zeros(B.kv8_decode_workspace_size(64, 64, 8, 128, max_ctx), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.zeros(B.kv8_decode_workspace_size(64, 64, 8, 128, max_ctx, args.tokens_per_split),
+                     dtype=torch.uint8, device=dev)
     out = torch.empty((64, 64, 128), dtype=torch.float32, device=dev)
 
     def sweep():
         for q, cache, table, lens, m in layers:
-            B.paged_decode_attn_kv8(q, *cache, table, lens, m, out, ws)
+            B.paged_decode_attn_kv8(q, *cache, table, lens, m, out, ws,
+                                    tokens_per_split=args.tokens_per_split)
 
     for _ in range(3):
         sweep()

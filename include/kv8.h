@@ -96,19 +96,28 @@ int kv8_version(void);
  * kv8_set_decode_kernel - choose the form of the INT8 / FP8 decode kernel
  * used by paged_decode_attn_kv8, paged_decode_attn_kv8_append and
  * paged_decode_attn_fp8kv, for this process (all threads, all devices).
- *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv;
+ *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv
+ *            (v_dot2 below G = 4, two-pass matrix-core at G = 4, one-pass
+ *            matrix-core from G = 8);
  *          KV8_DECODE_DOT  (1): the v_dot2 kernel;
- *          KV8_DECODE_MFMA (2): the matrix-core kernel (logits and values
- *          as 16x16 MFMA tiles over all G heads of a group at once).
- * Both forms compute the same attention (same softmax algebra, same work
- * split and merge); results agree within the attention tolerance, not
- * bitwise.  The INT4 decode always uses the v_dot2 kernel.  Takes effect for
- * launches issued after the call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED
- * for another value (the setting is then unchanged).
+ *          KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of
+ *            the split to LDS, then the weighted values; logits and values
+ *            as 16x16 MFMA tiles over all G heads of a group at once);
+ *          KV8_DECODE_MFMA_ONEPASS (3): the one-pass matrix-core kernel
+ *            (online softmax over K and V tiles streamed together, weights
+ *            kept in registers).
+ * All forms compute the same attention (the same work items and in-launch
+ * merge); results agree within the attention tolerance, not bitwise.  The
+ * form can change the default split size, hence the workspace a call needs;
+ * kv8_decode_workspace_size returns enough for every form.  The INT4 decode
+ * always uses the v_dot2 kernel.  Takes effect for launches issued after the
+ * call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED for another value (the
+ * setting is then unchanged).
  */
 #define KV8_DECODE_AUTO 0
 #define KV8_DECODE_DOT 1
 #define KV8_DECODE_MFMA 2
+#define KV8_DECODE_MFMA_ONEPASS 3
 int kv8_set_decode_kernel(int which);
 
 /*

@@ -28,7 +28,7 @@ EXPORTED = (
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
-    "kv8_quant_append_int4", "paged_decode_attn_int4kv",
+    "kv8_quant_append_int4", "paged_decode_attn_int4kv", "kv8_set_decode_kernel",
 )
 
 _lib = None
@@ -98,12 +98,13 @@ def load():
     return lib
 
 
-DECODE_AUTO, DECODE_DOT, DECODE_MFMA = 0, 1, 2
+DECODE_AUTO, DECODE_DOT, DECODE_MFMA, DECODE_MFMA_ONEPASS = 0, 1, 2, 3
 
 
 def kv8_set_decode_kernel(which):
     """Choose the INT8/FP8 decode kernel form for this process:
-    DECODE_AUTO (by group size), DECODE_DOT (v_dot2) or DECODE_MFMA."""
+    DECODE_AUTO (by group size), DECODE_DOT (v_dot2), DECODE_MFMA (two-pass
+    matrix-core) or DECODE_MFMA_ONEPASS (one-pass matrix-core)."""
     _check(load().kv8_set_decode_kernel(int(which)), "kv8_set_decode_kernel")
 
 

@@ -74,7 +74,8 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
     return KV8_ERR_UNSUPPORTED;
   kv8::DecodePlan plan;
   if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        tokens_per_split, &plan))
+                        tokens_per_split, kv8::decode_form(fmt, num_q_heads / num_kv_heads),
+                        &plan))
     return KV8_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KV8_ERR_ALIGN;
@@ -144,11 +145,13 @@ const char* kv8_status_string(int status) {
 int kv8_version(void) { return kVersion; }
 
 int kv8_set_decode_kernel(int which) {
-  if (which != KV8_DECODE_AUTO && which != KV8_DECODE_DOT && which != KV8_DECODE_MFMA)
-    return KV8_ERR_UNSUPPORTED;
-  kv8::set_decode_kernel(which == KV8_DECODE_DOT    ? kv8::kDecodeKernelDot
-                         : which == KV8_DECODE_MFMA ? kv8::kDecodeKernelMfma
-                                                    : kv8::kDecodeKernelAuto);
+  switch (which) {
+    case KV8_DECODE_AUTO: kv8::set_decode_kernel(kv8::kDecodeKernelAuto); break;
+    case KV8_DECODE_DOT: kv8::set_decode_kernel(kv8::kDecodeKernelDot); break;
+    case KV8_DECODE_MFMA: kv8::set_decode_kernel(kv8::kDecodeKernelMfma); break;
+    case KV8_DECODE_MFMA_ONEPASS: kv8::set_decode_kernel(kv8::kDecodeKernelMfmaOnePass); break;
+    default: return KV8_ERR_UNSUPPORTED;
+  }
   return KV8_OK;
 }
 
@@ -203,11 +206,16 @@ int kv8_quant_append_int4(const uint16_t* k_new, const uint16_t* v_new,
 size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int tokens_per_split) {
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
-  kv8::DecodePlan plan;
-  if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        tokens_per_split, &plan))
-    return 0;
-  return plan.total_bytes;
+  // enough for every kernel form (the form follows the code format and the
+  // process-wide kernel setting at launch time)
+  size_t need = 0;
+  for (int form : {kv8::kDecodeKernelDot, kv8::kDecodeKernelMfma, kv8::kDecodeKernelMfmaOnePass}) {
+    kv8::DecodePlan plan;
+    if (kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                         tokens_per_split, form, &plan) && plan.total_bytes > need)
+      need = plan.total_bytes;
+  }
+  return need;
 }
 
 int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
@@ -293,7 +301,7 @@ int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache
     return KV8_ERR_UNSUPPORTED;
   kv8::DecodePlan plan;
   if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        tokens_per_split, &plan))
+                        tokens_per_split, kv8::kDecodeKernelDot, &plan))
     return KV8_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KV8_ERR_ALIGN;

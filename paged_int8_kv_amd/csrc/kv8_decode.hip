@@ -468,44 +468,62 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 std::atomic<int> g_decode_kernel{kDecodeKernelAuto};
 
-// Automatic choice: the matrix-core kernel from four query heads per KV
-// head up, where the dot-product kernel's vector work per cache byte (G/2
-// v_dot2 issues per lane) outgrows the memory stream.
-bool use_mfma_decode(int G) {
-  const int k = g_decode_kernel.load(std::memory_order_relaxed);
-  if (k == kDecodeKernelDot) return false;
-  if (k == kDecodeKernelMfma) return true;
-  return G >= 4;
-}
-
 }  // namespace
 
 void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_order_relaxed); }
 
+// Automatic choice (measured on MI355X): from four query heads per KV head
+// up, the dot-product kernel's vector work per cache byte (G/2 v_dot2 issues
+// per lane) outgrows the memory stream and the matrix cores take over.  At
+// G = 4 the two-pass form, whose 96 VGPRs leave room for five workgroups
+// per CU, is ahead (37.4 against 39.7 us on the Llama-3.1-8B-shaped batch);
+// at G = 8 its logits take 50 KB of LDS per workgroup and the one-pass form,
+// which keeps no logits in LDS and takes 2048-token splits, is ahead (136.7
+// against 159.7 us per layer of the Llama-3-70B-shaped sweep).
+int decode_form(int fmt, int G) {
+  if (fmt == kFmtInt4) return kDecodeKernelDot;
+  const int k = g_decode_kernel.load(std::memory_order_relaxed);
+  if (k != kDecodeKernelAuto) return k;
+  if (G >= 8) return kDecodeKernelMfmaOnePass;
+  if (G >= 4) return kDecodeKernelMfma;
+  return kDecodeKernelDot;
+}
+
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                 int max_context_len, int tokens_per_split, DecodePlan* plan) {
+                 int max_context_len, int tokens_per_split, int form, DecodePlan* plan) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
   if (num_q_heads % num_kv_heads != 0) return false;
   const int G = num_q_heads / num_kv_heads;
+  // LDS of one workgroup at a split size: the one-pass kernel's does not
+  // grow with the split
+  auto smem = [&](int tps) {
+    if (form == kDecodeKernelMfmaOnePass) return 0;
+    if (form == kDecodeKernelMfma) return decode_mfma2_smem(tps, G, head_dim);
+    return smem_layout(tps, G, head_dim).total;
+  };
   int tps = tokens_per_split;
   if (tps <= 0) {
     // Largest split whose grid bound (every sequence at max_context_len)
     // still reaches 1024 workgroups, about four per CU: the per-workgroup
     // prologue, cross-wave reductions, partials and merge are a fixed cost
     // that larger splits amortise (measured on the Llama-3.1-8B-shaped
-    // batch: 1024-token splits 45.7 us, 512 51.0 us, 256 59.5 us).
+    // batch: 1024-token splits 45.7 us, 512 51.0 us, 256 59.5 us; on the
+    // Llama-3-70B-shaped sweep with the one-pass kernel: 2048-token splits
+    // 136.7 us per layer, 1024 152.6 us).  2048 only for the one-pass form.
     tps = 64;
-    const int cands[] = {1024, 512, 256, 128};
+    const int cands[] = {2048, 1024, 512, 256, 128};
     for (int c : cands) {
+      if (c == 2048 && form != kDecodeKernelMfmaOnePass) continue;
       const long long per_seq = max_context_len > 0 ? (max_context_len + c - 1) / c : 1;
       if ((long long)batch * num_kv_heads * per_seq >= 1024) { tps = c; break; }
     }
-    while (tps > 64 && smem_layout(tps, G, head_dim).total > 64 * 1024) tps /= 2;
+    while (tps > 64 && smem(tps) > 64 * 1024) tps /= 2;
   } else if (tps % 64 != 0 || tps < 64 || tps > 2048) {
     return false;
   }
-  if (smem_layout(tps, G, head_dim).total > 64 * 1024) return false;
+  if (smem(tps) > 64 * 1024) return false;
   const int n_split = max_context_len > 0 ? (max_context_len + tps - 1) / tps : 1;
+  plan->form = form;
   plan->split_tokens = tps;
   plan->n_split = n_split;
   plan->counter_bytes = align256((size_t)batch * num_kv_heads * sizeof(unsigned));
@@ -548,9 +566,10 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.qk_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   bool ok;
-  if (fmt != kFmtInt4 && use_mfma_decode(G)) {
-    a.period = a.snake_rounds = 0;
-    ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, stream);
+  if (plan.form != kDecodeKernelDot) {
+    if (fmt == kFmtInt4) return -2;
+    ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, plan.form == kDecodeKernelMfmaOnePass,
+                            stream);
   } else if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);
   else if (fmt == kFmtInt4) ok = dispatch_fmt<CodesInt4>(head_dim, q_f32, G, a, batch, stream);
   else ok = dispatch_fmt<CodesInt8>(head_dim, q_f32, G, a, batch, stream);

@@ -159,11 +159,13 @@ __device__ __forceinline__ void append_newest(const SplitArgs& a, int b, int g, 
   wait_vmem();
 }
 
-// Matrix-core form of the INT8 / FP8 decode (kv8_decode_mfma.hip): launches
-// the split kernel for head dim D in {64, 128}, group size G in {1, 2, 4, 8}
-// and the given code format; false for a shape it does not serve.
+// Matrix-core forms of the INT8 / FP8 decode (kv8_decode_mfma.hip): launch
+// the one-pass or the two-pass split kernel for head dim D in {64, 128},
+// group size G in {1, 2, 4, 8} and the given code format; false for a shape
+// they do not serve.  decode_mfma2_smem: LDS bytes of a two-pass workgroup.
 bool launch_decode_mfma(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
-                        hipStream_t stream);
+                        bool one_pass, hipStream_t stream);
+int decode_mfma2_smem(int split_tokens, int G, int head_dim);
 
 struct Item {
   int b;        // sequence, -1 past the last item

@@ -49,7 +49,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kPf = 4;        // blocks in flight per wave and pass
+constexpr int kPf = 2;        // one-pass kernel: blocks (K and V tiles) in flight per wave
+constexpr int kPf2 = 3;       // two-pass kernel: blocks in flight per wave and pass
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -57,15 +58,15 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 __host__ __device__ constexpr int align16m(int x) { return (x + 15) & ~15; }
 
-struct MSmem {
+struct M2Smem {
   int blk_off, z_off, vs_off, w_off, red_off, flag_off, total;
 };
 
-// LDS of one workgroup: block ids, logits [token][G] (reused for the
+// LDS of a two-pass workgroup: block ids, logits [token][G] (reused for the
 // cross-wave output sum [kWaves][G][D]), v scales per token, fp16 weights
 // [block][G][16 tokens], per-head scalars, the last-workgroup flag.
-__host__ __device__ inline MSmem msmem_layout(int split_tokens, int G, int D) {
-  MSmem L{};
+__host__ __device__ inline M2Smem m2smem_layout(int split_tokens, int G, int D) {
+  M2Smem L{};
   const int zbytes = split_tokens * G * 4;
   const int finbytes = kWaves * G * D * 4;
   L.blk_off = 0;
@@ -73,6 +74,21 @@ __host__ __device__ inline MSmem msmem_layout(int split_tokens, int G, int D) {
   L.vs_off = L.z_off + align16m(zbytes > finbytes ? zbytes : finbytes);
   L.w_off = L.vs_off + align16m(split_tokens * 2);
   L.red_off = L.w_off + align16m(split_tokens * G * 2);
+  L.flag_off = L.red_off + align16m(3 * kWaves * G * 4);
+  L.total = L.flag_off + 16;
+  return L;
+}
+
+struct MSmem {
+  int fin_off, red_off, flag_off, total;
+};
+
+// LDS of a one-pass workgroup: the per-wave outputs [kWaves][G][D], per-wave head
+// scalars (max, weight sum, fp16-weight sum) and the last-workgroup flag.
+__host__ __device__ inline MSmem msmem_layout(int G, int D) {
+  MSmem L{};
+  L.fin_off = 0;
+  L.red_off = align16m(kWaves * G * D * 4);
   L.flag_off = L.red_off + align16m(3 * kWaves * G * 4);
   L.total = L.flag_off + 16;
   return L;
@@ -90,14 +106,91 @@ __device__ __forceinline__ uint32_t dw(const uint4& r, int k) {
   return k == 0 ? r.x : k == 1 ? r.y : k == 2 ? r.z : r.w;
 }
 
+// Max over the four rows of 16 lanes (lanes l, l^16, l^32, l^48), every lane
+// receiving it: two row swaps on the vector unit, no LDS crossbar.
+__device__ __forceinline__ float rows_max(float x) {
+  float a, b;
+  swap16(x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+
 template <int NDW> struct VRowT;
 template <> struct VRowT<2> { using type = uint2; };
 template <> struct VRowT<1> { using type = uint32_t; };
 __device__ __forceinline__ uint32_t dw(const uint2& r, int k) { return k == 0 ? r.x : r.y; }
 __device__ __forceinline__ uint32_t dw(const uint32_t& r, int) { return r; }
 
+// q of head hl (lane % 16; zero for hl >= G) as the B operands of the logit
+// MFMAs: for MFMA j the 8 channels 64(j/2) + 16 q4 + 8(j%2) ... + 7, in fp16
+// after the head's power-of-two rescale (bf16 q is exact then; an fp32 q
+// also gets its fp16 remainder in qlo).  cz = log2(e) * sm_scale undoing the
+// rescale; nqb = minus the code bias times the head's fp16 q sum (the
+// logit accumulators start there).
 template <int D, int G, bool QF32, class C>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
+__device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int hl, int q4,
+                                           half8_t (&qb)[D / 32],
+                                           half8_t (&qlo)[QF32 ? D / 32 : 1], float& cz,
+                                           float& nqb) {
+  constexpr int NKM = D / 32;
+  const bool live = hl < G;
+  const int64_t qrow = (bh0 + (live ? hl : 0)) * D;
+  float x[NKM][8];
+#pragma unroll
+  for (int j = 0; j < NKM; ++j) {
+    const int c0 = 64 * (j / 2) + 16 * q4 + 8 * (j % 2);
+    if constexpr (QF32) {
+      const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + c0);
+      const float4 u = qp[0], v = qp[1];
+      x[j][0] = u.x; x[j][1] = u.y; x[j][2] = u.z; x[j][3] = u.w;
+      x[j][4] = v.x; x[j][5] = v.y; x[j][6] = v.z; x[j][7] = v.w;
+    } else {
+      const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow + c0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = dw(r, k);
+        x[j][2 * k] = __builtin_bit_cast(float, w << 16);
+        x[j][2 * k + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[j][i] = live ? x[j][i] : 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NKM; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[j][i]));
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  // power-of-two shift bringing the head's largest |q| into [2^14, 2^15)
+  const int e = m > 0.0f ? ilogbf(m) - 14 : 0;
+  float qsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NKM; ++j) {
+    _Float16 hv[8], lv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sc = ldexpf(x[j][i], -e);
+      hv[i] = (_Float16)sc;
+      qsum += (float)hv[i];
+      if constexpr (QF32) {
+        lv[i] = (_Float16)(sc - (float)hv[i]);
+        qsum += (float)lv[i];
+      }
+    }
+    qb[j] = half8_t{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+    if constexpr (QF32) qlo[j] = half8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
+  }
+  qsum += __shfl_xor(qsum, 16);
+  qsum += __shfl_xor(qsum, 32);
+  cz = ldexpf(a.qk_scale_log2, e);
+  nqb = -C::kBias * qsum;
+}
+
+template <int D, int G, bool QF32, class C>
+__global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
   static_assert(C::kBits == 8, "byte codes");
   static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
   constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block
@@ -107,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
   using VRow = typename VRowT<NVD>::type;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const MSmem L = msmem_layout(a.split_tokens, G, D);
+  const M2Smem L = m2smem_layout(a.split_tokens, G, D);
   int* s_blk = reinterpret_cast<int*>(smem + L.blk_off);
   float* s_z = reinterpret_cast<float*>(smem + L.z_off);
   float* s_fin = s_z;
@@ -147,61 +240,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
   // ---- q of head hl as the B operand of the logit MFMAs ------------------
   half8_t qb[NKM], qlo[QF32 ? NKM : 1];
   float cz, nqb;
-  {
-    const bool live = hl < G;
-    const int64_t qrow = (bh0 + (live ? hl : 0)) * D;
-    float x[NKM][8];
-#pragma unroll
-    for (int j = 0; j < NKM; ++j) {
-      const int c0 = 64 * (j / 2) + 16 * q4 + 8 * (j % 2);
-      if constexpr (QF32) {
-        const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + c0);
-        const float4 u = qp[0], v = qp[1];
-        x[j][0] = u.x; x[j][1] = u.y; x[j][2] = u.z; x[j][3] = u.w;
-        x[j][4] = v.x; x[j][5] = v.y; x[j][6] = v.z; x[j][7] = v.w;
-      } else {
-        const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow + c0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t w = dw(r, k);
-          x[j][2 * k] = __builtin_bit_cast(float, w << 16);
-          x[j][2 * k + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[j][i] = live ? x[j][i] : 0.0f;
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NKM; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[j][i]));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    // power-of-two shift bringing the head's largest |q| into [2^14, 2^15)
-    const int e = m > 0.0f ? ilogbf(m) - 14 : 0;
-    float qsum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NKM; ++j) {
-      _Float16 hv[8], lv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float s = ldexpf(x[j][i], -e);
-        hv[i] = (_Float16)s;
-        qsum += (float)hv[i];
-        if constexpr (QF32) {
-          lv[i] = (_Float16)(s - (float)hv[i]);
-          qsum += (float)lv[i];
-        }
-      }
-      qb[j] = half8_t{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
-      if constexpr (QF32) qlo[j] = half8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
-    }
-    qsum += __shfl_xor(qsum, 16);
-    qsum += __shfl_xor(qsum, 32);
-    cz = ldexpf(a.qk_scale_log2, e);
-    nqb = -C::kBias * qsum;
-  }
+  q_operands<D, G, QF32, C>(a, bh0, hl, q4, qb, qlo, cz, nqb);
   __syncthreads();   // s_blk visible
 
   // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1; lane i of
@@ -217,24 +256,27 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
   // ---- pass 1: logits ----------------------------------------------------
   float mloc = kNegInf;
   if (nmine > 0) {
-    uint4 rk[kPf][NCH];
-    uint2 ksc[kPf], vsc[kPf];
+    uint4 rk[kPf2][NCH];
+    uint2 ksc[kPf2], vsc[kPf2];
+    // Slots past the wave's last block still load (so the compiler's wait
+    // counts stay exact) but every lane reads the same bytes of the last
+    // block, one cache line per instruction, and the compute skips them.
     auto issue = [&](int s, int i) {
-      const int64_t row0 = row0_of(i);
-      const int8_t* p = a.k_cache + (row0 + hl) * D + 16 * q4;
+      const bool real = i <= last;                 // wave-uniform
+      const int64_t row0 = row0_of(min(i, last));
+      const int8_t* p = a.k_cache + row0 * D + (real ? hl * D + 16 * q4 : 0);
+      const int so = real ? 4 * q4 : 0;
 #pragma unroll
       for (int u = 0; u < NCH; ++u) rk[s][u] = *reinterpret_cast<const uint4*>(p + 64 * u);
-      ksc[s] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + 4 * q4);
-      vsc[s] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + 4 * q4);
+      ksc[s] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + so);
+      vsc[s] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + so);
     };
-    // Slots past the wave's last block re-read that block (L2 hits) and skip
-    // the compute, so every load stays unconditional.
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) issue(s, min(s, last));
-    for (int base = 0; base < nmine; base += kPf) {
+    for (int s = 0; s < kPf2; ++s) issue(s, s);
+    for (int base = 0; base < nmine; base += kPf2) {
       priority_by_remaining(2 * nmine - base);
 #pragma unroll
-      for (int s = 0; s < kPf; ++s) {
+      for (int s = 0; s < kPf2; ++s) {
         __builtin_amdgcn_sched_barrier(0);
         const int i = base + s;
         if (i < nmine) {
@@ -263,22 +305,24 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
           }
           if (hl == 0) *reinterpret_cast<uint2*>(s_vs + tb) = vsc[s];
         }
-        issue(s, min(i + kPf, last));
+        issue(s, i + kPf2);
       }
     }
   }
 
-  // V rows of the first kPf blocks are requested now, so that they arrive
+  // V rows of the first kPf2 blocks are requested now, so that they arrive
   // while the workgroup finishes the logits and builds the weights.
-  VRow rv[kPf][4];
+  VRow rv[kPf2][4];
   auto issue_v = [&](int s, int i) {
-    const int8_t* p = a.v_cache + (row0_of(i) + 4 * q4) * D + hl * NVT;
+    const bool real = i <= last;                   // wave-uniform, as in pass 1
+    const int8_t* p = a.v_cache + row0_of(min(i, last)) * D + (real ? 4 * q4 * D + hl * NVT : 0);
+    const int stride = real ? D : 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(p + t * D);
+    for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(p + t * stride);
   };
   if (nmine > 0) {
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) issue_v(s, min(s, last));
+    for (int s = 0; s < kPf2; ++s) issue_v(s, s);
   }
 
   // max per head over the four k groups of lanes
@@ -326,10 +370,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
   float4_t acc[NVT];
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int base = 0; base < nmine; base += kPf) {
+  for (int base = 0; base < nmine; base += kPf2) {
     priority_by_remaining(nmine - base);
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) {
+    for (int s = 0; s < kPf2; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       const int i = base + s;
       if (i < nmine) {
@@ -353,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
           acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
         }
       }
-      issue_v(s, min(i + kPf, last));
+      issue_v(s, i + kPf2);
     }
   }
 
@@ -373,43 +417,252 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(SplitArgs a) {
 }
 
 template <int D, int G, bool QF32, class C>
+__global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
+  static_assert(C::kBits == 8, "byte codes");
+  static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
+  constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block
+  constexpr int NKM = D / 32;     // logit MFMAs per block (per q part)
+  constexpr int NVT = D / 16;     // value tiles per block (= bytes per V row piece)
+  constexpr int NVD = NVT / 4;    // dwords of a lane's V row piece
+  using VRow = typename VRowT<NVD>::type;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const MSmem L = msmem_layout(G, D);
+  float* s_fin = reinterpret_cast<float*>(smem + L.fin_off);   // [kWaves][G][D]
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const Item it = locate_item(a.context_lens, a.batch, a.ctx_cap, a.num_kv_heads,
+                              a.split_tokens, a.period, a.snake_rounds, lane);
+  const int b = it.b, g = it.g, split = it.split;
+  if (b < 0) return;                           // uniform: past the item list
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15;                    // token (logit A) / head (B, D) / channel row
+  const int q4 = lane >> 4;                    // k group
+  const int64_t bh0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;
+
+  int ctx = a.context_lens[b];
+  ctx = min(max(ctx, 0), a.ctx_cap);
+  if (ctx == 0) {                              // uniform: empty context, zero output
+    for (int e = tid; e < G * D; e += kThreads) a.out[bh0 * D + e] = 0.0f;
+    return;
+  }
+  const Span sp = split_span(it, ctx);
+  const int nblk = sp.nblk, jb0 = sp.jb0, ntok = sp.ntok;
+  const int Hkv = a.num_kv_heads;
+
+  // Each wave owns blocks wave + i * kWaves, i = 0 .. nmine-1; lane i of
+  // `mine` holds the id of the wave's block i, read straight from the table.
+  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int last = nmine - 1;
+  int mine = 0;
+  if (lane < nmine) {
+    int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + jb0 + wave + lane * kWaves];
+    mine = (int)(id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id));
+  }
+  // Decode step with append: the wave that owns the split's last block (the
+  // block of position ctx - 1) quantises and stores the newest token before
+  // its own loads of that block, which are ordered after the stores' wait.
+  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == (nblk - 1) % kWaves)
+    append_newest<D, C>(a, b, g, ctx, lane);
+
+  auto row0_of = [&](int i) {       // first cache row of block i (wave-uniform)
+    const int id = __builtin_amdgcn_readlane(mine, i);
+    return ((int64_t)id * Hkv + g) * kBlock;
+  };
+
+  // ---- the ring: K and V tiles of kPf blocks in flight -----------------------
+  // Slots past the wave's last block still load (so the compiler's wait
+  // counts stay exact) but every lane reads the same bytes of the last
+  // block, one cache line per instruction, and the compute skips them.
+  uint4 rk[kPf][NCH];
+  uint2 ksc[kPf], vsc[kPf];
+  VRow rv[kPf][4];
+  auto issue = [&](int s, int i) {
+    const bool real = i <= last;                   // wave-uniform
+    const int64_t row0 = row0_of(min(i, last));
+    const int8_t* pk = a.k_cache + row0 * D + (real ? hl * D + 16 * q4 : 0);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) rk[s][u] = *reinterpret_cast<const uint4*>(pk + 64 * u);
+    const int so = real ? 4 * q4 : 0;
+    ksc[s] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + so);
+    vsc[s] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + so);
+    const int8_t* pv = a.v_cache + row0 * D + (real ? 4 * q4 * D + hl * NVT : 0);
+    const int stride = real ? D : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(pv + t * stride);
+  };
+  if (nmine > 0) {
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) issue(s, s);
+  }
+
+  // ---- q of head hl as the B operand of the logit MFMAs (while the first
+  // tiles are in flight) --------------------------------------------------------
+  half8_t qb[NKM], qlo[QF32 ? NKM : 1];
+  float cz, nqb;
+  q_operands<D, G, QF32, C>(a, bh0, hl, q4, qb, qlo, cz, nqb);
+
+  // ---- one pass: logits, online softmax, weighted values ---------------------
+  // Lane l holds, for head hl, the running max m (the same in the four lanes
+  // of the head), its partial weight sum l and fp16-weight sum ps over its
+  // tokens, and O[hl][channel (D/16)(4 q4 + r) + j] in acc[j][r].
+  float m_run = kNegInf, l_run = 0.0f, p_run = 0.0f;
+  float4_t acc[NVT];
+#pragma unroll
+  for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = 0; base < nmine; base += kPf) {
+    priority_by_remaining(nmine - base);
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = base + s;
+      if (i < nmine) {
+        // logits of tokens 4 q4 + r for head hl
+        float4_t S = {nqb, nqb, nqb, nqb};
+#pragma unroll
+        for (int j = 0; j < NKM; ++j) {
+          const uint4 r = rk[s][j / 2];
+          const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
+          const half8_t av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j], S, 0, 0, 0);
+          if constexpr (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[j], S, 0, 0, 0);
+        }
+        const int tb = (wave + i * kWaves) * kBlock + 4 * q4;   // split-local token of r = 0
+        const uint32_t kw[2] = {ksc[s].x, ksc[s].y};
+        const uint32_t vw[2] = {vsc[s].x, vsc[s].y};
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ks = fp16_bits_to_f32((uint16_t)(kw[r / 2] >> (16 * (r % 2))));
+          z[r] = tb + r < ntok ? (ks * cz) * S[r] : kNegInf;
+        }
+        // block max of the head over its four lanes; a new max rescales
+        float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        bm = rows_max(bm);
+        if (__builtin_amdgcn_ballot_w64(bm > m_run)) {   // wave-uniform branch
+          const float f = bm > m_run ? __builtin_amdgcn_exp2f(m_run - bm) : 1.0f;
+          m_run = fmaxf(m_run, bm);
+          l_run *= f;
+          p_run *= f;
+#pragma unroll
+          for (int j = 0; j < NVT; ++j) acc[j] *= f;
+        }
+        _Float16 w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(z[r] - m_run);   // 0 for masked tokens
+          const float vs = fp16_bits_to_f32((uint16_t)(vw[r / 2] >> (16 * (r % 2))));
+          w[r] = (_Float16)(tb + r < ntok ? p * vs : 0.0f);   // never reads a stale scale
+          l_run += p;
+          if constexpr (C::kBiased) p_run += (float)w[r];
+        }
+        const half4_t wb = {w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int k = 0; k < NVD; ++k) {
+          const uint32_t x0 = C::pre(dw(rv[s][0], k)), x1 = C::pre(dw(rv[s][1], k));
+          const uint32_t x2 = C::pre(dw(rv[s][2], k)), x3 = C::pre(dw(rv[s][3], k));
+          const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
+          const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
+          const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
+          const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
+          const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
+          const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
+          acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
+          acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
+          acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
+          acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
+        }
+      }
+      issue(s, i + kPf);
+    }
+  }
+
+  // ---- the four waves to one split result, all relative to the split max ----
+  if (lane < G) s_red[wave * G + lane] = m_run;
+  __syncthreads();
+  {
+    float M = s_red[hl < G ? hl : 0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w * G + (hl < G ? hl : 0)]);
+    // a wave without blocks holds m = -inf and nothing else: factor 0
+    const float f = m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    float lw = l_run * f, pw = p_run * f;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+    pw += __shfl_xor(pw, 16);
+    pw += __shfl_xor(pw, 32);
+    if (lane < G) {
+      s_red[kWaves * G + wave * G + lane] = lw;
+      s_red[2 * kWaves * G + wave * G + lane] = pw;
+    }
+    if (hl < G) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = s_fin + (wave * G + hl) * D + NVT * (4 * q4 + r);
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) dst[j] = acc[j][r] * f;
+      }
+    }
+  }
+  __syncthreads();
+  finish_split<G, D, kThreads, kWaves, C::kBiased>(
+      PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
+}
+
+template <int D, int G, bool QF32, class C, bool ONEPASS>
 bool launch_one(const SplitArgs& a, hipStream_t stream) {
-  const MSmem L = msmem_layout(a.split_tokens, G, D);
+  constexpr auto kernel = ONEPASS ? decode_mfma1_kernel<D, G, QF32, C>
+                                  : decode_mfma2_kernel<D, G, QF32, C>;
+  const int smem = ONEPASS ? msmem_layout(G, D).total : m2smem_layout(a.split_tokens, G, D).total;
   SplitArgs args = a;
-  const int64_t grid = item_grid<decode_mfma_kernel<D, G, QF32, C>>(
-      kThreads, L.total, a.batch, (int64_t)a.n_split * a.num_kv_heads * a.batch, &args.period,
-      &args.snake_rounds);
+  const int64_t grid = item_grid<kernel>(kThreads, smem, a.batch,
+                                         (int64_t)a.n_split * a.num_kv_heads * a.batch,
+                                         &args.period, &args.snake_rounds);
   if (grid > 0x7FFFFFFF) return false;
-  decode_mfma_kernel<D, G, QF32, C><<<dim3((unsigned)grid), dim3(kThreads), L.total, stream>>>(
-      args);
+  kernel<<<dim3((unsigned)grid), dim3(kThreads), smem, stream>>>(args);
   return true;
 }
 
-template <int D, bool QF32, class C>
+template <int D, bool QF32, class C, bool ONEPASS>
 bool by_group(int G, const SplitArgs& a, hipStream_t s) {
   switch (G) {
-    case 1: return launch_one<D, 1, QF32, C>(a, s);
-    case 2: return launch_one<D, 2, QF32, C>(a, s);
-    case 4: return launch_one<D, 4, QF32, C>(a, s);
-    case 8: return launch_one<D, 8, QF32, C>(a, s);
+    case 1: return launch_one<D, 1, QF32, C, ONEPASS>(a, s);
+    case 2: return launch_one<D, 2, QF32, C, ONEPASS>(a, s);
+    case 4: return launch_one<D, 4, QF32, C, ONEPASS>(a, s);
+    case 8: return launch_one<D, 8, QF32, C, ONEPASS>(a, s);
     default: return false;
   }
 }
 
-template <class C>
+template <class C, bool ONEPASS>
 bool by_dim(int head_dim, bool q_f32, int G, const SplitArgs& a, hipStream_t s) {
-  if (head_dim == 128) return q_f32 ? by_group<128, true, C>(G, a, s) : by_group<128, false, C>(G, a, s);
-  if (head_dim == 64) return q_f32 ? by_group<64, true, C>(G, a, s) : by_group<64, false, C>(G, a, s);
+  if (head_dim == 128)
+    return q_f32 ? by_group<128, true, C, ONEPASS>(G, a, s) : by_group<128, false, C, ONEPASS>(G, a, s);
+  if (head_dim == 64)
+    return q_f32 ? by_group<64, true, C, ONEPASS>(G, a, s) : by_group<64, false, C, ONEPASS>(G, a, s);
+  return false;
+}
+
+template <bool ONEPASS>
+bool by_fmt(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt, hipStream_t stream) {
+  if (fmt == kFmtFp8) return by_dim<CodesFp8, ONEPASS>(head_dim, q_f32, G, a, stream);
+  if (fmt == kFmtInt8) return by_dim<CodesInt8, ONEPASS>(head_dim, q_f32, G, a, stream);
   return false;
 }
 
 }  // namespace
 
+int decode_mfma2_smem(int split_tokens, int G, int head_dim) {
+  return m2smem_layout(split_tokens, G, head_dim).total;
+}
+
 bool launch_decode_mfma(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
-                        hipStream_t stream) {
-  if (fmt == kFmtFp8) return by_dim<CodesFp8>(head_dim, q_f32, G, a, stream);
-  if (fmt == kFmtInt8) return by_dim<CodesInt8>(head_dim, q_f32, G, a, stream);
-  return false;
+                        bool one_pass, hipStream_t stream) {
+  return one_pass ? by_fmt<true>(a, head_dim, G, q_f32, fmt, stream)
+                  : by_fmt<false>(a, head_dim, G, q_f32, fmt, stream);
 }
 
 }  // namespace kv8

@@ -28,11 +28,17 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                              hipStream_t stream);
 
 // Which form of the INT8 / FP8 decode kernel launches: automatic (by group
-// size), the v_dot2 kernel, or the matrix-core kernel.  Process-wide.
-enum : int { kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2 };
+// size), the v_dot2 kernel, the two-pass or the one-pass matrix-core kernel.
+// Process-wide.  decode_form: the form a launch of this code format and
+// group size takes under the current setting (INT4 always takes v_dot2).
+enum : int {
+  kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3
+};
 void set_decode_kernel(int which);
+int decode_form(int fmt, int G);
 
 struct DecodePlan {
+  int form;              // kDecodeKernelDot / Mfma / MfmaOnePass
   int split_tokens;      // tokens per workgroup (multiple of 64)
   int n_split;           // workgroups per (sequence, KV head)
   size_t counter_bytes;  // uint32 [B, Hkv] finished-split counters (self-resetting)
@@ -43,7 +49,7 @@ struct DecodePlan {
 
 // Split plan shared by the workspace query and the launch.
 bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                 int max_context_len, int tokens_per_split, DecodePlan* plan);
+                 int max_context_len, int tokens_per_split, int form, DecodePlan* plan);
 
 int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t* v_cache,
                   const uint16_t* k_scale, const uint16_t* v_scale, int64_t num_blocks,

@@ -251,3 +251,26 @@ def test_int4_append_validation_matches_int8(kw):
 ])
 def test_int4_decode_validation_matches_int8(kw):
     assert decode(fn="paged_decode_attn_int4kv", **kw) == decode(**kw)
+
+
+def test_set_decode_kernel_values():
+    """Host-side only: the four kernel-form values are accepted, others are
+    rejected with the setting unchanged; the automatic choice is restored."""
+    lib = B.load()
+    try:
+        for which in (B.DECODE_DOT, B.DECODE_MFMA, B.DECODE_MFMA_ONEPASS, B.DECODE_AUTO):
+            assert lib.kv8_set_decode_kernel(which) == B.KV8_OK
+        for bad in (-1, 4, 99):
+            assert lib.kv8_set_decode_kernel(bad) == B.KV8_ERR_UNSUPPORTED
+    finally:
+        lib.kv8_set_decode_kernel(B.DECODE_AUTO)
+
+
+def test_decode_workspace_covers_every_form():
+    """The workspace query sizes for the smallest default split any kernel
+    form may take: at G = 8 and 64 sequences of up to 16384 tokens the
+    one-pass form takes 2048-token splits and the others 1024, so the query
+    answers for 1024 (16 splits)."""
+    ws = B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 0)
+    assert ws == B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 1024)
+    assert ws > B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 2048)
