@@ -97,8 +97,10 @@ int kv8_version(void);
  * used by paged_decode_attn_kv8, paged_decode_attn_kv8_append and
  * paged_decode_attn_fp8kv, for this process (all threads, all devices).
  *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv
- *            (v_dot2 below G = 4, two-pass matrix-core at G = 4, one-pass
- *            matrix-core from G = 8);
+ *            and grid size (v_dot2 below G = 4; at G = 4 two-pass
+ *            matrix-core while the grid bound, every sequence at
+ *            max_context_len in 1024-token splits, is at most 4096
+ *            workgroups, else one-pass; one-pass matrix-core from G = 8);
  *          KV8_DECODE_DOT  (1): the v_dot2 kernel;
  *          KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of
  *            the split to LDS, then the weighted values; logits and values
@@ -110,7 +112,9 @@ int kv8_version(void);
  * merge); results agree within the attention tolerance, not bitwise.  The
  * form can change the default split size, hence the workspace a call needs;
  * kv8_decode_workspace_size returns enough for every form.  The INT4 decode
- * always uses the v_dot2 kernel.  Takes effect for launches issued after the
+ * (paged_decode_attn_int4kv) has two forms: the one-pass matrix-core kernel
+ * at d = 128 (AUTO from G = 4, or MFMA_ONEPASS) and the v_dot2 kernel
+ * otherwise.  Takes effect for launches issued after the
  * call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED for another value (the
  * setting is then unchanged).
  */

@@ -74,7 +74,11 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
     return KV8_ERR_UNSUPPORTED;
   kv8::DecodePlan plan;
   if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        tokens_per_split, kv8::decode_form(fmt, num_q_heads / num_kv_heads),
+                        tokens_per_split,
+                        kv8::decode_form(fmt, num_q_heads / num_kv_heads,
+                                         (long long)batch * num_kv_heads *
+                                             ((max_context_len + 1023) / 1024),
+                                         head_dim),
                         &plan))
     return KV8_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;

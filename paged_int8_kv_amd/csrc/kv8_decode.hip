@@ -474,18 +474,29 @@ void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_ord
 
 // Automatic choice (measured on MI355X): from four query heads per KV head
 // up, the dot-product kernel's vector work per cache byte (G/2 v_dot2 issues
-// per lane) outgrows the memory stream and the matrix cores take over.  At
-// G = 4 the two-pass form, whose 96 VGPRs leave room for five workgroups
-// per CU, is ahead (37.4 against 39.7 us on the Llama-3.1-8B-shaped batch);
-// at G = 8 its logits take 50 KB of LDS per workgroup and the one-pass form,
-// which keeps no logits in LDS and takes 2048-token splits, is ahead (136.7
-// against 159.7 us per layer of the Llama-3-70B-shaped sweep).
-int decode_form(int fmt, int G) {
-  if (fmt == kFmtInt4) return kDecodeKernelDot;
+// per lane) outgrows the memory stream and the matrix cores take over.
+// - G = 8: the two-pass form's logits take 50 KB of LDS per workgroup; the
+//   one-pass form keeps none and takes 2048-token splits (136.7 against
+//   159.7 us per layer of the Llama-3-70B-shaped sweep).
+// - G = 4, a grid of about one round of workgroups: the two-pass form, whose
+//   84 VGPRs leave room for five workgroups per CU (37.5 against 39.7 us on
+//   the Llama-3.1-8B-shaped batch, 1024 workgroups at most).
+// - G = 4, many rounds: the one-pass form (1513 against 1663 us on 15
+//   sequences of 264192 tokens, about 31000 workgroups).
+// `grid_bound` is the workgroup count with every sequence at the longest
+// context and 1024-token splits.
+// - INT4 codes: the one-pass form at d = 128 from G = 4 (any other
+//   setting or shape takes the v_dot2 kernel, the only other INT4 form).
+int decode_form(int fmt, int G, long long grid_bound, int head_dim) {
   const int k = g_decode_kernel.load(std::memory_order_relaxed);
+  if (fmt == kFmtInt4) {
+    const bool mfma = head_dim == 128 && (k == kDecodeKernelMfmaOnePass ||
+                                          (k == kDecodeKernelAuto && G >= 4));
+    return mfma ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
+  }
   if (k != kDecodeKernelAuto) return k;
   if (G >= 8) return kDecodeKernelMfmaOnePass;
-  if (G >= 4) return kDecodeKernelMfma;
+  if (G >= 4) return grid_bound > 4096 ? kDecodeKernelMfmaOnePass : kDecodeKernelMfma;
   return kDecodeKernelDot;
 }
 
@@ -567,7 +578,7 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   const int G = num_q_heads / num_kv_heads;
   bool ok;
   if (plan.form != kDecodeKernelDot) {
-    if (fmt == kFmtInt4) return -2;
+    if (fmt == kFmtInt4 && plan.form != kDecodeKernelMfmaOnePass) return -2;
     ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, plan.form == kDecodeKernelMfmaOnePass,
                             stream);
   } else if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);

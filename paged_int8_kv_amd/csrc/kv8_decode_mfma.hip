@@ -50,6 +50,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kPf = 2;        // one-pass kernel: blocks (K and V tiles) in flight per wave
+constexpr int kPfNib = 2;     // the same for 4-bit codes (4 measured slower: 29.5 vs 28.7 us)
 constexpr int kPf2 = 3;       // two-pass kernel: blocks in flight per wave and pass
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -123,7 +124,9 @@ __device__ __forceinline__ uint32_t dw(const uint2& r, int k) { return k == 0 ? 
 __device__ __forceinline__ uint32_t dw(const uint32_t& r, int) { return r; }
 
 // q of head hl (lane % 16; zero for hl >= G) as the B operands of the logit
-// MFMAs: for MFMA j the 8 channels 64(j/2) + 16 q4 + 8(j%2) ... + 7, in fp16
+// MFMAs: for MFMA j the 8 channels 64(j/2) + 16 q4 + 8(j%2) ... + 7 of byte
+// codes, or for 4-bit codes the channels 32 q4 + 8j + (0, 4, 1, 5, 2, 6, 3,
+// 7) in the order the nibble pairs come out, in fp16
 // after the head's power-of-two rescale (bf16 q is exact then; an fp32 q
 // also gets its fp16 remainder in qlo).  cz = log2(e) * sm_scale undoing the
 // rescale; nqb = minus the code bias times the head's fp16 q sum (the
@@ -134,12 +137,13 @@ __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int 
                                            half8_t (&qlo)[QF32 ? D / 32 : 1], float& cz,
                                            float& nqb) {
   constexpr int NKM = D / 32;
+  constexpr bool NIB = C::kBits == 4;
   const bool live = hl < G;
   const int64_t qrow = (bh0 + (live ? hl : 0)) * D;
   float x[NKM][8];
 #pragma unroll
   for (int j = 0; j < NKM; ++j) {
-    const int c0 = 64 * (j / 2) + 16 * q4 + 8 * (j % 2);
+    const int c0 = NIB ? 32 * q4 + 8 * j : 64 * (j / 2) + 16 * q4 + 8 * (j % 2);
     if constexpr (QF32) {
       const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qrow + c0);
       const float4 u = qp[0], v = qp[1];
@@ -156,6 +160,11 @@ __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int 
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[j][i] = live ? x[j][i] : 0.0f;
+    if constexpr (NIB) {   // slot order of the nibble pairs: channels 0,4,1,5,2,6,3,7
+      const float y[8] = {x[j][0], x[j][4], x[j][1], x[j][5], x[j][2], x[j][6], x[j][3], x[j][7]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[j][i] = y[i];
+    }
   }
   float m = 0.0f;
 #pragma unroll
@@ -418,13 +427,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
 
 template <int D, int G, bool QF32, class C>
 __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
-  static_assert(C::kBits == 8, "byte codes");
   static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
-  constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block
+  constexpr bool NIB = C::kBits == 4;   // two 4-bit codes per byte
+  static_assert(!NIB || D == 128, "4-bit codes: d = 128");
+  constexpr int RB = NIB ? D / 2 : D;   // code bytes per cache row
+  constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block (byte codes)
   constexpr int NKM = D / 32;     // logit MFMAs per block (per q part)
-  constexpr int NVT = D / 16;     // value tiles per block (= bytes per V row piece)
-  constexpr int NVD = NVT / 4;    // dwords of a lane's V row piece
+  constexpr int NVT = D / 16;     // value tiles per block (= channels of a lane's V piece)
+  constexpr int NVD = NIB ? 1 : NVT / 4;   // dwords of a lane's V row piece
   using VRow = typename VRowT<NVD>::type;
+  constexpr int kPf = NIB ? kPfNib : ::kv8::kPf;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const MSmem L = msmem_layout(G, D);
@@ -464,8 +476,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
   // Decode step with append: the wave that owns the split's last block (the
   // block of position ctx - 1) quantises and stores the newest token before
   // its own loads of that block, which are ordered after the stores' wait.
-  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == (nblk - 1) % kWaves)
-    append_newest<D, C>(a, b, g, ctx, lane);
+  if constexpr (!NIB) {
+    if (a.k_new != nullptr && split == it.nsplit - 1 && wave == (nblk - 1) % kWaves)
+      append_newest<D, C>(a, b, g, ctx, lane);
+  }
 
   auto row0_of = [&](int i) {       // first cache row of block i (wave-uniform)
     const int id = __builtin_amdgcn_readlane(mine, i);
@@ -482,14 +496,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
   auto issue = [&](int s, int i) {
     const bool real = i <= last;                   // wave-uniform
     const int64_t row0 = row0_of(min(i, last));
-    const int8_t* pk = a.k_cache + row0 * D + (real ? hl * D + 16 * q4 : 0);
+    const int8_t* pk = a.k_cache + row0 * RB + (real ? hl * RB + 16 * q4 : 0);
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) rk[s][u] = *reinterpret_cast<const uint4*>(pk + 64 * u);
+    for (int u = 0; u < (NIB ? 1 : NCH); ++u) rk[s][u] = *reinterpret_cast<const uint4*>(pk + 64 * u);
     const int so = real ? 4 * q4 : 0;
     ksc[s] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + so);
     vsc[s] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + so);
-    const int8_t* pv = a.v_cache + row0 * D + (real ? 4 * q4 * D + hl * NVT : 0);
-    const int stride = real ? D : 0;
+    const int8_t* pv = a.v_cache + row0 * RB + (real ? 4 * q4 * RB + hl * (NIB ? NVT / 2 : NVT) : 0);
+    const int stride = real ? RB : 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(pv + t * stride);
   };
@@ -523,9 +537,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
         float4_t S = {nqb, nqb, nqb, nqb};
 #pragma unroll
         for (int j = 0; j < NKM; ++j) {
-          const uint4 r = rk[s][j / 2];
-          const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
-          const half8_t av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+          half8_t av;
+          if constexpr (NIB) {   // dword j: channels 32 q4 + 8j .. + 7 as nibble pairs (c, c+4)
+            const uint32_t x = C::pre(dw(rk[s][0], j));
+            av = cat8(C::nib_pair(x, 0), C::nib_pair(x, 1), C::nib_pair(x, 2), C::nib_pair(x, 3));
+          } else {
+            const uint4 r = rk[s][j / 2];
+            const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
+            av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+          }
           S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j], S, 0, 0, 0);
           if constexpr (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[j], S, 0, 0, 0);
         }
@@ -559,6 +579,24 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           if constexpr (C::kBiased) p_run += (float)w[r];
         }
         const half4_t wb = {w[0], w[1], w[2], w[3]};
+        if constexpr (NIB) {
+          // the 4 tokens' dwords hold channels 8 hl .. + 7; one byte permute
+          // joins two tokens' low (high) halves, whose nibble pairs are then
+          // (token t, token t+1) of channel j (4 + j)
+          const uint32_t u0 = dw(rv[s][0], 0), u1 = dw(rv[s][1], 0);
+          const uint32_t u2 = dw(rv[s][2], 0), u3 = dw(rv[s][3], 0);
+          const uint32_t l01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
+          const uint32_t h01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
+          const uint32_t l23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x05040100u));
+          const uint32_t h23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x07060302u));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                cat4(C::nib_pair(l01, j), C::nib_pair(l23, j)), wb, acc[j], 0, 0, 0);
+            acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                cat4(C::nib_pair(h01, j), C::nib_pair(h23, j)), wb, acc[4 + j], 0, 0, 0);
+          }
+        } else {
 #pragma unroll
         for (int k = 0; k < NVD; ++k) {
           const uint32_t x0 = C::pre(dw(rv[s][0], k)), x1 = C::pre(dw(rv[s][1], k));
@@ -573,6 +611,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
           acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
           acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
+        }
         }
       }
       issue(s, i + kPf);
@@ -613,9 +652,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
 }
 
 template <int D, int G, bool QF32, class C, bool ONEPASS>
+constexpr auto pick_kernel() {
+  if constexpr (ONEPASS) return decode_mfma1_kernel<D, G, QF32, C>;
+  else return decode_mfma2_kernel<D, G, QF32, C>;
+}
+
+template <int D, int G, bool QF32, class C, bool ONEPASS>
 bool launch_one(const SplitArgs& a, hipStream_t stream) {
-  constexpr auto kernel = ONEPASS ? decode_mfma1_kernel<D, G, QF32, C>
-                                  : decode_mfma2_kernel<D, G, QF32, C>;
+  constexpr auto kernel = pick_kernel<D, G, QF32, C, ONEPASS>();
   const int smem = ONEPASS ? msmem_layout(G, D).total : m2smem_layout(a.split_tokens, G, D).total;
   SplitArgs args = a;
   const int64_t grid = item_grid<kernel>(kThreads, smem, a.batch,
@@ -650,6 +694,11 @@ template <bool ONEPASS>
 bool by_fmt(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt, hipStream_t stream) {
   if (fmt == kFmtFp8) return by_dim<CodesFp8, ONEPASS>(head_dim, q_f32, G, a, stream);
   if (fmt == kFmtInt8) return by_dim<CodesInt8, ONEPASS>(head_dim, q_f32, G, a, stream);
+  if constexpr (ONEPASS) {   // 4-bit codes: the one-pass form at d = 128
+    if (fmt == kFmtInt4 && head_dim == 128)
+      return q_f32 ? by_group<128, true, CodesInt4, true>(G, a, stream)
+                   : by_group<128, false, CodesInt4, true>(G, a, stream);
+  }
   return false;
 }
 

@@ -103,6 +103,7 @@ def decode_parity(case, tokens_per_split=0, cache_from="oracle"):
     return out, host
 
 
+@pytest.mark.usefixtures("decode_kernel")
 @pytest.mark.parametrize("hq,hkv,d,qdt", [
     (4, 4, 128, "bf16"), (8, 4, 64, "f32"), (16, 2, 128, "f32"), (64, 8, 128, "bf16"),
     (8, 1, 64, "bf16"), (32, 8, 128, "f32"),
@@ -115,15 +116,18 @@ def test_int4_decode_group_sizes_dims_q_dtypes(hq, hkv, d, qdt):
     decode_parity(case, tokens_per_split=64)
 
 
+@pytest.mark.usefixtures("decode_kernel")
 @pytest.mark.parametrize("tps", [0, 64, 320, 2048])
 def test_int4_decode_llama8b_splits(tps):
     decode_parity(W.llama8b_decode(batch=4), tokens_per_split=tps)
 
 
+@pytest.mark.usefixtures("decode_kernel")
 def test_int4_decode_llama8b_full_batch_gpu_cache():
     decode_parity(W.llama8b_decode(), cache_from="gpu")
 
 
+@pytest.mark.usefixtures("decode_kernel")
 def test_int4_decode_single_token_and_poisoned_slots():
     case = W.make_paged_case(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
                              context_lens=[1, 23, 40], q_dtype="f32", seed=63, spare_blocks=2)
