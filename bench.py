@@ -288,6 +288,8 @@ def main():
             result["fp8_kv"]["prefill"] = bench_prefill(args, dev, fp8=True)
     if args.fp8_steps > 0:
         result["int4_kv"] = {"decode": bench_code_decode(args, dev, case, "int4")}
+        if args.prefill_steps > 0:
+            result["int4_kv"]["prefill"] = bench_prefill(args, dev, int4=True)
     if args.sweep_layers > 0:
         result["llama70b_sweep"] = bench_sweep70b(args, dev)
     if args.budget_steps > 0:
@@ -297,8 +299,8 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_prefill(args, dev, fp8=False):
-    """Chunked prefill over the INT8 (or FP8) cache (batch 8, 32/8 heads,
+def bench_prefill(args, dev, fp8=False, int4=False):
+    """Chunked prefill over the INT8 (or FP8, or INT4) cache (batch 8, 32/8 heads,
     d=128, 2048..8192 earlier tokens + a 512-row causal chunk): per step,
     append the chunk's own K/V (4096 tokens), then the prefill call.  HIP
     events on the stream the library launches on."""
@@ -312,9 +314,12 @@ def bench_prefill(args, dev, fp8=False):
     mask = case.extra["chunk_mask"]
     k_all = torch.from_numpy(case.k_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     v_all = torch.from_numpy(case.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    append = B.kv8_quant_append_fp8 if fp8 else B.kv8_quant_append
-    prefill = B.paged_prefill_chunk_attn_fp8kv if fp8 else B.paged_prefill_chunk_attn_kv8
-    cache = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=fp8)
+    fmt = "int4" if int4 else ("fp8" if fp8 else "kv8")
+    append = {"int4": B.kv8_quant_append_int4, "fp8": B.kv8_quant_append_fp8,
+              "kv8": B.kv8_quant_append}[fmt]
+    prefill = {"int4": B.paged_prefill_chunk_attn_int4kv, "fp8": B.paged_prefill_chunk_attn_fp8kv,
+               "kv8": B.paged_prefill_chunk_attn_kv8}[fmt]
+    cache = B.alloc_cache(case.num_blocks, hkv, d, dev, fp8=fp8, int4=int4)
     append(k_all, v_all, torch.from_numpy(case.slot_mapping).to(dev), *cache)
     sel = torch.from_numpy(np.nonzero(mask)[0]).to(dev)
     k_new = k_all.index_select(0, sel).contiguous()
@@ -351,7 +356,8 @@ def bench_prefill(args, dev, fp8=False):
     flops = prefill_flops(ctx, np.full(len(ctx), chunk), hq, d)
     tf = flops / (float(pre.mean()) * 1e-3) / 1e12
     return {"workload": "chunked prefill: B=8, Hq=32, Hkv=8, d=128, ctx_prev~U[2048,8192] + "
-                        f"512-row causal chunk, bf16 Q, {'fp8 e4m3' if fp8 else 'int8'} KV cache",
+                        f"512-row causal chunk, bf16 Q, "
+                        f"{ {'int4': 'int4', 'fp8': 'fp8 e4m3', 'kv8': 'int8'}[fmt]} KV cache",
             "steps": args.prefill_steps,
             "prefill_us": {"mean": round(float(pre.mean()) * 1e3, 2),
                            "p50": round(float(np.percentile(pre, 50)) * 1e3, 2)},
@@ -359,9 +365,8 @@ def bench_prefill(args, dev, fp8=False):
             "flops_per_call": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": None if fp8 else measured_traffic("prefill"),
-                         "kernel": ("paged_prefill_chunk_attn_fp8kv" if fp8 else
-                                    "paged_prefill_chunk_attn_kv8") + " (fp16 MFMA 32x32x16)"}}
+                         "traffic": measured_traffic("prefill") if fmt == "kv8" else None,
+                         "kernel": prefill.__name__ + " (fp16 MFMA 32x32x16)"}}
 
 
 def bench_code_decode(args, dev, case, fmt):

@@ -388,10 +388,11 @@ int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc
  * Two codes per byte as 4-bit two's complement, element 2i in the low
  * nibble of byte i: codes [num_blocks, Hkv, 16, d/2] bytes; one fp16 scale
  * per (token slot, KV head) for K and for V as in the INT8 cache.
- * kv8_quant_append_int4 and paged_decode_attn_int4kv take the same
- * arguments, with the same meaning, ownership and errors, as
- * kv8_quant_append and paged_decode_attn_kv8 (the decode workspace is sized
- * by kv8_decode_workspace_size).
+ * kv8_quant_append_int4, paged_decode_attn_int4kv and
+ * paged_prefill_chunk_attn_int4kv take the same arguments, with the same
+ * meaning, ownership and errors, as kv8_quant_append, paged_decode_attn_kv8
+ * and paged_prefill_chunk_attn_kv8 (the decode workspace is sized by
+ * kv8_decode_workspace_size).
  */
 int kv8_quant_append_int4(const uint16_t* k_new, const uint16_t* v_new,
                           const int32_t* slot_mapping, int64_t n_tokens,
@@ -411,6 +412,18 @@ int paged_decode_attn_int4kv(const void* q, int q_dtype,
                              int head_dim, int block_size, float sm_scale,
                              float* out, void* workspace, size_t workspace_bytes,
                              int tokens_per_split, void* stream);
+
+int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_loc,
+                                    int64_t total_q, int max_q_len,
+                                    const uint8_t* k_cache, const uint8_t* v_cache,
+                                    const uint16_t* k_scale, const uint16_t* v_scale,
+                                    int64_t num_blocks,
+                                    const int32_t* block_table, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len,
+                                    int batch, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int block_size, float sm_scale,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 #ifdef __cplusplus
 }

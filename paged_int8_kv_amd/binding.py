@@ -29,6 +29,7 @@ EXPORTED = (
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
     "kv8_quant_append_int4", "paged_decode_attn_int4kv", "kv8_set_decode_kernel",
+    "paged_prefill_chunk_attn_int4kv",
 )
 
 _lib = None
@@ -94,6 +95,8 @@ def load():
                                                  vp, vp, sz, vp]
     lib.paged_prefill_chunk_attn_fp8kv.restype = i32
     lib.paged_prefill_chunk_attn_fp8kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
+    lib.paged_prefill_chunk_attn_int4kv.restype = i32
+    lib.paged_prefill_chunk_attn_int4kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
     _lib = lib
     return lib
 
@@ -301,6 +304,15 @@ def paged_prefill_chunk_attn_fp8kv(q, q_start_loc, max_q_len, k_cache, v_cache, 
                                    workspace=None, sm_scale=None, stream=None):
     """As paged_prefill_chunk_attn_kv8, over an FP8 (e4m3) cache."""
     _prefill("paged_prefill_chunk_attn_fp8kv", q, q_start_loc, max_q_len, k_cache, v_cache,
+             k_scale, v_scale, block_table, context_lens, max_context_len, out, workspace,
+             sm_scale, stream)
+
+
+def paged_prefill_chunk_attn_int4kv(q, q_start_loc, max_q_len, k_cache, v_cache, k_scale,
+                                    v_scale, block_table, context_lens, max_context_len, out,
+                                    workspace=None, sm_scale=None, stream=None):
+    """As paged_prefill_chunk_attn_kv8, over an INT4 (nibble-packed) cache."""
+    _prefill("paged_prefill_chunk_attn_int4kv", q, q_start_loc, max_q_len, k_cache, v_cache,
              k_scale, v_scale, block_table, context_lens, max_context_len, out, workspace,
              sm_scale, stream)
 

@@ -358,4 +358,21 @@ int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc
                       workspace_bytes, kv8::kFmtFp8, stream);
 }
 
+int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_loc,
+                                    int64_t total_q, int max_q_len, const uint8_t* k_cache,
+                                    const uint8_t* v_cache, const uint16_t* k_scale,
+                                    const uint16_t* v_scale, int64_t num_blocks,
+                                    const int32_t* block_table, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len, int batch,
+                                    int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, float sm_scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, q_start_loc, total_q, max_q_len,
+                      reinterpret_cast<const int8_t*>(k_cache),
+                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
+                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
+                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
+                      workspace_bytes, kv8::kFmtInt4, stream);
+}
+
 }  // extern "C"

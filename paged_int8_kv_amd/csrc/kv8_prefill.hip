@@ -145,9 +145,12 @@ __device__ __forceinline__ float wave_sum32(float x) {
 // keys 16grp + 8a + 4hh + {0..3}, which sit at positions 8hh + 4a + {0..3}
 // of their group in the transposed layout.  Scales: threads 0..63 K,
 // 64..127 (wave 1) V.
-template <int D>
+// 4-bit codes (two per byte, element 2i in the low nibble of byte i) keep
+// the same thread roles with half the bytes: K d/16 bytes per thread, V
+// 2 bytes (4 channels) per row.
+template <int D, bool NIB = false>
 struct Stage {
-  static constexpr int kKBytes = D / 8;         // K code bytes per thread (16 or 8)
+  static constexpr int kKBytes = NIB ? D / 16 : D / 8;   // K code bytes per thread
   static constexpr int kVTasks = 4 * D;         // 512 (d=128) or 256 (d=64)
   uint32_t k[kKBytes / 4];
   uint32_t v[4];
@@ -162,31 +165,37 @@ __device__ __forceinline__ int64_t block_base(const PrefillArgs& a, const int32_
   return (int64_t)id * a.num_kv_heads + g;       // (block, KV head) slab index
 }
 
-template <int D>
+template <int D, bool NIB>
 __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* table_row,
                                            int kt, int last_blk, int g, int tid,
-                                           Stage<D>& st) {
+                                           Stage<D, NIB>& st) {
+  constexpr int RB = NIB ? D / 2 : D;           // code bytes per cache row
+  constexpr int KB = Stage<D, NIB>::kKBytes;
   {
     const int key = tid >> 3, part = tid & 7;
     const int64_t slab = block_base<D>(a, table_row, kt * 4 + (key >> 4), last_blk, g);
-    const int8_t* src = a.k_cache + slab * (kBlock * D) + (key & 15) * D + part * (D / 8);
-    if constexpr (D == 128) {
+    const int8_t* src = a.k_cache + slab * (kBlock * RB) + (key & 15) * RB + part * KB;
+    if constexpr (KB == 16) {
       const uint4 u = *reinterpret_cast<const uint4*>(src);
       st.k[0] = u.x; st.k[1] = u.y; st.k[2] = u.z; st.k[3] = u.w;
-    } else {
+    } else if constexpr (KB == 8) {
       const uint2 u = *reinterpret_cast<const uint2*>(src);
       st.k[0] = u.x; st.k[1] = u.y;
+    } else {
+      st.k[0] = *reinterpret_cast<const uint32_t*>(src);
     }
   }
-  if (tid < Stage<D>::kVTasks) {
+  if (tid < Stage<D, NIB>::kVTasks) {
     const int cq = tid % (D / 4), kq = tid / (D / 4);
     const int grp = kq >> 2, sub = kq & 3;
     const int64_t slab = block_base<D>(a, table_row, kt * 4 + grp, last_blk, g);
-    const int8_t* base = a.v_cache + slab * (kBlock * D) + cq * 4;
+    const int8_t* base = a.v_cache + slab * (kBlock * RB) + cq * (NIB ? 2 : 4);
     const int row0 = 8 * (sub >> 1) + 4 * (sub & 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      st.v[r] = *reinterpret_cast<const uint32_t*>(base + (row0 + r) * D);
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (NIB) st.v[r] = *reinterpret_cast<const uint16_t*>(base + (row0 + r) * RB);
+      else st.v[r] = *reinterpret_cast<const uint32_t*>(base + (row0 + r) * RB);
+    }
   }
   if (tid < 2 * kTileKeys) {
     const int key = tid & 63;
@@ -198,23 +207,59 @@ __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* 
 
 template <int D, class C>
 __device__ __forceinline__ void stage_store(Lds<D>& lds, int buf, int kt, int n_keys, int tid,
-                                            float k_mult, const Stage<D>& st) {
+                                            float k_mult,
+                                            const Stage<D, C::kBits == 4>& st) {
+  constexpr bool NIB = C::kBits == 4;
   {
     const int key = tid >> 3, part = tid & 7;
-    uint32_t o[Stage<D>::kKBytes / 2];
+    uint32_t o[D / 16];                         // the thread's d/8 channels as fp16 pairs
+    if constexpr (NIB) {
+      // dword j: channels 8j .. 8j+7 as nibbles; pair m (channels 2m, 2m+1)
+      // takes byte m's low nibble from x and its high nibble from x >> 4
 #pragma unroll
-    for (int j = 0; j < Stage<D>::kKBytes / 4; ++j) {
-      half2_t lo, hi;
-      codes_to_f16<C>(st.k[j], lo, hi);
-      o[2 * j] = h2_bits(lo);
-      o[2 * j + 1] = h2_bits(hi);
+      for (int j = 0; j < Stage<D, true>::kKBytes / 4; ++j) {
+        const uint32_t x = C::pre(st.k[j]), xs = x >> 4;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const uint32_t sel = 0x0C000C00u | ((4u + mm) << 16) | (uint32_t)mm;   // [x.b_m, 0, xs.b_m, 0]
+          const uint32_t t = (__builtin_amdgcn_perm(xs, x, sel) & 0x000F000Fu) | 0x64006400u;
+          o[4 * j + mm] = h2_bits(C::exact(__builtin_bit_cast(half2_t, t)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < Stage<D>::kKBytes / 4; ++j) {
+        half2_t lo, hi;
+        codes_to_f16<C>(st.k[j], lo, hi);
+        o[2 * j] = h2_bits(lo);
+        o[2 * j + 1] = h2_bits(hi);
+      }
     }
     uint4* dst = reinterpret_cast<uint4*>(&lds.k[buf][key][part * (D / 8)]);
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kKBytes / 8; ++i)
+    for (int i = 0; i < D / 64; ++i)
       dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
-  if (tid < Stage<D>::kVTasks) {
+  if constexpr (NIB) {
+    if (tid < Stage<D, true>::kVTasks) {
+      const int cq = tid % (D / 4), kq = tid / (D / 4);
+      const int grp = kq >> 2, sub = kq & 3;
+      const int a4 = sub >> 1, hh = sub & 1;
+      // rows r, r+1 side by side: nibble ci of each half is channel ci of
+      // that row, so nibble pair ci is (row r, row r+1) of channel 4 cq + ci
+      const uint32_t u01 = C::pre(st.v[0] | (st.v[1] << 16));
+      const uint32_t u23 = C::pre(st.v[2] | (st.v[3] << 16));
+#pragma unroll
+      for (int ci = 0; ci < 4; ++ci) {
+        const half2_t p01 = C::exact(C::nib_pair(u01, ci));
+        const half2_t p23 = C::exact(C::nib_pair(u23, ci));
+        const int row = cq * 4 + ci;
+        *reinterpret_cast<uint2*>(
+            &lds.v[buf][row][8 * ((grp * 2 + hh) ^ vt_swizzle(row)) + 4 * a4]) =
+            make_uint2(h2_bits(p01), h2_bits(p23));
+      }
+    }
+  } else if (tid < Stage<D>::kVTasks) {
     const int cq = tid % (D / 4), kq = tid / (D / 4);
     const int grp = kq >> 2, sub = kq & 3;
     const int a4 = sub >> 1, hh = sub & 1;
@@ -407,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int last_blk = n_keys > 0 ? (n_keys - 1) / kBlock : 0;
   const int32_t* table_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
 
-  Stage<D> st;
+  Stage<D, C::kBits == 4> st;
   if (nkt > 0) stage_load<D>(a, table_row, 0, last_blk, g, tid, st);
 
   // ---- this lane's query: load Q, exact fp16 after a power-of-two scale ----
@@ -616,7 +661,11 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
   a.num_kv_heads = num_kv_heads;
   a.sm_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
-  if (fmt == kFmtInt4) return -2;
+  if (fmt == kFmtInt4) {
+    if (head_dim == 128) return launch_d<128, CodesInt4>(a, G, batch, max_q_len, stream);
+    if (head_dim == 64) return launch_d<64, CodesInt4>(a, G, batch, max_q_len, stream);
+    return -2;
+  }
   const bool fp8 = fmt == kFmtFp8;
   if (head_dim == 128) return fp8 ? launch_d<128, CodesFp8>(a, G, batch, max_q_len, stream)
                                   : launch_d<128, CodesInt8>(a, G, batch, max_q_len, stream);

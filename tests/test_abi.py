@@ -274,3 +274,11 @@ def test_decode_workspace_covers_every_form():
     ws = B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 0)
     assert ws == B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 1024)
     assert ws > B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 2048)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qsl=None), dict(vc=None), dict(b=0), dict(tq=-1), dict(hq=31), dict(d=96),
+    dict(q=MIS), dict(tq=0),
+])
+def test_int4_prefill_validation_matches_int8(kw):
+    assert prefill(fn="paged_prefill_chunk_attn_int4kv", **kw) == prefill(**kw)

@@ -1,9 +1,10 @@
 """The INT4 cache on the GPU: kv8_quant_append_int4 bit-exact with the
 oracle's INT4 quantiser and nibble packing (every bf16 value under fixed
 scales, skipped slots, the Llama-3.1-8B-shaped batch), and
-paged_decode_attn_int4kv within tolerance of the oracle over the same
-dequantised cache (group sizes, head dims, q dtypes, split sizes, the full
-batch over a GPU-written cache, poisoned slots, single-token exactness)."""
+paged_decode_attn_int4kv and paged_prefill_chunk_attn_int4kv within
+tolerance of the oracle over the same dequantised cache (group sizes, head
+dims, q dtypes, split sizes, the full batch over a GPU-written cache,
+poisoned slots, single-token exactness; ragged prefill chunks)."""
 import numpy as np
 import pytest
 import torch
@@ -147,3 +148,39 @@ def test_int4_decode_single_token_and_poisoned_slots():
     v0 = O.gather_dequant_int4(vc, vs, case.block_table[0], 1, 0)[0]
     for h in range(4):
         assert np.array_equal(out[0, h], v0.astype(np.float32))
+
+
+# ---- prefill --------------------------------------------------------------
+def gpu_prefill_int4(case, cache):
+    q = bits_tensor(case.q_bits).view(torch.bfloat16)
+    qsl = np.ascontiguousarray(case.extra["q_start_loc"], np.int32)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev())
+    B.paged_prefill_chunk_attn_int4kv(
+        q, torch.from_numpy(qsl).to(dev()), int(np.max(np.diff(qsl))),
+        *cache, torch.from_numpy(case.block_table).to(dev()),
+        torch.from_numpy(case.context_lens).to(dev()), int(case.context_lens.max()), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def prefill_parity_int4(case, what, cache_from="oracle"):
+    host = oracle_cache_int4(case)
+    cache = upload_int4(*host) if cache_from == "oracle" else gpu_append_int4(case)
+    out = gpu_prefill_int4(case, cache)
+    ref = O.paged_prefill_chunk_int4(case.q, case.extra["q_start_loc"], *host, case.block_table,
+                                     case.context_lens)
+    check_close(out, ref, what)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (16, 2, 128), (32, 8, 128), (8, 8, 128)])
+def test_int4_prefill_ragged(hq, hkv, d):
+    case = W.prefill_case([0, 5, 1000, 17], [1, 77, 300, 0], num_q_heads=hq, num_kv_heads=hkv,
+                          head_dim=d, seed=hq * 5 + d + 3, k_outliers=True)
+    prefill_parity_int4(case, f"int4 prefill hq={hq} hkv={hkv} d={d}")
+
+
+def test_int4_prefill_chunked_config_reduced_batch_gpu_cache():
+    """The chunked-prefill shape (2 sequences), cache and chunk written by the
+    GPU's INT4 append."""
+    prefill_parity_int4(W.chunked_prefill(batch=2), "int4 chunked prefill batch 2",
+                        cache_from="gpu")
