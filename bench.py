@@ -45,6 +45,8 @@ def parse():
                    help="0 skips the FP8 (e4m3) and INT4 cache lines")
     p.add_argument("--sweep-layers", type=int, default=80,
                    help="layers of the Llama-3-70B-shaped decode sweep (0 skips it)")
+    p.add_argument("--long-steps", type=int, default=64,
+                   help="decode steps of the long-context leg, 4 x 32768 tokens (0 skips it)")
     p.add_argument("--budget-steps", type=int, default=10,
                    help="decode calls timed per side of the 258K equal-budget comparison "
                         "(0 skips it)")
@@ -290,6 +292,8 @@ def main():
         result["int4_kv"] = {"decode": bench_code_decode(args, dev, case, "int4")}
         if args.prefill_steps > 0:
             result["int4_kv"]["prefill"] = bench_prefill(args, dev, int4=True)
+    if args.long_steps > 0:
+        result["long_context"] = bench_long_context(args, dev)
     if args.sweep_layers > 0:
         result["llama70b_sweep"] = bench_sweep70b(args, dev)
     if args.budget_steps > 0:
@@ -418,6 +422,74 @@ def bench_code_decode(args, dev, case, fmt):
                         "cache, decode launches back to back", "decode_us": round(us, 2),
             "bytes_per_launch": nbytes, "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "kv_tokens_per_s": round(float(ctx.sum()) / (us * 1e-6), 1)}
+
+
+def bench_long_context(args, dev, batch=4, ctx0=32768):
+    """Long-context decode with append: 4 sequences of 32768 tokens, 32/8
+    heads, d=128, fp32 q; each step appends one token per sequence and
+    decodes over the grown context in one launch
+    (paged_decode_attn_kv8_append), `long_steps` steps back to back.  K/V/q
+    are drawn N(0, 1) on the device (torch.Generator seeded 3000), the
+    context quantised by the append kernel; the block table is a random
+    permutation (numpy PCG64 seeded 3) with room for every step."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    steps, hq, hkv, d = args.long_steps, 32, 8, 128
+    ctx_max = ctx0 + steps
+    bps = -(-ctx_max // 16)
+    nb = batch * bps
+    rng = np.random.Generator(np.random.PCG64(3))
+    table_np = rng.permutation(nb).astype(np.int32).reshape(batch, bps)
+    pos = np.arange(ctx0)
+    slots_np = np.concatenate([table_np[b][pos // 16] * 16 + pos % 16 for b in range(batch)])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3000)
+    cache = B.alloc_cache(nb, hkv, d, dev)
+    for b in range(batch):      # one sequence at a time keeps the bf16 staging small
+        k = torch.randn((ctx0, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((ctx0, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        sl = torch.from_numpy(np.ascontiguousarray(slots_np[b * ctx0:(b + 1) * ctx0])).to(dev)
+        B.kv8_quant_append(k, v, sl, *cache)
+        del k, v
+    k_new = torch.randn((steps, batch, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((steps, batch, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    q = torch.randn((steps, batch, hq, d), generator=gen, device=dev)
+    lens_np = ctx0 + 1 + np.arange(steps, dtype=np.int32)[:, None].repeat(batch, 1)
+    lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
+    table = torch.from_numpy(table_np).to(dev)
+    ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx_max), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev)
+
+    def run():
+        for s in range(steps):
+            B.paged_decode_attn_kv8_append(q[s], k_new[s], v_new[s], *cache, table, lens[s],
+                                           ctx_max, out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    us = float(np.median(times)) * 1e3 / steps
+    nbytes = float(np.mean([decode_bytes(lens_np[s], hkv, d, hq, 4) for s in range(steps)]))
+    nbytes += append_bytes(batch, hkv, d)
+    tokens = float(lens_np.sum()) / steps
+    del cache, k_new, v_new, q, ws, out
+    torch.cuda.empty_cache()
+    return {"workload": f"long-context decode with append: B={batch}, Hq={hq}, Hkv={hkv}, d={d}, "
+                        f"ctx {ctx0} + 1 token per sequence per step, fp32 q, {steps} steps "
+                        "back to back (paged_decode_attn_kv8_append)",
+            "us_per_step": round(us, 2), "bytes_per_step": int(nbytes),
+            "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / 8000 * 100, 2),
+            "kv_tokens_per_s": round(tokens / (us * 1e-6), 1)}
 
 
 def bench_sweep70b(args, dev):
