@@ -457,14 +457,14 @@ def bench_long_context(args, dev, batch=4, ctx0=32768):
     lens_np = ctx0 + 1 + np.arange(steps, dtype=np.int32)[:, None].repeat(batch, 1)
     lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
     table = torch.from_numpy(table_np).to(dev)
-    ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx_max), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx_max, args.tokens_per_split),
+                     dtype=torch.uint8, device=dev)
     out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev)
 
     def run():
         for s in range(steps):
             B.paged_decode_attn_kv8_append(q[s], k_new[s], v_new[s], *cache, table, lens[s],
-                                           ctx_max, out, ws)
+                                           ctx_max, out, ws, tokens_per_split=args.tokens_per_split)
 
     run()
     torch.cuda.synchronize()

@@ -97,9 +97,9 @@ int kv8_version(void);
  * used by paged_decode_attn_kv8, paged_decode_attn_kv8_append and
  * paged_decode_attn_fp8kv, for this process (all threads, all devices).
  *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv
- *            and grid size (v_dot2 below G = 4; at G = 4 two-pass
- *            matrix-core while the grid bound, every sequence at
- *            max_context_len in 1024-token splits, is at most 4096
+ *            and size (v_dot2 below G = 4; at G = 4 two-pass matrix-core
+ *            for max_context_len <= 8192 with a grid bound, every sequence
+ *            at max_context_len in 1024-token splits, of at most 4096
  *            workgroups, else one-pass; one-pass matrix-core from G = 8);
  *          KV8_DECODE_DOT  (1): the v_dot2 kernel;
  *          KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of

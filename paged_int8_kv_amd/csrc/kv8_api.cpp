@@ -78,7 +78,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                         kv8::decode_form(fmt, num_q_heads / num_kv_heads,
                                          (long long)batch * num_kv_heads *
                                              ((max_context_len + 1023) / 1024),
-                                         head_dim),
+                                         max_context_len, head_dim),
                         &plan))
     return KV8_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;

@@ -478,16 +478,18 @@ void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_ord
 // - G = 8: the two-pass form's logits take 50 KB of LDS per workgroup; the
 //   one-pass form keeps none and takes 2048-token splits (136.7 against
 //   159.7 us per layer of the Llama-3-70B-shaped sweep).
-// - G = 4, a grid of about one round of workgroups: the two-pass form, whose
-//   84 VGPRs leave room for five workgroups per CU (37.5 against 39.7 us on
-//   the Llama-3.1-8B-shaped batch, 1024 workgroups at most).
-// - G = 4, many rounds: the one-pass form (1513 against 1663 us on 15
-//   sequences of 264192 tokens, about 31000 workgroups).
+// - G = 4, short contexts (at most 8192 tokens) in a grid of about one
+//   round of workgroups: the two-pass form, whose 84 VGPRs leave room for
+//   five workgroups per CU (37.5 against 39.7 us on the Llama-3.1-8B-shaped
+//   batch: 1024..4096 tokens, 1024 workgroups at most).
+// - G = 4 otherwise: the one-pass form (58.4 against 67.4 us per step on 4
+//   sequences of 32768 tokens; 1513 against 1663 us on 15 sequences of
+//   264192 tokens, about 31000 workgroups).
 // `grid_bound` is the workgroup count with every sequence at the longest
 // context and 1024-token splits.
 // - INT4 codes: the one-pass form at d = 128 from G = 4 (any other
 //   setting or shape takes the v_dot2 kernel, the only other INT4 form).
-int decode_form(int fmt, int G, long long grid_bound, int head_dim) {
+int decode_form(int fmt, int G, long long grid_bound, int max_context_len, int head_dim) {
   const int k = g_decode_kernel.load(std::memory_order_relaxed);
   if (fmt == kFmtInt4) {
     const bool mfma = head_dim == 128 && (k == kDecodeKernelMfmaOnePass ||
@@ -496,7 +498,9 @@ int decode_form(int fmt, int G, long long grid_bound, int head_dim) {
   }
   if (k != kDecodeKernelAuto) return k;
   if (G >= 8) return kDecodeKernelMfmaOnePass;
-  if (G >= 4) return grid_bound > 4096 ? kDecodeKernelMfmaOnePass : kDecodeKernelMfma;
+  if (G >= 4)
+    return grid_bound <= 4096 && max_context_len <= 8192 ? kDecodeKernelMfma
+                                                         : kDecodeKernelMfmaOnePass;
   return kDecodeKernelDot;
 }
 

@@ -30,13 +30,14 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 // Which form of the INT8 / FP8 decode kernel launches: automatic (by group
 // size), the v_dot2 kernel, the two-pass or the one-pass matrix-core kernel.
 // Process-wide.  decode_form: the form a launch of this code format, group
-// size and grid bound (workgroups with every sequence at the longest context
-// and 1024-token splits) and head dim takes under the current setting.
+// size, grid bound (workgroups with every sequence at the longest context
+// and 1024-token splits), longest context and head dim takes under the
+// current setting.
 enum : int {
   kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3
 };
 void set_decode_kernel(int which);
-int decode_form(int fmt, int G, long long grid_bound, int head_dim);
+int decode_form(int fmt, int G, long long grid_bound, int max_context_len, int head_dim);
 
 struct DecodePlan {
   int form;              // kDecodeKernelDot / Mfma / MfmaOnePass
