@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma", "mfma1"], default="auto",
                    help="form of the INT8/FP8 decode kernel (auto: by group size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-read-ceiling", action="store_true",
+                   help="skip the read-only probe that measures the HBM read ceiling")
     p.add_argument("--cpu-steps", type=int, default=24,
                    help="oracle steps timed on the host (about 0.5 s each on 16 cores)")
     p.add_argument("--prefill-steps", type=int, default=20)
@@ -282,6 +284,10 @@ def main():
     }
     del caches, ws, out
     torch.cuda.empty_cache()
+    if not args.no_read_ceiling:
+        rc = bench_read_ceiling(dev, d_bytes)
+        result["read_ceiling"] = rc
+        result["roofline"]["frac_of_read_ceiling"] = round(dec_gbs / rc["gbs"], 4)
     if args.prefill_steps > 0:
         result["prefill"] = bench_prefill(args, dev)
     if args.fp8_steps > 0:
@@ -298,6 +304,11 @@ def main():
         result["llama70b_sweep"] = bench_sweep70b(args, dev)
     if args.budget_steps > 0:
         result["equal_budget_258k"] = bench_equal_budget(args, dev)
+    if "read_ceiling" in result:
+        ceil = result["read_ceiling"]["gbs"]
+        for leg in ("long_context", "llama70b_sweep"):
+            if leg in result:
+                result[leg]["frac_of_read_ceiling"] = round(result[leg]["kv_gbs"] / ceil, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_steps, d_bytes + a_bytes)
     print(json.dumps(result), flush=True)
@@ -422,6 +433,44 @@ def bench_code_decode(args, dev, case, fmt):
                         "cache, decode launches back to back", "decode_us": round(us, 2),
             "bytes_per_launch": nbytes, "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "kv_tokens_per_s": round(float(ctx.sum()) / (us * 1e-6), 1)}
+
+
+def bench_read_ceiling(dev, n_bytes, tile_bytes=2048, buffer_bytes=1 << 30, replicas=4,
+                       launches=100):
+    """The measured HBM read ceiling of the decode's access pattern: the
+    library's read-only probe (kv8_read_probe) streams about n_bytes per
+    launch as random tile_bytes tiles (one (block, KV head) code tile of the
+    decode) out of a 1 GiB buffer, rotating `replicas` tile orders, launches
+    back to back between HIP events on the current stream."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    per_wg = B.load().kv8_read_probe_bytes_per_workgroup()
+    wg = max(1, n_bytes // per_wg)
+    n_tiles_read = wg * per_wg // tile_bytes
+    n_tiles_buf = buffer_bytes // tile_bytes
+    buf = torch.zeros(buffer_bytes, dtype=torch.uint8, device=dev)
+    rng = np.random.Generator(np.random.PCG64(11))
+    orders = [torch.from_numpy(rng.permutation(n_tiles_buf)[:n_tiles_read].astype(np.int32)).to(dev)
+              for _ in range(replicas)]
+    out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+    for i in range(20):
+        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(launches):
+        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    read = wg * per_wg
+    del buf, orders, out
+    torch.cuda.empty_cache()
+    return {"kernel": "kv8_read_probe: read-only, random tiles, 32 KB per workgroup in flight",
+            "tile_bytes": tile_bytes, "buffer_bytes": buffer_bytes, "bytes_per_launch": int(read),
+            "us_per_launch": round(us, 2), "gbs": round(read / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(read / (us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100, 2)}
 
 
 def bench_long_context(args, dev, batch=4, ctx0=32768):

@@ -425,6 +425,28 @@ int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_lo
                                     float* out, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/*
+ * kv8_read_probe - measurement utility, not part of the attention method:
+ * the HBM read ceiling of the paged-decode access pattern on this device,
+ * against which the decode kernels' achieved bandwidth is reported.  One
+ * launch reads n_bytes = workgroups * kv8_read_probe_bytes_per_workgroup()
+ * bytes: logical 16-byte position p reads buf[tiles[p / (tile_bytes / 16)]
+ * * tile_bytes + (p % (tile_bytes / 16)) * 16], 32 KB per workgroup with all
+ * loads in flight, no arithmetic but an xor per thread written to `out`.
+ *   buf        device buffer of n_tiles * tile_bytes bytes (caller-owned;
+ *              make it far larger than the last-level cache)
+ *   tiles      device int32 [n_bytes / tile_bytes], each in [0, n_tiles)
+ *   tile_bytes a multiple of 16 that divides 32768
+ *   out        device uint32 [workgroups * 256]
+ * Returns KV8_OK, KV8_ERR_NULL, KV8_ERR_SHAPE (tile_bytes or workgroups out
+ * of range), KV8_ERR_ALIGN (buf not 16-byte aligned) or KV8_ERR_HIP.  Tile
+ * indices are not checked on the device: an index outside the buffer is
+ * undefined.  Asynchronous on `stream`.
+ */
+int64_t kv8_read_probe_bytes_per_workgroup(void);
+int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes,
+                   int64_t workgroups, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ EXPORTED = (
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
     "kv8_quant_append_int4", "paged_decode_attn_int4kv", "kv8_set_decode_kernel",
-    "paged_prefill_chunk_attn_int4kv",
+    "paged_prefill_chunk_attn_int4kv", "kv8_read_probe_bytes_per_workgroup", "kv8_read_probe",
 )
 
 _lib = None
@@ -95,6 +95,10 @@ def load():
                                                  vp, vp, sz, vp]
     lib.paged_prefill_chunk_attn_fp8kv.restype = i32
     lib.paged_prefill_chunk_attn_fp8kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
+    lib.kv8_read_probe_bytes_per_workgroup.restype = i64
+    lib.kv8_read_probe_bytes_per_workgroup.argtypes = []
+    lib.kv8_read_probe.restype = i32
+    lib.kv8_read_probe.argtypes = [vp, vp, i32, i64, vp, vp]
     lib.paged_prefill_chunk_attn_int4kv.restype = i32
     lib.paged_prefill_chunk_attn_int4kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
     _lib = lib
@@ -315,6 +319,22 @@ def paged_prefill_chunk_attn_int4kv(q, q_start_loc, max_q_len, k_cache, v_cache,
     _prefill("paged_prefill_chunk_attn_int4kv", q, q_start_loc, max_q_len, k_cache, v_cache,
              k_scale, v_scale, block_table, context_lens, max_context_len, out, workspace,
              sm_scale, stream)
+
+
+def kv8_read_probe(buf, tiles, tile_bytes, out, stream=None):
+    """Measurement utility: one launch of the read-only probe over `buf`
+    (uint8 device tensor) in the tile order `tiles` (int32); `out` uint32
+    [workgroups * 256] with workgroups = tiles.numel() * tile_bytes / bytes
+    per workgroup.  Returns the bytes the launch reads."""
+    lib = load()
+    per_wg = lib.kv8_read_probe_bytes_per_workgroup()
+    n_bytes = tiles.numel() * tile_bytes
+    wg = n_bytes // per_wg
+    if wg * 256 > out.numel():
+        raise ValueError("out too small")
+    _check(lib.kv8_read_probe(_ptr(buf), _ptr(tiles), int(tile_bytes), int(wg), _ptr(out),
+                              _stream(stream)), "kv8_read_probe")
+    return wg * per_wg
 
 
 def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False, int4=False):

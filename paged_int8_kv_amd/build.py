@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libkv8.so")
 ARCH = "gfx950"
 SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_decode_mfma.hip",
            "kv8_prefill.hip",
-           "kvbf16_decode.hip"]
+           "kvbf16_decode.hip", "kv8_probe.hip"]
 
 # Packed fp32 VALU instructions are kept out of the code object: the
 # compiler's automatic use of them is switched off for every HIP source.

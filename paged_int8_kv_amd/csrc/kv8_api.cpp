@@ -375,4 +375,21 @@ int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_lo
                       workspace_bytes, kv8::kFmtInt4, stream);
 }
 
+int64_t kv8_read_probe_bytes_per_workgroup(void) {
+  return kv8::read_probe_bytes_per_workgroup();
+}
+
+int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t workgroups,
+                   uint32_t* out, void* stream) {
+  if (!buf || !tiles || !out) return KV8_ERR_NULL;
+  const int64_t per_wg = kv8::read_probe_bytes_per_workgroup();
+  if (tile_bytes < 16 || tile_bytes % 16 != 0 || per_wg % tile_bytes != 0) return KV8_ERR_SHAPE;
+  if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return KV8_ERR_SHAPE;
+  if (!aligned16(buf)) return KV8_ERR_ALIGN;
+  return kv8::launch_read_probe(buf, tiles, tile_bytes, workgroups, out,
+                                static_cast<hipStream_t>(stream)) == 0
+             ? KV8_OK
+             : KV8_ERR_HIP;
+}
+
 }  // extern "C"

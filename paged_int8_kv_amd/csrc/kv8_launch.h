@@ -75,4 +75,9 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
                    int fmt, hipStream_t stream);
 
+// The read-only probe behind kv8_read_probe (kv8_probe.hip).
+int64_t read_probe_bytes_per_workgroup();
+int launch_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t workgroups,
+                      uint32_t* out, hipStream_t stream);
+
 }  // namespace kv8

@@ -282,3 +282,19 @@ def test_decode_workspace_covers_every_form():
 ])
 def test_int4_prefill_validation_matches_int8(kw):
     assert prefill(fn="paged_prefill_chunk_attn_int4kv", **kw) == prefill(**kw)
+
+
+def test_read_probe_validation():
+    """Host-side checks of the measurement probe: null pointers, tile sizes
+    that are not a multiple of 16 or do not divide the 32 KB per workgroup,
+    workgroup counts out of range, a misaligned buffer."""
+    lib = B.load()
+    assert lib.kv8_read_probe_bytes_per_workgroup() == 32768
+    assert lib.kv8_read_probe(None, P, 2048, 10, P2, None) == B.KV8_ERR_NULL
+    assert lib.kv8_read_probe(P, None, 2048, 10, P2, None) == B.KV8_ERR_NULL
+    assert lib.kv8_read_probe(P, P, 2048, 10, None, None) == B.KV8_ERR_NULL
+    for bad in (0, 8, 24, 3000, 65536):
+        assert lib.kv8_read_probe(P, P, bad, 10, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(P, P, 2048, 0, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(P, P, 2048, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(MIS, P, 2048, 10, P2, None) == B.KV8_ERR_ALIGN
