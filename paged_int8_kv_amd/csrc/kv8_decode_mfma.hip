@@ -1,6 +1,16 @@
-// Matrix-core form of paged_decode_attn_kv8 / paged_decode_attn_fp8kv:
-// split-K flash-decoding over the paged INT8 (or FP8 e4m3) cache on gfx950,
-// with both contractions of a block on MFMA.
+// Matrix-core forms of paged_decode_attn_kv8 / paged_decode_attn_fp8kv /
+// paged_decode_attn_int4kv: split-K flash-decoding over the paged INT8 (or
+// FP8 e4m3, or INT4) cache on gfx950, with both contractions of a block on
+// MFMA.  Two kernels share the per-block layouts below:
+//   decode_mfma2_kernel  two passes per split, as the dot-product kernel:
+//                        logits of the whole split to LDS, the exact split
+//                        max, fp16 weights to LDS, then the values;
+//   decode_mfma1_kernel  one pass with an online softmax: the logit MFMA's
+//                        output registers (token 4*(lane/16) + r, head
+//                        lane % 16) are exactly the value MFMA's B-operand
+//                        layout, so the weights never leave the registers
+//                        and no LDS is used until the cross-wave merge; it
+//                        also serves 4-bit codes at d = 128.
 //
 // Attention softmax(q K^T * sm_scale) V ("KV Cache 优化全景解析", section 2.1)
 // per GQA group (section 3.3) over K/V restored from INT8 codes and
@@ -37,8 +47,10 @@
 // pair, kv8_device.h); the bias is removed from the logits by starting the
 // accumulator at minus 1152 * sum(q_h) and from the outputs by 1152 * the sum
 // of the fp16 weights.  FP8 codes become exact fp16 by one hardware convert
-// per pair.  q enters as fp16 after an exact per-head power-of-two rescale;
-// an fp32 q is split into a high and a low fp16 part (two MFMAs).
+// per pair.  INT4 codes (one-pass kernel) enter as c + 1032: a flip of each
+// nibble's sign bit and one and-or with the fp16 pattern per nibble pair.  q
+// enters as fp16 after an exact per-head power-of-two rescale; an fp32 q is
+// split into a high and a low fp16 part (two MFMAs).
 #include "kv8_decode_common.h"
 #include "kv8_device.h"
 #include "kv8_launch.h"
