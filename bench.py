@@ -410,17 +410,19 @@ def bench_code_decode(args, dev, case, fmt):
     table = torch.from_numpy(case.block_table).to(dev)
     lens = torch.from_numpy(ctx).to(dev)
     out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
-    ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, max_ctx, args.tokens_per_split),
+                     dtype=torch.uint8, device=dev)
     n = max(args.steps, 50)
     for i in range(200):
-        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws,
+               tokens_per_split=args.tokens_per_split)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
-        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws)
+        decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws,
+               tokens_per_split=args.tokens_per_split)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
