@@ -112,9 +112,8 @@ int kv8_version(void);
  * merge); results agree within the attention tolerance, not bitwise.  The
  * form can change the default split size, hence the workspace a call needs;
  * kv8_decode_workspace_size returns enough for every form.  The INT4 decode
- * (paged_decode_attn_int4kv) has two forms: the one-pass matrix-core kernel
- * at d = 128 (AUTO from G = 4, or MFMA_ONEPASS) and the v_dot2 kernel
- * otherwise.  Takes effect for launches issued after the
+ * (paged_decode_attn_int4kv) runs all three forms at d = 128 (AUTO: one-pass
+ * from G = 4, else v_dot2) and the v_dot2 kernel at d = 64.  Takes effect for launches issued after the
  * call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED for another value (the
  * setting is then unchanged).
  */

@@ -487,16 +487,15 @@ void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_ord
 //   264192 tokens, about 31000 workgroups).
 // `grid_bound` is the workgroup count with every sequence at the longest
 // context and 1024-token splits.
-// - INT4 codes: the one-pass form at d = 128 from G = 4 (any other
-//   setting or shape takes the v_dot2 kernel, the only other INT4 form).
+// - INT4 codes: the matrix-core forms serve d = 128 only (the v_dot2
+//   kernel otherwise); from G = 4 the one-pass form (28.5 against 28.8 us
+//   for the two-pass form and 36.5 for v_dot2 on the Llama-3.1-8B-shaped
+//   batch; 1801 against 1971 and 2655 us on 31 sequences of 264192 tokens).
 int decode_form(int fmt, int G, long long grid_bound, int max_context_len, int head_dim) {
   const int k = g_decode_kernel.load(std::memory_order_relaxed);
-  if (fmt == kFmtInt4) {
-    const bool mfma = head_dim == 128 && (k == kDecodeKernelMfmaOnePass ||
-                                          (k == kDecodeKernelAuto && G >= 4));
-    return mfma ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
-  }
+  if (fmt == kFmtInt4 && head_dim != 128) return kDecodeKernelDot;
   if (k != kDecodeKernelAuto) return k;
+  if (fmt == kFmtInt4) return G >= 4 ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
   if (G >= 8) return kDecodeKernelMfmaOnePass;
   if (G >= 4)
     return grid_bound <= 4096 && max_context_len <= 8192 ? kDecodeKernelMfma
@@ -582,7 +581,6 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   const int G = num_q_heads / num_kv_heads;
   bool ok;
   if (plan.form != kDecodeKernelDot) {
-    if (fmt == kFmtInt4 && plan.form != kDecodeKernelMfmaOnePass) return -2;
     ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, plan.form == kDecodeKernelMfmaOnePass,
                             stream);
   } else if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);

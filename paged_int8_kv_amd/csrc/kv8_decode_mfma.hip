@@ -210,14 +210,74 @@ __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int 
   nqb = -C::kBias * qsum;
 }
 
+// The logit MFMA's A operand j of a block: the lane's 8 channels of MFMA j
+// (the same channels q_operands puts in B).  Byte codes: dwords 2(j%2) and
+// 2(j%2)+1 of 16-byte piece j/2.  4-bit codes: dword j of the lane's single
+// 16-byte piece, as nibble pairs (c, c+4).
+template <class C, int NCH>
+__device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) {
+  if constexpr (C::kBits == 4) {
+    const uint32_t x = C::pre(dw(rk[0], j));
+    return cat8(C::nib_pair(x, 0), C::nib_pair(x, 1), C::nib_pair(x, 2), C::nib_pair(x, 3));
+  } else {
+    const uint4 r = rk[j / 2];
+    const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
+    return cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+  }
+}
+
+// The value MFMAs of a block: acc[j] += A_j . wb with A_j the codes of
+// channel (D/16) hl + j for the 4 tokens whose rows the lane holds.  Byte
+// codes: one interleave per token pair and dword, then byte pairs.  4-bit
+// codes (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
+// permute joins two tokens' low (high) halves, whose nibble pairs are then
+// (token t, token t+1) of channel j (4 + j).
+template <class C, int NVT, class VRow>
+__device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
+                                            float4_t (&acc)[NVT]) {
+  if constexpr (C::kBits == 4) {
+    const uint32_t u0 = dw(rv[0], 0), u1 = dw(rv[1], 0);
+    const uint32_t u2 = dw(rv[2], 0), u3 = dw(rv[3], 0);
+    const uint32_t l01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
+    const uint32_t h01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
+    const uint32_t l23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x05040100u));
+    const uint32_t h23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x07060302u));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          cat4(C::nib_pair(l01, j), C::nib_pair(l23, j)), wb, acc[j], 0, 0, 0);
+      acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          cat4(C::nib_pair(h01, j), C::nib_pair(h23, j)), wb, acc[4 + j], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NVT / 4; ++k) {
+      const uint32_t x0 = C::pre(dw(rv[0], k)), x1 = C::pre(dw(rv[1], k));
+      const uint32_t x2 = C::pre(dw(rv[2], k)), x3 = C::pre(dw(rv[3], k));
+      const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
+      const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
+      const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
+      const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
+      const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
+      const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
+      acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
+      acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
+      acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
+      acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int G, bool QF32, class C>
 __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
-  static_assert(C::kBits == 8, "byte codes");
   static_assert(G >= 1 && G <= 16, "one 16-column tile of heads");
-  constexpr int NCH = D / 64;     // 16-byte K pieces per lane per block
+  constexpr bool NIB = C::kBits == 4;   // two 4-bit codes per byte
+  static_assert(!NIB || D == 128, "4-bit codes: d = 128");
+  constexpr int RB = NIB ? D / 2 : D;   // code bytes per cache row
+  constexpr int NCH = NIB ? 1 : D / 64; // 16-byte K pieces per lane per block
   constexpr int NKM = D / 32;     // logit MFMAs per block (per q part)
-  constexpr int NVT = D / 16;     // value tiles per block (= bytes per V row piece)
-  constexpr int NVD = NVT / 4;    // dwords of a lane's V row piece
+  constexpr int NVT = D / 16;     // value tiles per block (= channels of a lane's V piece)
+  constexpr int NVD = NIB ? 1 : NVT / 4;   // dwords of a lane's V row piece
   using VRow = typename VRowT<NVD>::type;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -255,8 +315,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
     id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
     s_blk[tid] = (int)id;
   }
-  if (a.k_new != nullptr && split == it.nsplit - 1 && wave == 0)
-    append_newest<D, C>(a, b, g, ctx, lane);
+  if constexpr (!NIB) {
+    if (a.k_new != nullptr && split == it.nsplit - 1 && wave == 0)
+      append_newest<D, C>(a, b, g, ctx, lane);
+  }
 
   // ---- q of head hl as the B operand of the logit MFMAs ------------------
   half8_t qb[NKM], qlo[QF32 ? NKM : 1];
@@ -285,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
     auto issue = [&](int s, int i) {
       const bool real = i <= last;                 // wave-uniform
       const int64_t row0 = row0_of(min(i, last));
-      const int8_t* p = a.k_cache + row0 * D + (real ? hl * D + 16 * q4 : 0);
+      const int8_t* p = a.k_cache + row0 * RB + (real ? hl * RB + 16 * q4 : 0);
       const int so = real ? 4 * q4 : 0;
 #pragma unroll
       for (int u = 0; u < NCH; ++u) rk[s][u] = *reinterpret_cast<const uint4*>(p + 64 * u);
@@ -304,9 +366,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
           float4_t acc = {nqb, nqb, nqb, nqb};
 #pragma unroll
           for (int j = 0; j < NKM; ++j) {
-            const uint4 r = rk[s][j / 2];
-            const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
-            const half8_t av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
+            const half8_t av = logit_operand<C>(rk[s], j);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j], acc, 0, 0, 0);
             if constexpr (QF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[j], acc, 0, 0, 0);
           }
@@ -336,8 +396,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
   VRow rv[kPf2][4];
   auto issue_v = [&](int s, int i) {
     const bool real = i <= last;                   // wave-uniform, as in pass 1
-    const int8_t* p = a.v_cache + row0_of(min(i, last)) * D + (real ? 4 * q4 * D + hl * NVT : 0);
-    const int stride = real ? D : 0;
+    const int8_t* p = a.v_cache + row0_of(min(i, last)) * RB +
+                      (real ? 4 * q4 * RB + hl * (NIB ? NVT / 2 : NVT) : 0);
+    const int stride = real ? RB : 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) rv[s][t] = *reinterpret_cast<const VRow*>(p + t * stride);
   };
@@ -402,21 +463,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
         if (hl < G)
           wb = *reinterpret_cast<const half4_t*>(
               s_w + ((wave + i * kWaves) * G + hl) * kBlock + 4 * q4);
-#pragma unroll
-        for (int k = 0; k < NVD; ++k) {
-          const uint32_t x0 = C::pre(dw(rv[s][0], k)), x1 = C::pre(dw(rv[s][1], k));
-          const uint32_t x2 = C::pre(dw(rv[s][2], k)), x3 = C::pre(dw(rv[s][3], k));
-          const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
-          const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
-          const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
-          const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
-          const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
-          const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
-          acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
-          acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
-          acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
-          acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
-        }
+        value_mfmas<C, NVT>(rv[s], wb, acc);
       }
       issue_v(s, i + kPf2);
     }
@@ -549,15 +596,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
         float4_t S = {nqb, nqb, nqb, nqb};
 #pragma unroll
         for (int j = 0; j < NKM; ++j) {
-          half8_t av;
-          if constexpr (NIB) {   // dword j: channels 32 q4 + 8j .. + 7 as nibble pairs (c, c+4)
-            const uint32_t x = C::pre(dw(rk[s][0], j));
-            av = cat8(C::nib_pair(x, 0), C::nib_pair(x, 1), C::nib_pair(x, 2), C::nib_pair(x, 3));
-          } else {
-            const uint4 r = rk[s][j / 2];
-            const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
-            av = cat8(C::lo(x0), C::hi(x0), C::lo(x1), C::hi(x1));
-          }
+          const half8_t av = logit_operand<C>(rk[s], j);
           S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j], S, 0, 0, 0);
           if constexpr (QF32) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qlo[j], S, 0, 0, 0);
         }
@@ -591,40 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           if constexpr (C::kBiased) p_run += (float)w[r];
         }
         const half4_t wb = {w[0], w[1], w[2], w[3]};
-        if constexpr (NIB) {
-          // the 4 tokens' dwords hold channels 8 hl .. + 7; one byte permute
-          // joins two tokens' low (high) halves, whose nibble pairs are then
-          // (token t, token t+1) of channel j (4 + j)
-          const uint32_t u0 = dw(rv[s][0], 0), u1 = dw(rv[s][1], 0);
-          const uint32_t u2 = dw(rv[s][2], 0), u3 = dw(rv[s][3], 0);
-          const uint32_t l01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
-          const uint32_t h01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
-          const uint32_t l23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x05040100u));
-          const uint32_t h23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x07060302u));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                cat4(C::nib_pair(l01, j), C::nib_pair(l23, j)), wb, acc[j], 0, 0, 0);
-            acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                cat4(C::nib_pair(h01, j), C::nib_pair(h23, j)), wb, acc[4 + j], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-        for (int k = 0; k < NVD; ++k) {
-          const uint32_t x0 = C::pre(dw(rv[s][0], k)), x1 = C::pre(dw(rv[s][1], k));
-          const uint32_t x2 = C::pre(dw(rv[s][2], k)), x3 = C::pre(dw(rv[s][3], k));
-          const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
-          const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
-          const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
-          const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
-          const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
-          const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
-          acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
-          acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
-          acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
-          acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
-        }
-        }
+        value_mfmas<C, NVT>(rv[s], wb, acc);
       }
       issue(s, i + kPf);
     }
@@ -706,11 +712,9 @@ template <bool ONEPASS>
 bool by_fmt(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt, hipStream_t stream) {
   if (fmt == kFmtFp8) return by_dim<CodesFp8, ONEPASS>(head_dim, q_f32, G, a, stream);
   if (fmt == kFmtInt8) return by_dim<CodesInt8, ONEPASS>(head_dim, q_f32, G, a, stream);
-  if constexpr (ONEPASS) {   // 4-bit codes: the one-pass form at d = 128
-    if (fmt == kFmtInt4 && head_dim == 128)
-      return q_f32 ? by_group<128, true, CodesInt4, true>(G, a, stream)
-                   : by_group<128, false, CodesInt4, true>(G, a, stream);
-  }
+  if (fmt == kFmtInt4 && head_dim == 128)   // 4-bit codes: d = 128
+    return q_f32 ? by_group<128, true, CodesInt4, ONEPASS>(G, a, stream)
+                 : by_group<128, false, CodesInt4, ONEPASS>(G, a, stream);
   return false;
 }
 

@@ -3,8 +3,9 @@ side of the rule, a launch under KV8_DECODE_AUTO must be bitwise the launch
 of the form the rule names:
 - v_dot2 below 4 query heads per KV head;
 - two-pass matrix-core at 4 for short contexts in a small grid;
-- one-pass matrix-core for long contexts, from 8 heads per KV head, and for
-  INT4 at d = 128.
+- one-pass matrix-core for long contexts and from 8 heads per KV head;
+- INT4: one-pass matrix-core from 4 heads per KV head at d = 128, v_dot2 at
+  d = 64.
 The named form must also differ from the other forms on that input, so that
 the comparison can tell them apart.  Each result is checked against the
 oracle too."""
@@ -53,17 +54,31 @@ def test_auto_form_int8(hq, hkv, lens, expected):
     check_close(outs["auto"], ref, f"auto form hq={hq} hkv={hkv}")
 
 
-def test_auto_form_int4():
-    """INT4 has two forms: one-pass matrix-core at d = 128 from G = 4, else
-    v_dot2 (the two-pass setting falls back to v_dot2)."""
-    case = W.make_paged_case(batch=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                             context_lens=[1200, 77, 2500], q_dtype="bf16", k_outliers=True,
-                             seed=91)
+@pytest.mark.parametrize("lens,expected", [([1200, 77, 2500], "mfma1"), ([9000, 300], "mfma1")])
+def test_auto_form_int4(lens, expected):
+    """INT4 at d = 128 and G = 4 takes the one-pass matrix-core form, short
+    or long contexts (the two-pass form is there on request)."""
+    case = W.make_paged_case(batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             context_lens=lens, q_dtype="bf16", k_outliers=True,
+                             seed=91 + sum(lens))
     host = oracle_cache_int4(case)
     cache = upload_int4(*host)
     outs = run_forms(lambda: gpu_decode_int4(case, cache))
-    assert np.array_equal(outs["auto"], outs["mfma1"])
-    assert np.array_equal(outs["mfma"], outs["dot"])
-    assert not np.array_equal(outs["mfma1"], outs["dot"])
+    assert np.array_equal(outs["auto"], outs[expected])
+    for other in FORMS:
+        if other != expected:
+            assert not np.array_equal(outs[expected], outs[other]), f"{expected} == {other}"
     ref = O.paged_decode_int4(case.q, *host, case.block_table, case.context_lens)
     check_close(outs["auto"], ref, "auto form int4")
+
+
+def test_int4_head_dim_64_takes_dot():
+    """The matrix-core forms serve INT4 at d = 128 only: at d = 64 every
+    setting runs the v_dot2 kernel."""
+    case = W.make_paged_case(batch=2, num_q_heads=16, num_kv_heads=4, head_dim=64,
+                             context_lens=[700, 33], q_dtype="bf16", seed=17)
+    host = oracle_cache_int4(case)
+    cache = upload_int4(*host)
+    outs = run_forms(lambda: gpu_decode_int4(case, cache))
+    for name in ("auto", "mfma", "mfma1"):
+        assert np.array_equal(outs[name], outs["dot"]), name
