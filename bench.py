@@ -47,6 +47,8 @@ def parse():
                    help="0 skips the FP8 (e4m3) and INT4 cache lines")
     p.add_argument("--sweep-layers", type=int, default=80,
                    help="layers of the Llama-3-70B-shaped decode sweep (0 skips it)")
+    p.add_argument("--fill-steps", type=int, default=20,
+                   help="calls of the append fill leg, 131072 tokens each (0 skips it)")
     p.add_argument("--long-steps", type=int, default=64,
                    help="decode steps of the long-context leg, 4 x 32768 tokens (0 skips it)")
     p.add_argument("--budget-steps", type=int, default=10,
@@ -298,6 +300,8 @@ def main():
         result["int4_kv"] = {"decode": bench_code_decode(args, dev, case, "int4")}
         if args.prefill_steps > 0:
             result["int4_kv"]["prefill"] = bench_prefill(args, dev, int4=True)
+    if args.fill_steps > 0:
+        result["append_fill"] = bench_append_fill(args, dev)
     if args.long_steps > 0:
         result["long_context"] = bench_long_context(args, dev)
     if args.sweep_layers > 0:
@@ -435,6 +439,46 @@ def bench_code_decode(args, dev, case, fmt):
                         "cache, decode launches back to back", "decode_us": round(us, 2),
             "bytes_per_launch": nbytes, "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "kv_tokens_per_s": round(float(ctx.sum()) / (us * 1e-6), 1)}
+
+
+def bench_append_fill(args, dev, n_tokens=131072, hkv=8, d=128):
+    """kv8_quant_append at fill size: 131072 new tokens (4 sequences of
+    32768, the long-context config's fill), 8 KV heads, d=128, bf16 K/V
+    drawn on the device, slots a random permutation of the cache (numpy
+    PCG64 seeded 13); calls back to back between HIP events."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    nb = n_tokens // 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+    k = torch.randn((n_tokens, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((n_tokens, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    rng = np.random.Generator(np.random.PCG64(13))
+    blocks = rng.permutation(nb).astype(np.int64)
+    slots_np = (blocks[:, None] * 16 + np.arange(16)[None, :]).reshape(-1).astype(np.int32)
+    slots = torch.from_numpy(slots_np).to(dev)
+    cache = B.alloc_cache(nb, hkv, d, dev)
+    for _ in range(3):
+        B.kv8_quant_append(k, v, slots, *cache)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.fill_steps):
+        B.kv8_quant_append(k, v, slots, *cache)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.fill_steps
+    nbytes = append_bytes(n_tokens, hkv, d)
+    del k, v, slots, cache
+    torch.cuda.empty_cache()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"kv8_quant_append fill: {n_tokens} tokens, Hkv={hkv}, d={d}, bf16 K/V, "
+                        "random block order, calls back to back",
+            "us_per_call": round(us, 2), "bytes_per_call": int(nbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "tokens_per_s": round(n_tokens / (us * 1e-6), 1)}
 
 
 def bench_read_ceiling(dev, n_bytes, tile_bytes=2048, buffer_bytes=1 << 30, replicas=4,
