@@ -143,6 +143,7 @@ __device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
 // ---------------------------------------------------------------------------
 struct CodesInt8 {
   static constexpr int kBits = 8;
+  static constexpr bool kIntCodes = true;   // code = clamp(rint(quotient))
   static constexpr bool kBiased = true;
   static constexpr float kBias = kCodeBias;
   static constexpr float kQmax = 127.0f;
@@ -153,15 +154,19 @@ struct CodesInt8 {
     const half2_t bias = {(_Float16)kCodeBias, (_Float16)kCodeBias};
     return p - bias;
   }
+  __device__ static uint32_t code_of_quotient(float q) {   // q = fl32(x / s)
+    float c = __builtin_rintf(q);                      // ties to even
+    c = fminf(fmaxf(c, -127.0f), 127.0f);
+    return (uint32_t)((int32_t)c) & 0xFFu;
+  }
   __device__ static uint32_t code(float x, float s) {
-    float q = __builtin_rintf(x / s);                 // IEEE divide, ties to even
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (uint32_t)((int32_t)q) & 0xFFu;
+    return code_of_quotient(x / s);                   // IEEE divide
   }
 };
 
 struct CodesFp8 {
   static constexpr int kBits = 8;
+  static constexpr bool kIntCodes = false;
   static constexpr bool kBiased = false;
   static constexpr float kBias = 0.0f;
   static constexpr float kQmax = 448.0f;
@@ -198,6 +203,7 @@ struct CodesFp8 {
 // nibbles j and j + 4 of the (already flipped) dword x.
 struct CodesInt4 {
   static constexpr int kBits = 4;
+  static constexpr bool kIntCodes = true;
   static constexpr bool kBiased = true;
   static constexpr float kBias = 1032.0f;
   static constexpr float kQmax = 7.0f;
@@ -209,10 +215,13 @@ struct CodesInt4 {
     const half2_t bias = {(_Float16)kBias, (_Float16)kBias};
     return p - bias;
   }
+  __device__ static uint32_t code_of_quotient(float q) {   // q = fl32(x / s)
+    float c = __builtin_rintf(q);                      // ties to even
+    c = fminf(fmaxf(c, -7.0f), 7.0f);
+    return (uint32_t)((int32_t)c) & 0xFu;
+  }
   __device__ static uint32_t code(float x, float s) {
-    float q = __builtin_rintf(x / s);                 // IEEE divide, ties to even
-    q = fminf(fmaxf(q, -7.0f), 7.0f);
-    return (uint32_t)((int32_t)q) & 0xFu;
+    return code_of_quotient(x / s);                   // IEEE divide
   }
 };
 
@@ -238,14 +247,46 @@ __device__ __forceinline__ float fp16_scale(float absmax) {
   return (float)s16;
 }
 
+// Integer codes rint(fl32(x / s)) of a lane's 8 values without a division
+// per value where that is provably the same.  q_a = x * rcp(s) (v_rcp_f32,
+// relative error <= 2^-23) differs from the specified fp32 quotient
+// fl32(x / s) by at most about 2^-21.6 |q|, so both round to the same
+// integer unless q_a lies within that distance of a half-integer; a lane
+// with any value within 2^-20 |q_a| of one (every exact tie among them)
+// takes the IEEE division for all 8.  Returns the quotients to round.
+template <int N>
+__device__ __forceinline__ void quotients(const float (&x)[N], float s, float (&q)[N]) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    q[i] = x[i] * r;
+    const float a = fabsf(q[i]);
+    near |= fabsf(__builtin_amdgcn_fractf(a) - 0.5f) <= a * 0x1p-20f;   // fract: a - floor(a), exact
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = x[i] / s;   // IEEE divide
+  }
+}
+
 template <class C>
 __device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
   uint32_t w0 = 0, w1 = 0;
   if (s != 0.0f) {
+    if constexpr (C::kIntCodes) {
+      float q[8];
+      quotients<8>(x, s, q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w0 |= C::code(x[i], s) << (8 * i);
+      for (int i = 0; i < 4; ++i) w0 |= C::code_of_quotient(q[i]) << (8 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w1 |= C::code(x[4 + i], s) << (8 * i);
+      for (int i = 0; i < 4; ++i) w1 |= C::code_of_quotient(q[4 + i]) << (8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w0 |= C::code(x[i], s) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w1 |= C::code(x[4 + i], s) << (8 * i);
+    }
   }
   return make_uint2(w0, w1);
 }
@@ -255,8 +296,10 @@ template <class C>
 __device__ __forceinline__ uint32_t quantise8_nibbles(const float (&x)[8], float s) {
   uint32_t w = 0;
   if (s != 0.0f) {
+    float q[8];
+    quotients<8>(x, s, q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= C::code(x[i], s) << (4 * i);
+    for (int i = 0; i < 8; ++i) w |= C::code_of_quotient(q[i]) << (4 * i);
   }
   return w;
 }
