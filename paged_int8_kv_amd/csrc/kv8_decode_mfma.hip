@@ -228,10 +228,17 @@ __device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) 
 
 // The value MFMAs of a block: acc[j] += A_j . wb with A_j the codes of
 // channel (D/16) hl + j for the 4 tokens whose rows the lane holds.  Byte
-// codes: one interleave per token pair and dword, then byte pairs.  4-bit
-// codes (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
+// codes: one interleave per token pair and dword, then byte pairs, biased
+// (INT8: c + 1152; the split removes 1152 * sum(w) at its end).  4-bit codes
+// (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
 // permute joins two tokens' low (high) halves, whose nibble pairs are then
-// (token t, token t+1) of channel j (4 + j).
+// (token t, token t+1) of channel j (4 + j); their bias is taken off here,
+// exactly, by one packed fp16 subtract per pair, because with codes of at
+// most 7 the biased sums over a long split would cancel away too many bits
+// (measured at 264K tokens: relative error 1.5e-3 with the bias kept).
+template <class C>
+constexpr bool value_bias_kept() { return C::kBiased && C::kBits == 8; }
+
 template <class C, int NVT, class VRow>
 __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
                                             float4_t (&acc)[NVT]) {
@@ -245,9 +252,11 @@ __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::nib_pair(l01, j), C::nib_pair(l23, j)), wb, acc[j], 0, 0, 0);
+          cat4(C::exact(C::nib_pair(l01, j)), C::exact(C::nib_pair(l23, j))), wb, acc[j], 0, 0,
+          0);
       acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::nib_pair(h01, j), C::nib_pair(h23, j)), wb, acc[4 + j], 0, 0, 0);
+          cat4(C::exact(C::nib_pair(h01, j)), C::exact(C::nib_pair(h23, j))), wb, acc[4 + j], 0,
+          0, 0);
     }
   } else {
 #pragma unroll
@@ -431,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
         const float p = __builtin_amdgcn_exp2f(z - Mh);
         p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
         lsum += p;
-        if constexpr (C::kBiased) psum += (float)p16;
+        if constexpr (value_bias_kept<C>()) psum += (float)p16;
       }
       const int jj = t / kBlock, r = t % kBlock;
       s_w[(jj * G + h) * kBlock + r] = p16;
@@ -479,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
     }
   }
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, C::kBiased>(
+  finish_split<G, D, kThreads, kWaves, value_bias_kept<C>()>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
       bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
 }
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           const float vs = fp16_bits_to_f32((uint16_t)(vw[r / 2] >> (16 * (r % 2))));
           w[r] = (_Float16)(tb + r < ntok ? p * vs : 0.0f);   // never reads a stale scale
           l_run += p;
-          if constexpr (C::kBiased) p_run += (float)w[r];
+          if constexpr (value_bias_kept<C>()) p_run += (float)w[r];
         }
         const half4_t wb = {w[0], w[1], w[2], w[3]};
         value_mfmas<C, NVT>(rv[s], wb, acc);
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
     }
   }
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, C::kBiased>(
+  finish_split<G, D, kThreads, kWaves, value_bias_kept<C>()>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
       bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
 }

@@ -171,3 +171,48 @@ def test_equal_budget_258k_sampled():
                 check_close(got[b, g * 4:(g + 1) * 4], ref, f"258K {kind} seq {b} head {g}")
         del w, table, lens, out, ws
         torch.cuda.empty_cache()
+
+
+def test_equal_budget_258k_int4_sampled():
+    """The INT4 side of the 258K equal-memory-budget comparison at full size:
+    the 31 sequences of 264,192 tokens that fit 8 bf16 sequences' bytes, as
+    the benchmark launches them (the automatic decode form).  On sequences
+    {0, last} and KV heads {0, 5}: packed codes and scales match the
+    oracle's INT4 quantiser bit for bit, and the decode matches the oracle's
+    attention over the same cache."""
+    hq, hkv, d, ctx = 32, 8, 128, 258 * 1024
+    budget = 8 * ctx * (2 * hkv * d * 2)
+    batch = budget // (ctx * 2 * hkv * (d // 2 + 2))
+    assert batch == 31
+    sm = 1.0 / np.sqrt(d)
+    w = W.long_context_258k(batch, dev())
+    nb = w["num_blocks"]
+    table = torch.from_numpy(w["block_table"]).to(dev())
+    lens = torch.from_numpy(w["context_lens"]).to(dev())
+    out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev())
+    ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx, 0), dtype=torch.uint8,
+                     device=dev())
+    cache = B.alloc_cache(nb, hkv, d, dev(), int4=True)
+    for b in range(batch):
+        k, v = w["tokens"](b)
+        B.kv8_quant_append_int4(k, v, w["slots"](b), *cache)
+    B.paged_decode_attn_int4kv(w["q"], *cache, table, lens, ctx, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in (0, batch - 1):
+        rows = table[b].long()
+        k_src, v_src = w["tokens"](b)
+        for g in (0, 5):
+            q = w["q"][b, g * 4:(g + 1) * 4].float().cpu().numpy().astype(np.float64)
+            kcodes = cache[0][rows, g].reshape(ctx, d // 2).cpu().numpy()
+            vcodes = cache[1][rows, g].reshape(ctx, d // 2).cpu().numpy()
+            ksc = cache[2][rows, g].reshape(ctx).cpu().numpy().view(np.float16)
+            vsc = cache[3][rows, g].reshape(ctx).cpu().numpy().view(np.float16)
+            kq, ks_ref = O.quantize_rows_int4(k_src[:, g].float().cpu().numpy())
+            vq, vs_ref = O.quantize_rows_int4(v_src[:, g].float().cpu().numpy())
+            assert np.array_equal(kcodes, kq) and np.array_equal(vcodes, vq)
+            assert np.array_equal(ksc.view(np.uint16), ks_ref.view(np.uint16))
+            assert np.array_equal(vsc.view(np.uint16), vs_ref.view(np.uint16))
+            kd, vd = O.dequantize_rows_int4(kq, ks_ref), O.dequantize_rows_int4(vq, vs_ref)
+            ref = O.softmax_attention(q, kd, vd, sm)
+            check_close(got[b, g * 4:(g + 1) * 4], ref, f"258K int4 seq {b} head {g}")
