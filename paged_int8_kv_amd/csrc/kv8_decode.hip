@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const float p = __builtin_amdgcn_exp2f(z - Mh);
         p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
         lsum += p;
-        if constexpr (C::kBiased) psum += (float)p16;
+        if constexpr (C::kBiased && !NIB) psum += (float)p16;
       }
       const int jj = t / kBlock, r = t % kBlock;
       pph[((jj * 8 + (r & 7)) * G + h) * 2 + (r >> 3)] = p16;
@@ -396,7 +396,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
             const uint32_t hi = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const half2_t fl = C::nib_pair(lo, j), fh = C::nib_pair(hi, j);
+              // unbiased exactly here (4-bit codes: biased sums over a long
+              // split would cancel away too many bits)
+              const half2_t fl = C::exact(C::nib_pair(lo, j)), fh = C::exact(C::nib_pair(hi, j));
 #pragma unroll
               for (int h = 0; h < G; ++h) {
                 acc[h * CPL + 8 * k + j] = fdot2(wp[h], fl, acc[h * CPL + 8 * k + j]);
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 
   groups_to_lds<G, CPL, D>(acc, s_fin, wave, lane, chunk);
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, C::kBiased>(
+  finish_split<G, D, kThreads, kWaves, C::kBiased && !NIB>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
       bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
 }
