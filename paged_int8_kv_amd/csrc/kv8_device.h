@@ -270,6 +270,17 @@ __device__ __forceinline__ void quotients(const float (&x)[N], float s, float (&
   }
 }
 
+// Integer code of a quotient as the low bits of an fp32: q clamped to
+// [-qmax, qmax] (clamping to integer bounds commutes with rounding), plus
+// 1.5 * 2^23, rounds to the nearest integer with ties to even (the fp32 add
+// itself rounds so, the magic constant being even), and the sum's bits are
+// 0x4B400000 + rint(q): their low byte (nibble) is the code in two's
+// complement.
+__device__ __forceinline__ uint32_t code_bits(float q, float qmax) {
+  const float c = __builtin_amdgcn_fmed3f(q, -qmax, qmax);
+  return __builtin_bit_cast(uint32_t, c + 12582912.0f);
+}
+
 template <class C>
 __device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
   uint32_t w0 = 0, w1 = 0;
@@ -277,10 +288,12 @@ __device__ __forceinline__ uint2 quantise8(const float (&x)[8], float s) {
     if constexpr (C::kIntCodes) {
       float q[8];
       quotients<8>(x, s, q);
+      uint32_t y[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w0 |= C::code_of_quotient(q[i]) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w1 |= C::code_of_quotient(q[4 + i]) << (8 * i);
+      for (int i = 0; i < 8; ++i) y[i] = code_bits(q[i], C::kQmax);
+      // low bytes of y0..y3 -> one dword: [y0.b0, y1.b0, 0, 0] | [0, 0, y2.b0, y3.b0]
+      w0 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u) | __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);
+      w1 = __builtin_amdgcn_perm(y[5], y[4], 0x0C0C0400u) | __builtin_amdgcn_perm(y[7], y[6], 0x04000C0Cu);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) w0 |= C::code(x[i], s) << (8 * i);
@@ -299,7 +312,7 @@ __device__ __forceinline__ uint32_t quantise8_nibbles(const float (&x)[8], float
     float q[8];
     quotients<8>(x, s, q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= C::code_of_quotient(q[i]) << (4 * i);
+    for (int i = 0; i < 8; ++i) w |= (code_bits(q[i], C::kQmax) & 0xFu) << (4 * i);
   }
   return w;
 }
