@@ -137,7 +137,9 @@ int kv8_set_decode_kernel(int which);
  *                  the fp16 scale of (slot, h) are overwritten
  *   stream         hipStream_t
  * Two tokens mapping to the same slot race (undefined which one wins).
- * n_tokens == 0 is a no-op returning KV8_OK.
+ * n_tokens == 0 is a no-op returning KV8_OK.  KV8_ERR_SHAPE for a negative
+ * n_tokens, num_kv_heads <= 0, or n_tokens * num_kv_heads >= 2^31 rows in
+ * one call (more than 500 GB of bf16 K/V; split such a call).
  */
 int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                      const int32_t* slot_mapping, int64_t n_tokens,

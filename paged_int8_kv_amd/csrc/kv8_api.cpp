@@ -43,7 +43,7 @@ int append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slo
   if (n_tokens == 0) return KV8_OK;
   if (!k_new || !v_new || !slot_mapping) return KV8_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return KV8_ERR_ALIGN;
-  if (n_tokens * num_kv_heads * (head_dim / 8) / 256 >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;
+  if (n_tokens * num_kv_heads >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;   // rows fit 31 bits
   const int r = kv8::launch_quant_append(k_new, v_new, slot_mapping, n_tokens, num_kv_heads,
                                          head_dim, num_blocks, k_cache, v_cache, k_scale,
                                          v_scale, fmt, static_cast<hipStream_t>(stream));
@@ -190,7 +190,7 @@ int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
   if (!k_new || !v_new || !slot_mapping || !positions || !cos_sin) return KV8_ERR_NULL;
   if (max_position <= 0) return KV8_ERR_SHAPE;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_sin)) return KV8_ERR_ALIGN;
-  if (n_tokens * num_kv_heads * (head_dim / 8) / 256 >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;
+  if (n_tokens * num_kv_heads >= (int64_t)0x7FFFFFFF) return KV8_ERR_SHAPE;   // rows fit 31 bits
   const int r = kv8::launch_rope_quant_append(k_new, v_new, slot_mapping, positions, cos_sin,
                                               max_position, n_tokens, num_kv_heads, head_dim,
                                               num_blocks, k_cache, v_cache, k_scale, v_scale,

@@ -66,8 +66,10 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
   const int64_t row = gtid / LPR;          // (token, head) row
   const int part = (int)(gtid % LPR);      // which 8 channels
   if (row >= n_rows) return;               // whole rows exit together
-  const int64_t n = row / num_kv_heads;
-  const int h = (int)(row % num_kv_heads);
+  // rows fit 31 bits (checked on the host): 32-bit division by the head count
+  const uint32_t row32 = (uint32_t)row, nh = (uint32_t)num_kv_heads;
+  const uint32_t n = row32 / nh;
+  const int h = (int)(row32 - n * nh);
   const int64_t slot = slot_mapping[n];
   const bool keep = slot >= 0 && slot < num_slots;
 
