@@ -322,13 +322,15 @@ def e4m3_encode(x):
     exact grid (spacing 2^(e-3) for |x| in [2^e, 2^(e+1)), e >= -6; spacing
     2^-9 below 2^-6), then saturate to +-448.  Zero keeps its sign."""
     x = np.asarray(x, np.float32).astype(np.float64)
-    a = np.abs(x)
+    # saturation first: every magnitude at or above 448 (an overflowed,
+    # infinite quotient included) codes as 448, and below it rounding to the
+    # grid never exceeds 448, so clamping before rounding is the same rule
+    a = np.minimum(np.abs(x), E4M3_MAX)
     with np.errstate(divide="ignore"):
         e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     e = np.maximum(e, -6.0)
     ulp = np.exp2(e - 3)
     r = np.rint(a / ulp) * ulp                 # exact: power-of-two scaling, RNE
-    r = np.minimum(r, E4M3_MAX)
     # code of the rounded magnitude r (a grid point or 448)
     sub = r < 2.0 ** -6
     ee = np.where(sub, 0, np.floor(np.log2(np.where(sub, 1.0, r))) + 7).astype(np.int64)

@@ -47,6 +47,10 @@ def _battery():
         ("int4_invariants", P.test_int4_quantiser_invariants),
         ("int4_attention", P.test_int4_decode_and_prefill_brute_force),
         ("int4_codes", lambda: P.test_int4_codes_every_bf16(1.0)),
+        ("int4_scale_exhaustive", P.test_int4_scale_every_bf16_absmax),
+        ("codes_exhaustive", lambda: [P.test_codes_exhaustive_all_bf16(s) for s in P.SCALES]),
+        ("fp8_scale_exhaustive", P.test_fp8_scale_every_bf16_absmax),
+        ("fp8_codes_exhaustive", lambda: [P.test_fp8_codes_every_bf16(s) for s in P.FP8_SCALES]),
     ]
     for name, fn in checks:
         try:
@@ -180,6 +184,63 @@ def _row_scale_fp8_127(x):
     return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
 
 
+def _fp16_truncate(s32):
+    """fp32 -> fp16 rounding toward zero (a plausible slip for RNE)."""
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    over = np.abs(s16.astype(np.float32)) > np.abs(s32)
+    return np.where(over, np.nextafter(s16, np.float16(0)), s16).astype(np.float16)
+
+
+def _row_scale_fp8_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    s16 = _fp16_truncate(a / np.float32(448))
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
+def _row_scale_fp8_no_saturation(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return (a / np.float32(448)).astype(np.float16)
+
+
+def _codes_fp8_quotient_fp16(x, s):
+    x16 = np.asarray(x, dtype=np.float64).astype(np.float16)
+    s16 = np.asarray(s, dtype=np.float16)[..., None]
+    zero = s16 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x16 / np.where(zero, np.float16(1), s16)
+    return np.where(zero, np.uint8(0), O.e4m3_encode(quot.astype(np.float32))).astype(np.uint8)
+
+
+def _codes_fp8_reciprocal(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 * (np.float32(1) / np.where(zero, np.float32(1), s32))
+    return np.where(zero, np.uint8(0), O.e4m3_encode(quot)).astype(np.uint8)
+
+
+def _codes_reciprocal(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 * (np.float32(1) / np.where(zero, np.float32(1), s32))
+    q = np.where(zero, 0.0, np.clip(np.rint(quot.astype(np.float64)), -127, 127))
+    return q.astype(np.int8)
+
+
+def _row_scale_int4_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1).astype(np.float32)
+    s16 = _fp16_truncate(a / np.float32(7))
+    return np.where(np.isinf(s16), np.float16(65504), s16).astype(np.float16)
+
+
 def _rope_sign(x, positions, cos_sin):
     x = np.asarray(x, np.float32)
     half = x.shape[-1] // 2
@@ -245,6 +306,7 @@ MUTANTS = {
     "codes_half_away": ("codes_for_scale", _codes_half_away),
     "codes_clamp_128": ("codes_for_scale", _codes_clamp_128),
     "codes_truncate": ("codes_for_scale", _codes_truncate),
+    "codes_reciprocal": ("codes_for_scale", _codes_reciprocal),
     "dequant_sign": ("dequantize_rows", _dequant_sign_flip),
     "causal_exclusive": ("causal_visibility",
                          lambda ctx, lc: np.arange(ctx)[None, :] < (ctx - lc + np.arange(lc))[:, None]),
@@ -257,6 +319,11 @@ MUTANTS = {
     "fp8_encode_truncates": ("e4m3_encode", _e4m3_truncate),
     "fp8_value_bias8": ("e4m3_value", _e4m3_value_bias8),
     "fp8_scale_127": ("row_scale_fp8", _row_scale_fp8_127),
+    "fp8_scale_truncates": ("row_scale_fp8", _row_scale_fp8_truncate),
+    "fp8_scale_no_saturation": ("row_scale_fp8", _row_scale_fp8_no_saturation),
+    "fp8_quotient_fp16": ("codes_fp8_for_scale", _codes_fp8_quotient_fp16),
+    "fp8_quotient_reciprocal": ("codes_fp8_for_scale", _codes_fp8_reciprocal),
+    "int4_scale_truncates": ("row_scale_int4", _row_scale_int4_truncate),
     "rope_sign": ("rope_rotate_half", _rope_sign),
     "rope_cos_sin_swapped": ("rope_rotate_half", _rope_cos_sin_swapped),
     "rope_interleaved": ("rope_rotate_half", _rope_interleaved),

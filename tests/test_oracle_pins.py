@@ -171,8 +171,10 @@ def test_scale_edges():
     assert O.row_scale(np.array([[8323072.0]]))[0] == np.float16(65504)
 
 
+# 14 and 0.875: scales whose fp32 reciprocal is inexact, where x * fp32(1/s)
+# rounds 6 bf16 values differently from the specified division
 SCALES = [1.0, 0.0234375, 0.5 + 2 ** -11, 6.103515625e-05, 2 ** -24, 3 * 2 ** -24,
-          1000 * 2 ** -24, 65504.0, 2.0 ** 10 * 1.5]
+          1000 * 2 ** -24, 65504.0, 2.0 ** 10 * 1.5, 14.0, 0.875]
 
 
 @pytest.mark.parametrize("s", SCALES)
@@ -591,6 +593,101 @@ def test_fp8_quantiser_invariants():
     assert np.all(codes[~nz] == 0) and np.all(neg[~nz] == 0)
 
 
+def test_fp8_scale_every_bf16_absmax():
+    """Every positive finite bf16 absmax against exact rational rounding of
+    absmax / 448 to fp16 (nearest even, gradual underflow), saturated to
+    65504: covers the underflow band (scale 0), the subnormal scales and the
+    saturation band (absmax >= 448 * 65520)."""
+    a = all_finite_bf16(positive_only=True)
+    got = O.row_scale_fp8(a[:, None]).astype(np.float64)
+    exp = []
+    for v in a.tolist():
+        s = fp16_rne_exact(Fraction(v) / 448)
+        exp.append(65504.0 if s == math.inf else s)
+    exp = np.array(exp)
+    assert np.array_equal(got, exp)
+    assert np.count_nonzero(exp == 0) > 0                       # underflow band present
+    assert np.count_nonzero((exp > 0) & (exp < 2.0 ** -14)) > 0   # subnormal scales
+    assert np.count_nonzero(a >= 448.0 * 65520) > 1000           # saturation band
+
+
+def e4m3_grid():
+    """The 127 non-negative finite e4m3 values in code order, from the
+    format's definition (bias 7, 3 mantissa bits, subnormals m * 2^-9, code
+    0x7F reserved): fp64, exact."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10))
+    return np.array(vals)
+
+
+def exact_e4m3_codes(x, s):
+    """e4m3 codes of x / s by exact comparison against the exact midpoints
+    s * (v_k + v_{k+1}) / 2 (each a product of a 5-bit and an 11-bit
+    significand, so exact in fp64); ties go to the even code; beyond the
+    last midpoint everything is 448 (code 0x7E); the sign of x is kept."""
+    x = np.asarray(x, np.float64)
+    if s == 0:
+        return np.zeros(x.shape, np.int64)
+    grid = e4m3_grid()
+    thr = float(s) * (grid[:-1] + grid[1:]) / 2
+    a = np.abs(x)
+    k = np.searchsorted(thr, a, side="left")           # number of midpoints below a
+    tie = (k < len(thr)) & (thr[np.minimum(k, len(thr) - 1)] == a)
+    k = np.where(tie & (k % 2 == 1), k + 1, k)          # tie between k and k+1: even code
+    return np.where(np.signbit(x), 0x80, 0) | k
+
+
+FP8_SCALES = [1.0, 3.0, 3.5, 0.0234375, 2.0 ** -14, 3 * 2 ** -24, 1000 * 2 ** -24, 65504.0,
+              1.5 * 2.0 ** 10]
+
+
+@pytest.mark.parametrize("s", FP8_SCALES)
+def test_fp8_codes_every_bf16(s):
+    """Every finite bf16 x (both signs, zeros, subnormals, values whose
+    quotient saturates) under normal, subnormal and saturated scales against
+    exact rounding onto the e4m3 grid.  At s = 3 the bf16 grid holds exact
+    midpoints x / s (5-bit midpoints times 3), so tie handling is decided
+    exactly; at s = 3.5 a quotient taken as x * fp32(1/s) rounds 60 values
+    differently; a quotient rounded through fp16 fails at large |x|."""
+    x = all_finite_bf16()
+    got = O.codes_fp8_for_scale(x[None, :], np.array([s], np.float16))[0].astype(np.int64)
+    exp = exact_e4m3_codes(x, float(np.float16(s)))
+    assert np.array_equal(got, exp)
+    if s == 3.0:
+        grid = e4m3_grid()
+        mids = 3.0 * (grid[:-1] + grid[1:]) / 2
+        assert np.count_nonzero(np.isin(np.abs(x), mids)) > 50   # ties really occur
+
+
+def test_fp8_exact_reference_vs_fraction():
+    """The exact e4m3 reference above against Fraction arithmetic on a
+    random sample plus every exact midpoint at s = 3."""
+    grid = [Fraction(v) for v in e4m3_grid().tolist()]
+
+    def frac_code(xv, s):
+        q = abs(Fraction(xv) / Fraction(s))
+        best = None
+        for k, v in enumerate(grid):
+            d = abs(q - v)
+            if best is None or d < best[0] or (d == best[0] and k % 2 == 0):
+                best = (d, k)
+        return (0x80 if math.copysign(1.0, xv) < 0 else 0) | best[1]
+
+    x = all_finite_bf16()
+    rng = np.random.default_rng(25)
+    for s in (3.0, 1000 * 2 ** -24, 65504.0):
+        pick = x[rng.choice(len(x), 400, replace=False)]
+        if s == 3.0:
+            g = e4m3_grid()
+            mids = 3.0 * (g[:-1] + g[1:]) / 2
+            pick = np.concatenate([pick, x[np.isin(np.abs(x), mids)]])
+        exp = exact_e4m3_codes(pick, s)
+        for xv, e in zip(pick.tolist(), exp.tolist()):
+            assert frac_code(xv, s) == e
+
+
 def build_cache_fp8(case):
     kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, case.num_kv_heads, case.head_dim)
     kc, vc = kc.view(np.uint8), vc.view(np.uint8)
@@ -723,10 +820,11 @@ def exact_codes_q(x, s, qmax):
 def test_int4_scale_every_bf16_absmax():
     a = all_finite_bf16(positive_only=True)
     got = O.row_scale_int4(a[:, None]).astype(np.float64)
-    pick = np.random.default_rng(51).choice(len(a), 4000, replace=False)
-    for i in pick.tolist():
-        e = fp16_rne_exact(Fraction(float(a[i])) / 7)
-        assert got[i] == (65504.0 if e == math.inf else e)
+    exp = []
+    for v in a.tolist():
+        e = fp16_rne_exact(Fraction(v) / 7)
+        exp.append(65504.0 if e == math.inf else e)
+    assert np.array_equal(got, np.array(exp))
 
 
 @pytest.mark.parametrize("s", [1.0, 0.0234375, 3 * 2 ** -24, 2.0 ** -14, 9362.0])
