@@ -36,7 +36,8 @@ def parse():
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--tokens-per-split", type=int, default=0)
     p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma", "mfma1"], default="auto",
-                   help="form of the INT8/FP8 decode kernel (auto: by group size)")
+                   help="form of the INT8/FP8/INT4 decode kernel passed to every decode call "
+                        "(auto: the library's choice by group size and size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-read-ceiling", action="store_true",
                    help="skip the read-only probe that measures the HBM read ceiling")
@@ -51,6 +52,8 @@ def parse():
                    help="calls of the append fill leg, 131072 tokens each (0 skips it)")
     p.add_argument("--long-steps", type=int, default=64,
                    help="decode steps of the long-context leg, 4 x 32768 tokens (0 skips it)")
+    p.add_argument("--long-replicas", type=int, default=3,
+                   help="cache copies the long-context leg rotates (each about 273 MB)")
     p.add_argument("--budget-steps", type=int, default=10,
                    help="decode calls timed per side of the 258K equal-budget comparison "
                         "(0 skips it)")
@@ -119,8 +122,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B.kv8_set_decode_kernel({"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
-                             "mfma1": B.DECODE_MFMA_ONEPASS}[args.decode_kernel])
+    args.form = {"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
+                 "mfma1": B.DECODE_MFMA_ONEPASS}[args.decode_kernel]
     if args.calibrate_copy:
         calibrate_copy(dev)
         return
@@ -158,7 +161,8 @@ def main():
         # sequence (quantised inside the decode kernel), then attend
         c = caches[i % len(caches)]
         B.paged_decode_attn_kv8_append(q, k_new, v_new, *c, table, lens, max_ctx, out, ws,
-                                       tokens_per_split=args.tokens_per_split)
+                                       tokens_per_split=args.tokens_per_split,
+                                       kernel_form=args.form)
 
     def two_launch_step(i, ev=None):
         c = caches[i % len(caches)]
@@ -168,7 +172,8 @@ def main():
         if ev is not None:
             ev[1].record()
         B.paged_decode_attn_kv8(q, *c, table, lens, max_ctx, out, ws,
-                                tokens_per_split=args.tokens_per_split)
+                                tokens_per_split=args.tokens_per_split,
+                                kernel_form=args.form)
         if ev is not None:
             ev[2].record()
 
@@ -207,7 +212,8 @@ def main():
     for i in range(n_b2b):
         c = caches[i % len(caches)]
         B.paged_decode_attn_kv8(q, *c, table, lens, max_ctx, out, ws,
-                                tokens_per_split=args.tokens_per_split)
+                                tokens_per_split=args.tokens_per_split,
+                                kernel_form=args.form)
     b1.record()
     torch.cuda.synchronize()
     dec_b2b_us = b0.elapsed_time(b1) / n_b2b * 1e3
@@ -254,7 +260,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 operands (int8 codes exact in f16, q rescaled by a power of two, "
+                 "weights p*v_scale), f32 accumulation and softmax",
         "data": "synthetic",
         "config": {
             "workload": "Llama-3.1-8B-shaped decode layer: append 1 token/seq + paged INT8-KV "
@@ -287,9 +294,13 @@ def main():
     del caches, ws, out
     torch.cuda.empty_cache()
     if not args.no_read_ceiling:
-        rc = bench_read_ceiling(dev, d_bytes)
-        result["read_ceiling"] = rc
-        result["roofline"]["frac_of_read_ceiling"] = round(dec_gbs / rc["gbs"], 4)
+        tiles = bench_read_ceiling(dev, d_bytes)
+        stream = bench_stream_read(dev)
+        best = max(tiles["gbs"], stream["gbs"])
+        result["read_ceiling"] = {"gbs": best, "pct_of_hbm_peak": round(best / HBM_PEAK_GBS * 100, 2),
+                                  "stream": stream, "random_tiles": tiles,
+                                  "note": "the larger of the two measured read rates"}
+        result["roofline"]["frac_of_read_ceiling"] = round(dec_gbs / best, 4)
     if args.prefill_steps > 0:
         result["prefill"] = bench_prefill(args, dev)
     if args.fp8_steps > 0:
@@ -419,14 +430,16 @@ def bench_code_decode(args, dev, case, fmt):
     n = max(args.steps, 50)
     for i in range(200):
         decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws,
-               tokens_per_split=args.tokens_per_split)
+               tokens_per_split=args.tokens_per_split,
+               kernel_form=args.form)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(n):
         decode(q, *caches[i % len(caches)], table, lens, max_ctx, out, ws,
-               tokens_per_split=args.tokens_per_split)
+               tokens_per_split=args.tokens_per_split,
+               kernel_form=args.form)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / n * 1e3
@@ -481,41 +494,81 @@ def bench_append_fill(args, dev, n_tokens=131072, hkv=8, d=128):
             "tokens_per_s": round(n_tokens / (us * 1e-6), 1)}
 
 
+def probe_workgroups(dev, per_cu=4):
+    """Persistent workgroups of the read-ceiling kernels: a few per CU."""
+    import torch
+    return per_cu * torch.cuda.get_device_properties(dev).multi_processor_count
+
+
 def bench_read_ceiling(dev, n_bytes, tile_bytes=2048, buffer_bytes=1 << 30, replicas=4,
                        launches=100):
-    """The measured HBM read ceiling of the decode's access pattern: the
-    library's read-only probe (kv8_read_probe) streams about n_bytes per
-    launch as random tile_bytes tiles (one (block, KV head) code tile of the
-    decode) out of a 1 GiB buffer, rotating `replicas` tile orders, launches
-    back to back between HIP events on the current stream."""
+    """The measured HBM read rate of the decode's access pattern: the
+    library's kv8_read_probe streams about n_bytes per launch as random
+    tile_bytes tiles (one (block, KV head) code tile of the decode) out of a
+    1 GiB buffer, rotating `replicas` tile orders, persistent workgroups
+    with nontemporal loads, launches back to back between HIP events on the
+    current stream."""
     import torch
     from paged_int8_kv_amd import binding as B
-    per_wg = B.load().kv8_read_probe_bytes_per_workgroup()
-    wg = max(1, n_bytes // per_wg)
-    n_tiles_read = wg * per_wg // tile_bytes
+    chunk = B.load().kv8_read_probe_chunk_bytes()
+    n_read = max(1, n_bytes // chunk) * chunk
+    n_tiles_read = n_read // tile_bytes
     n_tiles_buf = buffer_bytes // tile_bytes
     buf = torch.zeros(buffer_bytes, dtype=torch.uint8, device=dev)
     rng = np.random.Generator(np.random.PCG64(11))
     orders = [torch.from_numpy(rng.permutation(n_tiles_buf)[:n_tiles_read].astype(np.int32)).to(dev)
               for _ in range(replicas)]
+    wg = probe_workgroups(dev)
     out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
     for i in range(20):
-        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, out)
+        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, wg, out)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(launches):
-        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, out)
+        B.kv8_read_probe(buf, orders[i % replicas], tile_bytes, wg, out)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / launches
-    read = wg * per_wg
     del buf, orders, out
     torch.cuda.empty_cache()
-    return {"kernel": "kv8_read_probe: read-only, random tiles, 32 KB per workgroup in flight",
-            "tile_bytes": tile_bytes, "buffer_bytes": buffer_bytes, "bytes_per_launch": int(read),
-            "us_per_launch": round(us, 2), "gbs": round(read / (us * 1e-6) / 1e9, 1),
+    return {"kernel": "kv8_read_probe: read-only, random tiles, persistent workgroups, "
+                      "nontemporal 16-byte loads",
+            "tile_bytes": tile_bytes, "buffer_bytes": buffer_bytes, "bytes_per_launch": int(n_read),
+            "workgroups": wg, "us_per_launch": round(us, 2),
+            "gbs": round(n_read / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(n_read / (us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100, 2)}
+
+
+def bench_stream_read(dev, buffer_bytes=2 << 30, launches=30):
+    """The plain streaming read rate of HBM: the library's kv8_stream_read
+    over a 2 GiB buffer (eight times the last-level cache), persistent
+    workgroups with nontemporal loads, launches back to back between HIP
+    events on the current stream."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    chunk = B.load().kv8_read_probe_chunk_bytes()
+    buf = torch.zeros(buffer_bytes // chunk * chunk, dtype=torch.uint8, device=dev)
+    wg = probe_workgroups(dev)
+    out = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        B.kv8_stream_read(buf, wg, out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        read = B.kv8_stream_read(buf, wg, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"kernel": "kv8_stream_read: read-only, contiguous, persistent workgroups, "
+                      "nontemporal 16-byte loads",
+            "buffer_bytes": int(read), "workgroups": wg, "us_per_launch": round(us, 2),
+            "gbs": round(read / (us * 1e-6) / 1e9, 1),
             "pct_of_hbm_peak": round(read / (us * 1e-6) / 1e9 / HBM_PEAK_GBS * 100, 2)}
 
 
@@ -526,10 +579,18 @@ def bench_long_context(args, dev, batch=4, ctx0=32768):
     (paged_decode_attn_kv8_append), `long_steps` steps back to back.  K/V/q
     are drawn N(0, 1) on the device (torch.Generator seeded 3000), the
     context quantised by the append kernel; the block table is a random
-    permutation (numpy PCG64 seeded 3) with room for every step."""
+    permutation (numpy PCG64 seeded 3) with room for every step.
+
+    One cache is about 273 MB, close to the 256 MB last-level cache, so
+    `long_replicas` copies of the cache are rotated step by step (3 by
+    default: 820 MB between two reads of one copy).  Every copy is filled
+    beforehand with the same tokens, those the steps append included, so a
+    step's append rewrites the values its copy already holds and every copy
+    holds the whole sequence whichever step reads it."""
     import torch
     from paged_int8_kv_amd import binding as B
     steps, hq, hkv, d = args.long_steps, 32, 8, 128
+    reps = max(1, args.long_replicas)
     ctx_max = ctx0 + steps
     bps = -(-ctx_max // 16)
     nb = batch * bps
@@ -539,17 +600,23 @@ def bench_long_context(args, dev, batch=4, ctx0=32768):
     slots_np = np.concatenate([table_np[b][pos // 16] * 16 + pos % 16 for b in range(batch)])
     gen = torch.Generator(device=dev)
     gen.manual_seed(3000)
-    cache = B.alloc_cache(nb, hkv, d, dev)
+    caches = [B.alloc_cache(nb, hkv, d, dev) for _ in range(reps)]
     for b in range(batch):      # one sequence at a time keeps the bf16 staging small
         k = torch.randn((ctx0, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
         v = torch.randn((ctx0, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
         sl = torch.from_numpy(np.ascontiguousarray(slots_np[b * ctx0:(b + 1) * ctx0])).to(dev)
-        B.kv8_quant_append(k, v, sl, *cache)
+        for c in caches:
+            B.kv8_quant_append(k, v, sl, *c)
         del k, v
     k_new = torch.randn((steps, batch, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
     v_new = torch.randn((steps, batch, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
     q = torch.randn((steps, batch, hq, d), generator=gen, device=dev)
     lens_np = ctx0 + 1 + np.arange(steps, dtype=np.int32)[:, None].repeat(batch, 1)
+    for st in range(steps):     # the appended tokens, into every copy beforehand
+        p = ctx0 + st
+        sl = torch.from_numpy((table_np[:, p // 16] * 16 + p % 16).astype(np.int32)).to(dev)
+        for c in caches:
+            B.kv8_quant_append(k_new[st], v_new[st], sl, *c)
     lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
     table = torch.from_numpy(table_np).to(dev)
     ws = torch.zeros(B.kv8_decode_workspace_size(batch, hq, hkv, d, ctx_max, args.tokens_per_split),
@@ -558,8 +625,10 @@ def bench_long_context(args, dev, batch=4, ctx0=32768):
 
     def run():
         for s in range(steps):
-            B.paged_decode_attn_kv8_append(q[s], k_new[s], v_new[s], *cache, table, lens[s],
-                                           ctx_max, out, ws, tokens_per_split=args.tokens_per_split)
+            B.paged_decode_attn_kv8_append(q[s], k_new[s], v_new[s], *caches[s % reps], table,
+                                           lens[s], ctx_max, out, ws,
+                                           tokens_per_split=args.tokens_per_split,
+                                           kernel_form=args.form)
 
     run()
     torch.cuda.synchronize()
@@ -576,11 +645,13 @@ def bench_long_context(args, dev, batch=4, ctx0=32768):
     nbytes = float(np.mean([decode_bytes(lens_np[s], hkv, d, hq, 4) for s in range(steps)]))
     nbytes += append_bytes(batch, hkv, d)
     tokens = float(lens_np.sum()) / steps
-    del cache, k_new, v_new, q, ws, out
+    del caches, k_new, v_new, q, ws, out
     torch.cuda.empty_cache()
     return {"workload": f"long-context decode with append: B={batch}, Hq={hq}, Hkv={hkv}, d={d}, "
                         f"ctx {ctx0} + 1 token per sequence per step, fp32 q, {steps} steps "
-                        "back to back (paged_decode_attn_kv8_append)",
+                        f"back to back (paged_decode_attn_kv8_append), {reps} cache copies "
+                        "rotated step by step",
+            "replicas_rotated": reps,
             "us_per_step": round(us, 2), "bytes_per_step": int(nbytes),
             "kv_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "pct_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / 8000 * 100, 2),
@@ -618,7 +689,8 @@ def bench_sweep70b(args, dev):
     def sweep():
         for q, cache, table, lens, m in layers:
             B.paged_decode_attn_kv8(q, *cache, table, lens, m, out, ws,
-                                    tokens_per_split=args.tokens_per_split)
+                                    tokens_per_split=args.tokens_per_split,
+                                    kernel_form=args.form)
 
     for _ in range(3):
         sweep()
@@ -710,7 +782,8 @@ def bench_equal_budget(args, dev):
                 k, v = w["tokens"](b)
                 B.kv8_quant_append(k, v, w["slots"](b), *cache)
                 del k, v
-            call = lambda: B.paged_decode_attn_kv8(w["q"], *cache, table, lens, ctx, out, ws)
+            call = lambda: B.paged_decode_attn_kv8(w["q"], *cache, table, lens, ctx, out, ws,
+                                                   kernel_form=args.form)
             nbytes = batch * ctx * per_tok_int8
         else:
             cache = B.alloc_cache(nb, hkv, d, dev, int4=True)
@@ -718,7 +791,8 @@ def bench_equal_budget(args, dev):
                 k, v = w["tokens"](b)
                 B.kv8_quant_append_int4(k, v, w["slots"](b), *cache)
                 del k, v
-            call = lambda: B.paged_decode_attn_int4kv(w["q"], *cache, table, lens, ctx, out, ws)
+            call = lambda: B.paged_decode_attn_int4kv(w["q"], *cache, table, lens, ctx, out, ws,
+                                                      kernel_form=args.form)
             nbytes = batch * ctx * per_tok_int4
         torch.cuda.synchronize()
         us = timed(call, args.budget_steps)
@@ -757,6 +831,17 @@ def calibrate_copy(dev, n_bytes=256 << 20, launches=5):
                       "launches": launches}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, n_steps, step_bytes):
     """The fp64 oracle on the host: the same step (append the newest token of
     every sequence, then decode the whole batch), repeated n_steps times."""
@@ -775,6 +860,7 @@ def cpu_baseline(case, n_steps, step_bytes):
         O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
     dt = (time.perf_counter() - t0) / n_steps
     return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "cpu_model": cpu_model(), "host_cpus_usable": len(os.sched_getaffinity(0)),
             "kind": "oracle", "seconds_per_step": round(dt, 3),
             "kv_tokens_per_s": round(float(case.context_lens.sum()) / dt, 1),
             "sample": f"{n_steps} full steps of the same workload (append 32 tokens + decode "

@@ -93,35 +93,42 @@ const char* kv8_status_string(int status);
 int kv8_version(void);
 
 /*
- * kv8_set_decode_kernel - choose the form of the INT8 / FP8 decode kernel
- * used by paged_decode_attn_kv8, paged_decode_attn_kv8_append and
- * paged_decode_attn_fp8kv, for this process (all threads, all devices).
- *   which  KV8_DECODE_AUTO (0, the default): by group size G = Hq / Hkv
- *            and size (v_dot2 below G = 4; at G = 4 two-pass matrix-core
- *            for max_context_len <= 8192 with a grid bound, every sequence
- *            at max_context_len in 1024-token splits, of at most 4096
- *            workgroups, else one-pass; one-pass matrix-core from G = 8);
- *          KV8_DECODE_DOT  (1): the v_dot2 kernel;
- *          KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of
- *            the split to LDS, then the weighted values; logits and values
- *            as 16x16 MFMA tiles over all G heads of a group at once);
- *          KV8_DECODE_MFMA_ONEPASS (3): the one-pass matrix-core kernel
- *            (online softmax over K and V tiles streamed together, weights
- *            kept in registers).
- * All forms compute the same attention (the same work items and in-launch
- * merge); results agree within the attention tolerance, not bitwise.  The
- * form can change the default split size, hence the workspace a call needs;
- * kv8_decode_workspace_size returns enough for every form.  The INT4 decode
- * (paged_decode_attn_int4kv) runs all three forms at d = 128 (AUTO: one-pass
- * from G = 4, else v_dot2) and the v_dot2 kernel at d = 64.  Takes effect for launches issued after the
- * call.  Returns KV8_OK, or KV8_ERR_UNSUPPORTED for another value (the
- * setting is then unchanged).
+ * Decode kernel forms: the `kernel_form` argument of paged_decode_attn_kv8,
+ * paged_decode_attn_kv8_append, paged_decode_attn_fp8kv and
+ * paged_decode_attn_int4kv chooses, for that call only, which kernel runs:
+ *   KV8_DECODE_AUTO (0): by group size G = Hq / Hkv and size (v_dot2 below
+ *     G = 4; at G = 4 two-pass matrix-core for max_context_len <= 8192 with
+ *     a grid bound, every sequence at max_context_len in 1024-token splits,
+ *     of at most 4096 workgroups, else one-pass; one-pass matrix-core from
+ *     G = 8; for the INT4 cache one-pass from G = 4 at d = 128, else v_dot2);
+ *   KV8_DECODE_DOT (1): the v_dot2 kernel;
+ *   KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of the
+ *     split to LDS, then the weighted values; logits and values as 16x16
+ *     MFMA tiles over all G heads of a group at once);
+ *   KV8_DECODE_MFMA_ONEPASS (3): the one-pass matrix-core kernel (online
+ *     softmax over K and V tiles streamed together, weights kept in
+ *     registers).
+ * The INT4 cache at d = 64 always runs the v_dot2 kernel.  All forms
+ * compute the same attention (the same work items and in-launch merge);
+ * results agree within the attention tolerance, not bitwise.  The form can
+ * change the default split size, hence the workspace a call needs;
+ * kv8_decode_workspace_size returns enough for every form.  Another value
+ * returns KV8_ERR_UNSUPPORTED.  The library keeps no setting: two calls
+ * with the same arguments run the same kernel.
+ *
+ * Split sizes.  tokens_per_split > 0 must be a multiple of 64 in
+ * [64, 2048].  The v_dot2 and two-pass forms hold a split's logits in LDS,
+ * so at G = 8 they accept at most 1280 tokens per split (a larger value
+ * returns KV8_ERR_UNSUPPORTED); the one-pass form accepts every value.
  */
 #define KV8_DECODE_AUTO 0
 #define KV8_DECODE_DOT 1
 #define KV8_DECODE_MFMA 2
 #define KV8_DECODE_MFMA_ONEPASS 3
-int kv8_set_decode_kernel(int which);
+
+/* Most (sequence, KV head) pairs, batch * num_kv_heads, of one decode
+ * call; more returns KV8_ERR_SHAPE. */
+#define KV8_DECODE_MAX_PAIRS 65536
 
 /*
  * kv8_quant_append - quantise N new tokens' K and V and scatter them into
@@ -180,10 +187,17 @@ int kv8_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 
 /*
  * kv8_decode_workspace_size - bytes of workspace paged_decode_attn_kv8
- * needs for these sizes.  tokens_per_split: most tokens one workgroup covers
- * (a multiple of 64 in [64, 2048]), or <= 0 for the library's choice,
- * which depends on batch, num_kv_heads and max_context_len only.  Returns
- * 0 for invalid sizes.
+ * needs for these sizes, under any kernel form.  tokens_per_split: most
+ * tokens one workgroup covers (a multiple of 64 in [64, 2048]), or <= 0 for
+ * the library's choice, which depends on batch, num_kv_heads and
+ * max_context_len only.  Returns 0 for invalid sizes (including
+ * batch * num_kv_heads > KV8_DECODE_MAX_PAIRS).
+ *
+ * Workspace layout: the first 4 * KV8_DECODE_MAX_PAIRS bytes hold one
+ * uint32 finished-split counter per (sequence b, KV head g), at index
+ * b * num_kv_heads + g, whatever the call's shape; the partial results of
+ * the splits follow.  Each call returns every counter it used to zero, so
+ * a workspace zero-filled once is ready for every later call of any shape.
  */
 size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                  int head_dim, int max_context_len,
@@ -216,12 +230,15 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *   workspace     device scratch of at least kv8_decode_workspace_size()
  *                 bytes (16-byte aligned).  It must be zero-filled once
  *                 before its first use; every completed call leaves it
- *                 ready for the next (its leading per-(sequence, KV head)
- *                 counters return to zero).  Calls sharing one workspace
- *                 must not overlap in time (use one stream, or one
- *                 workspace per stream).
- *   tokens_per_split  as for kv8_decode_workspace_size (same value!)
- * Same inputs and same tokens_per_split give bitwise-identical output.
+ *                 ready for the next call of any shape (layout above).
+ *                 Calls sharing one workspace must not overlap in time
+ *                 (use one stream, or one workspace per stream).
+ *   tokens_per_split  as for kv8_decode_workspace_size (same value!); the
+ *                 per-form limits are listed with the kernel forms above
+ *   kernel_form   KV8_DECODE_AUTO or a kernel form (see above)
+ * Same inputs, tokens_per_split and kernel_form give bitwise-identical
+ * output.  batch * num_kv_heads > KV8_DECODE_MAX_PAIRS returns
+ * KV8_ERR_SHAPE.
  */
 int paged_decode_attn_kv8(const void* q, int q_dtype,
                           const int8_t* k_cache, const int8_t* v_cache,
@@ -232,7 +249,7 @@ int paged_decode_attn_kv8(const void* q, int q_dtype,
                           int batch, int num_q_heads, int num_kv_heads,
                           int head_dim, int block_size, float sm_scale,
                           float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, void* stream);
+                          int tokens_per_split, int kernel_form, void* stream);
 
 /*
  * paged_decode_attn_kv8_append - one decode step in one launch: append the
@@ -244,7 +261,8 @@ int paged_decode_attn_kv8(const void* q, int q_dtype,
  * (context_lens already count it; values above max_context_len are clamped
  * first, as in paged_decode_attn_kv8), i.e. to slot
  * block_table[b][p / 16] * 16 + p % 16; sequences with an empty context
- * append nothing.  The workgroup that attends over a sequence's last split
+ * append nothing, and a block id outside [0, num_blocks) stores nothing
+ * (as kv8_quant_append skips such a slot).  The workgroup that attends over a sequence's last split
  * quantises the row and stores it before reading it back, so no separate
  * append kernel and no grid-wide synchronisation is needed.
  *
@@ -264,7 +282,7 @@ int paged_decode_attn_kv8_append(const void* q, int q_dtype,
                                  int batch, int num_q_heads, int num_kv_heads,
                                  int head_dim, int block_size, float sm_scale,
                                  float* out, void* workspace, size_t workspace_bytes,
-                                 int tokens_per_split, void* stream);
+                                 int tokens_per_split, int kernel_form, void* stream);
 
 /*
  * paged_decode_attn_bf16kv - the same decode attention over a paged cache
@@ -278,10 +296,11 @@ int paged_decode_attn_kv8_append(const void* q, int q_dtype,
  * split-K scheme, item order and in-launch merge as paged_decode_attn_kv8.
  *
  *   k_cache, v_cache  device bf16 bit patterns [num_blocks, Hkv, 16, d]
- *   all other arguments as for paged_decode_attn_kv8; the workspace is
- *   sized by kv8_decode_workspace_size() with the same sizes and
- *   tokens_per_split, zero-filled once, and may be shared with
- *   paged_decode_attn_kv8 calls that do not overlap in time.
+ *   all other arguments as for paged_decode_attn_kv8 (there is one kernel
+ *   form, so no kernel_form argument); the workspace is sized by
+ *   kv8_decode_workspace_size() with the same sizes and tokens_per_split,
+ *   zero-filled once, and may be shared with paged_decode_attn_kv8 calls
+ *   that do not overlap in time.
  * Slots past a sequence's context are never used, whatever they hold.
  * Returns KV8_OK or a negative kv8_status as paged_decode_attn_kv8 does.
  */
@@ -364,7 +383,7 @@ int paged_decode_attn_fp8kv(const void* q, int q_dtype,
                             int batch, int num_q_heads, int num_kv_heads,
                             int head_dim, int block_size, float sm_scale,
                             float* out, void* workspace, size_t workspace_bytes,
-                            int tokens_per_split, void* stream);
+                            int tokens_per_split, int kernel_form, void* stream);
 
 int paged_prefill_chunk_attn_fp8kv(const uint16_t* q, const int32_t* q_start_loc,
                                    int64_t total_q, int max_q_len,
@@ -412,7 +431,7 @@ int paged_decode_attn_int4kv(const void* q, int q_dtype,
                              int batch, int num_q_heads, int num_kv_heads,
                              int head_dim, int block_size, float sm_scale,
                              float* out, void* workspace, size_t workspace_bytes,
-                             int tokens_per_split, void* stream);
+                             int tokens_per_split, int kernel_form, void* stream);
 
 int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_loc,
                                     int64_t total_q, int max_q_len,
@@ -427,25 +446,35 @@ int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_lo
                                     void* stream);
 
 /*
- * kv8_read_probe - measurement utility, not part of the attention method:
- * the HBM read ceiling of the paged-decode access pattern on this device,
- * against which the decode kernels' achieved bandwidth is reported.  One
- * launch reads n_bytes = workgroups * kv8_read_probe_bytes_per_workgroup()
- * bytes: logical 16-byte position p reads buf[tiles[p / (tile_bytes / 16)]
- * * tile_bytes + (p % (tile_bytes / 16)) * 16], 32 KB per workgroup with all
- * loads in flight, no arithmetic but an xor per thread written to `out`.
- *   buf        device buffer of n_tiles * tile_bytes bytes (caller-owned;
- *              make it far larger than the last-level cache)
- *   tiles      device int32 [n_bytes / tile_bytes], each in [0, n_tiles)
- *   tile_bytes a multiple of 16 that divides 32768
- *   out        device uint32 [workgroups * 256]
- * Returns KV8_OK, KV8_ERR_NULL, KV8_ERR_SHAPE (tile_bytes or workgroups out
- * of range), KV8_ERR_ALIGN (buf not 16-byte aligned) or KV8_ERR_HIP.  Tile
- * indices are not checked on the device: an index outside the buffer is
- * undefined.  Asynchronous on `stream`.
+ * Read ceilings - measurement utilities, not part of the attention method:
+ * HBM read rates of this device against which the decode kernels' achieved
+ * bandwidth is reported (the memory-bound decode argument of the
+ * garden.houmin.site KV-cache optimisation page, section 1.3).  Both read
+ * n_bytes (a positive multiple of kv8_read_probe_chunk_bytes(), 32 KB)
+ * with `workgroups` persistent workgroups of 256 threads: workgroup w reads
+ * chunks w, w + workgroups, w + 2 * workgroups, ... with nontemporal 16-byte
+ * loads, 8 per lane in flight, and writes one xor per thread to `out`
+ * (device uint32 [workgroups * 256]).  A few workgroups per compute unit
+ * (e.g. 4 x 256 on MI355X) give the highest rate.  Make buf far larger
+ * than the last-level cache.  Both return KV8_OK, KV8_ERR_NULL,
+ * KV8_ERR_SHAPE (sizes out of range), KV8_ERR_ALIGN (buf not 16-byte
+ * aligned) or KV8_ERR_HIP, asynchronously on `stream`.
+ *
+ * kv8_stream_read - plain streaming read: chunk c is bytes
+ *   [c * chunk, (c + 1) * chunk) of buf, which holds n_bytes.
+ * kv8_read_probe - the access pattern of the paged decode: logical 16-byte
+ *   position p of the stream reads
+ *     buf[tiles[p / (tile_bytes / 16)] * tile_bytes + (p % (tile_bytes / 16)) * 16]
+ *   tiles: device int32 [n_bytes / tile_bytes], each in [0, n_tiles) for a
+ *   buf of n_tiles * tile_bytes bytes (not checked on the device: an index
+ *   outside the buffer is undefined); tile_bytes a multiple of 256 that
+ *   divides the chunk.  A workgroup loads the tile indices of its next chunk
+ *   while the current chunk's data loads are in flight.
  */
-int64_t kv8_read_probe_bytes_per_workgroup(void);
-int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes,
+int64_t kv8_read_probe_chunk_bytes(void);
+int kv8_stream_read(const void* buf, int64_t n_bytes, int64_t workgroups, uint32_t* out,
+                    void* stream);
+int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t n_bytes,
                    int64_t workgroups, uint32_t* out, void* stream);
 
 #ifdef __cplusplus

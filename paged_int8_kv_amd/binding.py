@@ -28,8 +28,9 @@ EXPORTED = (
     "paged_decode_attn_kv8", "paged_decode_attn_bf16kv", "kv8_prefill_workspace_size",
     "paged_prefill_chunk_attn_kv8", "kv8_quant_append_fp8", "paged_decode_attn_fp8kv",
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
-    "kv8_quant_append_int4", "paged_decode_attn_int4kv", "kv8_set_decode_kernel",
-    "paged_prefill_chunk_attn_int4kv", "kv8_read_probe_bytes_per_workgroup", "kv8_read_probe",
+    "kv8_quant_append_int4", "paged_decode_attn_int4kv",
+    "paged_prefill_chunk_attn_int4kv", "kv8_read_probe_chunk_bytes", "kv8_read_probe",
+    "kv8_stream_read",
 )
 
 _lib = None
@@ -60,8 +61,6 @@ def load():
     lib.kv8_status_string.argtypes = [i32]
     lib.kv8_version.restype = i32
     lib.kv8_version.argtypes = []
-    lib.kv8_set_decode_kernel.restype = i32
-    lib.kv8_set_decode_kernel.argtypes = [i32]
     lib.kv8_quant_append.restype = i32
     lib.kv8_quant_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
     lib.kv8_rope_quant_append.restype = i32
@@ -75,11 +74,12 @@ def load():
     lib.kv8_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_decode_attn_kv8.restype = i32
     lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
-                                          i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, vp]
+                                          i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, i32,
+                                          vp]
     lib.paged_decode_attn_kv8_append.restype = i32
     lib.paged_decode_attn_kv8_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, i32,
                                                  vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
-                                                 sz, i32, vp]
+                                                 sz, i32, i32, vp]
     lib.paged_decode_attn_fp8kv.restype = i32
     lib.paged_decode_attn_fp8kv.argtypes = lib.paged_decode_attn_kv8.argtypes
     lib.paged_decode_attn_int4kv.restype = i32
@@ -95,24 +95,22 @@ def load():
                                                  vp, vp, sz, vp]
     lib.paged_prefill_chunk_attn_fp8kv.restype = i32
     lib.paged_prefill_chunk_attn_fp8kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
-    lib.kv8_read_probe_bytes_per_workgroup.restype = i64
-    lib.kv8_read_probe_bytes_per_workgroup.argtypes = []
+    lib.kv8_read_probe_chunk_bytes.restype = i64
+    lib.kv8_read_probe_chunk_bytes.argtypes = []
     lib.kv8_read_probe.restype = i32
-    lib.kv8_read_probe.argtypes = [vp, vp, i32, i64, vp, vp]
+    lib.kv8_read_probe.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    lib.kv8_stream_read.restype = i32
+    lib.kv8_stream_read.argtypes = [vp, i64, i64, vp, vp]
     lib.paged_prefill_chunk_attn_int4kv.restype = i32
     lib.paged_prefill_chunk_attn_int4kv.argtypes = lib.paged_prefill_chunk_attn_kv8.argtypes
     _lib = lib
     return lib
 
 
+# decode kernel forms (the kernel_form argument of the INT8 / FP8 / INT4
+# decode calls): automatic, v_dot2, two-pass matrix-core, one-pass matrix-core
 DECODE_AUTO, DECODE_DOT, DECODE_MFMA, DECODE_MFMA_ONEPASS = 0, 1, 2, 3
-
-
-def kv8_set_decode_kernel(which):
-    """Choose the INT8/FP8 decode kernel form for this process:
-    DECODE_AUTO (by group size), DECODE_DOT (v_dot2), DECODE_MFMA (two-pass
-    matrix-core) or DECODE_MFMA_ONEPASS (one-pass matrix-core)."""
-    _check(load().kv8_set_decode_kernel(int(which)), "kv8_set_decode_kernel")
+MAX_DECODE_PAIRS = 65536
 
 
 def status_string(status):
@@ -188,7 +186,7 @@ def kv8_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_co
 
 
 def _decode(name, q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
-            max_context_len, out, workspace, sm_scale, tokens_per_split, stream):
+            max_context_len, out, workspace, sm_scale, tokens_per_split, kernel_form, stream):
     import torch
     b, hq, d = q.shape
     nb, hkv = k_cache.shape[0], k_cache.shape[1]
@@ -200,38 +198,42 @@ def _decode(name, q, k_cache, v_cache, k_scale, v_scale, block_table, context_le
         _ptr(block_table), block_table.shape[1], _ptr(context_lens), int(max_context_len),
         b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-        int(tokens_per_split), _stream(stream))
+        int(tokens_per_split), int(kernel_form), _stream(stream))
     _check(st, name)
 
 
 def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                           max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
-                          stream=None):
+                          kernel_form=DECODE_AUTO, stream=None):
     """q: fp32 or bf16 [B, Hq, d]; out fp32 [B, Hq, d]; workspace uint8 of at
-    least kv8_decode_workspace_size() bytes."""
+    least kv8_decode_workspace_size() bytes; kernel_form one of DECODE_*."""
     _decode("paged_decode_attn_kv8", q, k_cache, v_cache, k_scale, v_scale, block_table,
-            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split,
+            kernel_form, stream)
 
 
 def paged_decode_attn_int4kv(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                              max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
-                             stream=None):
+                             kernel_form=DECODE_AUTO, stream=None):
     """As paged_decode_attn_kv8, over an INT4 cache."""
     _decode("paged_decode_attn_int4kv", q, k_cache, v_cache, k_scale, v_scale, block_table,
-            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split,
+            kernel_form, stream)
 
 
 def paged_decode_attn_fp8kv(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
                             max_context_len, out, workspace, sm_scale=None, tokens_per_split=0,
-                            stream=None):
+                            kernel_form=DECODE_AUTO, stream=None):
     """As paged_decode_attn_kv8, over an FP8 (e4m3) cache."""
     _decode("paged_decode_attn_fp8kv", q, k_cache, v_cache, k_scale, v_scale, block_table,
-            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split, stream)
+            context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split,
+            kernel_form, stream)
 
 
 def paged_decode_attn_kv8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
                                  block_table, context_lens, max_context_len, out, workspace,
-                                 sm_scale=None, tokens_per_split=0, stream=None):
+                                 sm_scale=None, tokens_per_split=0, kernel_form=DECODE_AUTO,
+                                 stream=None):
     """One decode step: append k_new/v_new (bf16 [B, Hkv, d], the newest token
     of each sequence, at position context_lens[b] - 1), then decode."""
     import torch
@@ -246,7 +248,7 @@ def paged_decode_attn_kv8_append(q, k_new, v_new, k_cache, v_cache, k_scale, v_s
         int(max_context_len), b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out),
         _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-        int(tokens_per_split), _stream(stream))
+        int(tokens_per_split), int(kernel_form), _stream(stream))
     _check(st, "paged_decode_attn_kv8_append")
 
 
@@ -321,20 +323,30 @@ def paged_prefill_chunk_attn_int4kv(q, q_start_loc, max_q_len, k_cache, v_cache,
              sm_scale, stream)
 
 
-def kv8_read_probe(buf, tiles, tile_bytes, out, stream=None):
-    """Measurement utility: one launch of the read-only probe over `buf`
-    (uint8 device tensor) in the tile order `tiles` (int32); `out` uint32
-    [workgroups * 256] with workgroups = tiles.numel() * tile_bytes / bytes
-    per workgroup.  Returns the bytes the launch reads."""
-    lib = load()
-    per_wg = lib.kv8_read_probe_bytes_per_workgroup()
+def kv8_read_probe(buf, tiles, tile_bytes, workgroups, out, stream=None):
+    """Measurement utility: one launch of the random-tile read over `buf`
+    (uint8 device tensor) in the tile order `tiles` (int32; tiles.numel() *
+    tile_bytes must be a multiple of the chunk size) by `workgroups`
+    persistent workgroups; `out` uint32 [workgroups * 256].  Returns the
+    bytes the launch reads."""
     n_bytes = tiles.numel() * tile_bytes
-    wg = n_bytes // per_wg
-    if wg * 256 > out.numel():
+    if workgroups * 256 > out.numel():
         raise ValueError("out too small")
-    _check(lib.kv8_read_probe(_ptr(buf), _ptr(tiles), int(tile_bytes), int(wg), _ptr(out),
-                              _stream(stream)), "kv8_read_probe")
-    return wg * per_wg
+    _check(load().kv8_read_probe(_ptr(buf), _ptr(tiles), int(tile_bytes), int(n_bytes),
+                                 int(workgroups), _ptr(out), _stream(stream)), "kv8_read_probe")
+    return n_bytes
+
+
+def kv8_stream_read(buf, workgroups, out, stream=None):
+    """Measurement utility: one launch of the contiguous streaming read over
+    the whole of `buf` (uint8 device tensor, size a multiple of the chunk
+    size) by `workgroups` persistent workgroups; `out` uint32
+    [workgroups * 256].  Returns the bytes the launch reads."""
+    if workgroups * 256 > out.numel():
+        raise ValueError("out too small")
+    _check(load().kv8_stream_read(_ptr(buf), int(buf.numel()), int(workgroups), _ptr(out),
+                                  _stream(stream)), "kv8_stream_read")
+    return int(buf.numel())
 
 
 def alloc_cache(num_blocks, num_kv_heads, head_dim, device="cuda", fp8=False, int4=False):

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;   // 0.1.0
+constexpr int kVersion = 200;   // 0.2.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -57,8 +57,8 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                           const int32_t* context_lens, int max_context_len, int batch,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, int fmt, const uint16_t* k_new,
-                const uint16_t* v_new, void* stream) {
+                          int tokens_per_split, int kernel_form, int fmt, const uint16_t* k_new,
+                          const uint16_t* v_new, void* stream) {
   if (!q || !block_table || !context_lens || !out) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
   if (rc != KV8_OK) return rc;
@@ -66,8 +66,11 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return KV8_ERR_SHAPE;
   if (batch > 65535 || num_kv_heads > 65535) return KV8_ERR_SHAPE;
+  if ((int64_t)batch * num_kv_heads > kv8::kMaxDecodePairs) return KV8_ERR_SHAPE;
   if (q_dtype != KV8_F32 && q_dtype != KV8_BF16) return KV8_ERR_UNSUPPORTED;
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
+    return KV8_ERR_UNSUPPORTED;
+  if (kernel_form < KV8_DECODE_AUTO || kernel_form > KV8_DECODE_MFMA_ONEPASS)
     return KV8_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(out)) return KV8_ERR_ALIGN;
   if (tokens_per_split > 0 && (tokens_per_split % 64 != 0 || tokens_per_split > 2048))
@@ -75,7 +78,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
   kv8::DecodePlan plan;
   if (!kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                         tokens_per_split,
-                        kv8::decode_form(fmt, num_q_heads / num_kv_heads,
+                        kv8::decode_form(kernel_form, fmt, num_q_heads / num_kv_heads,
                                          (long long)batch * num_kv_heads *
                                              ((max_context_len + 1023) / 1024),
                                          max_context_len, head_dim),
@@ -148,17 +151,6 @@ const char* kv8_status_string(int status) {
 
 int kv8_version(void) { return kVersion; }
 
-int kv8_set_decode_kernel(int which) {
-  switch (which) {
-    case KV8_DECODE_AUTO: kv8::set_decode_kernel(kv8::kDecodeKernelAuto); break;
-    case KV8_DECODE_DOT: kv8::set_decode_kernel(kv8::kDecodeKernelDot); break;
-    case KV8_DECODE_MFMA: kv8::set_decode_kernel(kv8::kDecodeKernelMfma); break;
-    case KV8_DECODE_MFMA_ONEPASS: kv8::set_decode_kernel(kv8::kDecodeKernelMfmaOnePass); break;
-    default: return KV8_ERR_UNSUPPORTED;
-  }
-  return KV8_OK;
-}
-
 int kv8_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                      const int32_t* slot_mapping, int64_t n_tokens, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int8_t* k_cache,
@@ -210,8 +202,7 @@ int kv8_quant_append_int4(const uint16_t* k_new, const uint16_t* v_new,
 size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int tokens_per_split) {
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
-  // enough for every kernel form (the form follows the code format and the
-  // process-wide kernel setting at launch time)
+  // enough for every kernel form (a call may ask for any of them)
   size_t need = 0;
   for (int form : {kv8::kDecodeKernelDot, kv8::kDecodeKernelMfma, kv8::kDecodeKernelMfmaOnePass}) {
     kv8::DecodePlan plan;
@@ -229,11 +220,12 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
                           const int32_t* context_lens, int max_context_len, int batch,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                          int tokens_per_split, void* stream) {
+                          int tokens_per_split, int kernel_form, void* stream) {
   return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, kv8::kFmtInt8, nullptr, nullptr, stream);
+                     workspace_bytes, tokens_per_split, kernel_form, kv8::kFmtInt8, nullptr,
+                     nullptr, stream);
 }
 
 int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
@@ -243,12 +235,13 @@ int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,
                             const int32_t* context_lens, int max_context_len, int batch,
                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                             float sm_scale, float* out, void* workspace, size_t workspace_bytes,
-                            int tokens_per_split, void* stream) {
+                            int tokens_per_split, int kernel_form, void* stream) {
   return decode_impl(q, q_dtype, reinterpret_cast<const int8_t*>(k_cache),
                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, kv8::kFmtFp8, nullptr, nullptr, stream);
+                     workspace_bytes, tokens_per_split, kernel_form, kv8::kFmtFp8, nullptr,
+                     nullptr, stream);
 }
 
 int paged_decode_attn_kv8_append(const void* q, int q_dtype, const uint16_t* k_new,
@@ -258,13 +251,15 @@ int paged_decode_attn_kv8_append(const void* q, int q_dtype, const uint16_t* k_n
                                  const int32_t* context_lens, int max_context_len, int batch,
                                  int num_q_heads, int num_kv_heads, int head_dim,
                                  int block_size, float sm_scale, float* out, void* workspace,
-                                 size_t workspace_bytes, int tokens_per_split, void* stream) {
+                                 size_t workspace_bytes, int tokens_per_split, int kernel_form,
+                                 void* stream) {
   if (!k_new || !v_new) return KV8_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return KV8_ERR_ALIGN;
   return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                      max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, kv8::kFmtInt8, k_new, v_new, stream);
+                     workspace_bytes, tokens_per_split, kernel_form, kv8::kFmtInt8, k_new, v_new,
+                     stream);
 }
 
 int paged_decode_attn_int4kv(const void* q, int q_dtype, const uint8_t* k_cache,
@@ -274,12 +269,14 @@ int paged_decode_attn_int4kv(const void* q, int q_dtype, const uint8_t* k_cache,
                              const int32_t* context_lens, int max_context_len, int batch,
                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                              float sm_scale, float* out, void* workspace,
-                             size_t workspace_bytes, int tokens_per_split, void* stream) {
+                             size_t workspace_bytes, int tokens_per_split, int kernel_form,
+                             void* stream) {
   return decode_impl(q, q_dtype, reinterpret_cast<const int8_t*>(k_cache),
                      reinterpret_cast<const int8_t*>(v_cache), k_scale, v_scale, num_blocks,
                      block_table, max_blocks_per_seq, context_lens, max_context_len, batch,
                      num_q_heads, num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
-                     workspace_bytes, tokens_per_split, kv8::kFmtInt4, nullptr, nullptr, stream);
+                     workspace_bytes, tokens_per_split, kernel_form, kv8::kFmtInt4, nullptr,
+                     nullptr, stream);
 }
 
 int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache,
@@ -297,6 +294,7 @@ int paged_decode_attn_bf16kv(const void* q, int q_dtype, const uint16_t* k_cache
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return KV8_ERR_SHAPE;
   if (batch > 65535 || num_kv_heads > 65535) return KV8_ERR_SHAPE;
+  if ((int64_t)batch * num_kv_heads > kv8::kMaxDecodePairs) return KV8_ERR_SHAPE;
   if (q_dtype != KV8_F32 && q_dtype != KV8_BF16) return KV8_ERR_UNSUPPORTED;
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
     return KV8_ERR_UNSUPPORTED;
@@ -375,18 +373,30 @@ int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_lo
                       workspace_bytes, kv8::kFmtInt4, stream);
 }
 
-int64_t kv8_read_probe_bytes_per_workgroup(void) {
-  return kv8::read_probe_bytes_per_workgroup();
-}
+int64_t kv8_read_probe_chunk_bytes(void) { return kv8::read_probe_chunk_bytes(); }
 
-int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t workgroups,
-                   uint32_t* out, void* stream) {
+int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t n_bytes,
+                   int64_t workgroups, uint32_t* out, void* stream) {
   if (!buf || !tiles || !out) return KV8_ERR_NULL;
-  const int64_t per_wg = kv8::read_probe_bytes_per_workgroup();
-  if (tile_bytes < 16 || tile_bytes % 16 != 0 || per_wg % tile_bytes != 0) return KV8_ERR_SHAPE;
+  const int64_t chunk = kv8::read_probe_chunk_bytes();
+  if (tile_bytes < 256 || tile_bytes % 256 != 0 || chunk % tile_bytes != 0) return KV8_ERR_SHAPE;
+  if (n_bytes <= 0 || n_bytes % chunk != 0) return KV8_ERR_SHAPE;
   if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return KV8_ERR_SHAPE;
   if (!aligned16(buf)) return KV8_ERR_ALIGN;
-  return kv8::launch_read_probe(buf, tiles, tile_bytes, workgroups, out,
+  return kv8::launch_read_probe(buf, tiles, tile_bytes, n_bytes, workgroups, out,
+                                static_cast<hipStream_t>(stream)) == 0
+             ? KV8_OK
+             : KV8_ERR_HIP;
+}
+
+int kv8_stream_read(const void* buf, int64_t n_bytes, int64_t workgroups, uint32_t* out,
+                    void* stream) {
+  if (!buf || !out) return KV8_ERR_NULL;
+  const int64_t chunk = kv8::read_probe_chunk_bytes();
+  if (n_bytes <= 0 || n_bytes % chunk != 0) return KV8_ERR_SHAPE;
+  if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return KV8_ERR_SHAPE;
+  if (!aligned16(buf)) return KV8_ERR_ALIGN;
+  return kv8::launch_read_probe(buf, nullptr, 0, n_bytes, workgroups, out,
                                 static_cast<hipStream_t>(stream)) == 0
              ? KV8_OK
              : KV8_ERR_HIP;

@@ -468,11 +468,7 @@ bool dispatch_fmt(int head_dim, bool q_f32, int G, const SplitArgs& a, int batch
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-std::atomic<int> g_decode_kernel{kDecodeKernelAuto};
-
 }  // namespace
-
-void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_order_relaxed); }
 
 // Automatic choice (measured on MI355X): from four query heads per KV head
 // up, the dot-product kernel's vector work per cache byte (G/2 v_dot2 issues
@@ -493,10 +489,10 @@ void set_decode_kernel(int which) { g_decode_kernel.store(which, std::memory_ord
 //   kernel otherwise); from G = 4 the one-pass form (28.5 against 28.8 us
 //   for the two-pass form and 36.5 for v_dot2 on the Llama-3.1-8B-shaped
 //   batch; 1801 against 1971 and 2655 us on 31 sequences of 264192 tokens).
-int decode_form(int fmt, int G, long long grid_bound, int max_context_len, int head_dim) {
-  const int k = g_decode_kernel.load(std::memory_order_relaxed);
+int decode_form(int requested, int fmt, int G, long long grid_bound, int max_context_len,
+                int head_dim) {
   if (fmt == kFmtInt4 && head_dim != 128) return kDecodeKernelDot;
-  if (k != kDecodeKernelAuto) return k;
+  if (requested != kDecodeKernelAuto) return requested;
   if (fmt == kFmtInt4) return G >= 4 ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
   if (G >= 8) return kDecodeKernelMfmaOnePass;
   if (G >= 4)
@@ -509,6 +505,7 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                  int max_context_len, int tokens_per_split, int form, DecodePlan* plan) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
   if (num_q_heads % num_kv_heads != 0) return false;
+  if ((int64_t)batch * num_kv_heads > kMaxDecodePairs) return false;
   const int G = num_q_heads / num_kv_heads;
   // LDS of one workgroup at a split size: the one-pass kernel's does not
   // grow with the split
@@ -542,7 +539,7 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
   plan->form = form;
   plan->split_tokens = tps;
   plan->n_split = n_split;
-  plan->counter_bytes = align256((size_t)batch * num_kv_heads * sizeof(unsigned));
+  plan->counter_bytes = kCounterBytes;
   plan->o_bytes = align256((size_t)batch * num_q_heads * n_split * head_dim * sizeof(float));
   plan->lse_bytes = align256((size_t)batch * num_q_heads * n_split * sizeof(float));
   plan->total_bytes = plan->counter_bytes + plan->o_bytes + plan->lse_bytes;

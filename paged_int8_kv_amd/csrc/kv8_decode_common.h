@@ -127,18 +127,19 @@ struct SplitArgs {
 // Decode step with append: the newest token of sequence b sits at position
 // ctx - 1, inside the sequence's last split, so that split's workgroup
 // quantises the token's K and V rows of KV head g (as the append kernel
-// does) and stores them before its passes read the block back.  Called by
-// one whole wave; the stores complete (vmcnt 0) before it returns, so every
-// load the workgroup issues after its next barrier sees the new codes.
+// does) and stores them before its passes read the block back.  A block id
+// outside [0, num_blocks) stores nothing, as the append kernel skips such a
+// slot (the reads that follow clamp it, as every read does).  Called by one
+// whole wave; the stores complete (vmcnt 0) before it returns, so every load
+// the workgroup issues after its next barrier sees the new codes.
 template <int D, class C>
 __device__ __forceinline__ void append_newest(const SplitArgs& a, int b, int g, int ctx,
                                               int lane) {
   constexpr int LPR = D / 8;          // lanes per row, 8 values each
-  if (lane < LPR) {
-    const int p = ctx - 1;
+  const int p = ctx - 1;
+  const int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + p / kBlock];
+  if (lane < LPR && id >= 0 && id < a.num_blocks) {
     const int Hkv = a.num_kv_heads;
-    int64_t id = a.block_table[(int64_t)b * a.max_blocks_per_seq + p / kBlock];
-    id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
     const int64_t line = (id * Hkv + g) * kBlock + p % kBlock;
     const int64_t src = ((int64_t)b * Hkv + g) * D + lane * 8;
     float kx[8], vx[8], ka, va;

@@ -27,23 +27,32 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                              int8_t* v_cache, uint16_t* k_scale, uint16_t* v_scale,
                              hipStream_t stream);
 
-// Which form of the INT8 / FP8 decode kernel launches: automatic (by group
-// size), the v_dot2 kernel, the two-pass or the one-pass matrix-core kernel.
-// Process-wide.  decode_form: the form a launch of this code format, group
-// size, grid bound (workgroups with every sequence at the longest context
-// and 1024-token splits), longest context and head dim takes under the
-// current setting.
+// Which form of the INT8 / FP8 / INT4 decode kernel a call launches:
+// automatic (by group size and size), the v_dot2 kernel, the two-pass or the
+// one-pass matrix-core kernel.  A per-call choice (the library keeps no
+// setting).  decode_form: the form a launch of this code format, group size,
+// grid bound (workgroups with every sequence at the longest context and
+// 1024-token splits), longest context and head dim takes when `requested`
+// is asked for.
 enum : int {
   kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3
 };
-void set_decode_kernel(int which);
-int decode_form(int fmt, int G, long long grid_bound, int max_context_len, int head_dim);
+int decode_form(int requested, int fmt, int G, long long grid_bound, int max_context_len,
+                int head_dim);
+
+// The decode workspace starts with a fixed region of per-(sequence, KV
+// head) split counters, one uint32 per pair at index b * Hkv + g, for up to
+// kMaxDecodePairs pairs; the partial results follow it.  Because the
+// counters never move with the shape, a workspace zero-filled once stays
+// ready for every later call of any shape (the counters reset themselves).
+constexpr int64_t kMaxDecodePairs = 65536;
+constexpr size_t kCounterBytes = (size_t)kMaxDecodePairs * sizeof(unsigned);
 
 struct DecodePlan {
   int form;              // kDecodeKernelDot / Mfma / MfmaOnePass
   int split_tokens;      // tokens per workgroup (multiple of 64)
   int n_split;           // workgroups per (sequence, KV head)
-  size_t counter_bytes;  // uint32 [B, Hkv] finished-split counters (self-resetting)
+  size_t counter_bytes;  // kCounterBytes: uint32 finished-split counters (self-resetting)
   size_t o_bytes;        // partial outputs  fp32 [B, Hq, n_split, d]
   size_t lse_bytes;      // partial log2-sum-exp fp32 [B, Hq, n_split]
   size_t total_bytes;
@@ -75,9 +84,12 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
                    int fmt, hipStream_t stream);
 
-// The read-only probe behind kv8_read_probe (kv8_probe.hip).
-int64_t read_probe_bytes_per_workgroup();
-int launch_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t workgroups,
-                      uint32_t* out, hipStream_t stream);
+// The read-only kernels behind kv8_read_probe (tiles given) and
+// kv8_stream_read (tiles null: contiguous), in kv8_probe.hip: `workgroups`
+// persistent workgroups read n_bytes (a multiple of read_probe_chunk_bytes)
+// in chunks.
+int64_t read_probe_chunk_bytes();
+int launch_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t n_bytes,
+                      int64_t workgroups, uint32_t* out, hipStream_t stream);
 
 }  // namespace kv8

@@ -15,11 +15,12 @@ def pytest_configure(config):
 
 @pytest.fixture(params=["dot", "mfma", "mfma1"])
 def decode_kernel(request):
-    """Run a test under each form of the INT8/FP8 decode kernel (v_dot2,
-    two-pass and one-pass matrix-core), restoring the automatic choice
-    afterwards."""
+    """Run a test under each form of the INT8/FP8/INT4 decode kernel (v_dot2,
+    two-pass and one-pass matrix-core): the test helpers pass the form as
+    the kernel_form argument of every decode call they make."""
     from paged_int8_kv_amd import binding as B
-    B.kv8_set_decode_kernel({"dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
-                             "mfma1": B.DECODE_MFMA_ONEPASS}[request.param])
+    from tests import kv8_testutil as U
+    U.FORM = {"dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
+              "mfma1": B.DECODE_MFMA_ONEPASS}[request.param]
     yield request.param
-    B.kv8_set_decode_kernel(B.DECODE_AUTO)
+    U.FORM = B.DECODE_AUTO

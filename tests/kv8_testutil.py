@@ -14,6 +14,14 @@ REL_L2 = 1e-3
 
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")
 
+# Decode kernel form the helpers pass to every decode call (the
+# decode_kernel fixture sets it per test; the library keeps no setting).
+FORM = B.DECODE_AUTO
+
+
+def form(kernel_form=None):
+    return FORM if kernel_form is None else kernel_form
+
 
 def dev():
     return torch.device("cuda:0")
@@ -67,7 +75,7 @@ def q_tensor(case, q=None):
 
 
 def gpu_decode(case, cache, q=None, tokens_per_split=0, block_table=None, context_lens=None,
-               max_context_len=None, sm_scale=None, workspace=None):
+               max_context_len=None, sm_scale=None, workspace=None, kernel_form=None):
     bt = case.block_table if block_table is None else block_table
     cl = case.context_lens if context_lens is None else context_lens
     mcl = int(np.max(cl)) if max_context_len is None else max_context_len
@@ -79,7 +87,8 @@ def gpu_decode(case, cache, q=None, tokens_per_split=0, block_table=None, contex
     B.paged_decode_attn_kv8(qt, *cache,
                             torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev()),
                             torch.from_numpy(np.ascontiguousarray(cl, np.int32)).to(dev()),
-                            mcl, out, ws, sm_scale=sm_scale, tokens_per_split=tokens_per_split)
+                            mcl, out, ws, sm_scale=sm_scale, tokens_per_split=tokens_per_split,
+                            kernel_form=form(kernel_form))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

@@ -37,7 +37,7 @@ def test_status_strings_and_version():
     for st in range(-6, 1):
         assert B.status_string(st).startswith("KV8_")
     assert "unknown" in B.status_string(-99)
-    assert B.load().kv8_version() >= 100
+    assert B.load().kv8_version() == 200
 
 
 def append(fn="kv8_quant_append", **kw):
@@ -70,12 +70,12 @@ def test_append_validation(kw, expected):
 def decode(fn="paged_decode_attn_kv8", **kw):
     a = dict(q=P, dt=B.KV8_BF16, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
              maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, ws=P2,
-             wsb=1 << 30, tps=0, stream=None)
+             wsb=1 << 30, tps=0, form=B.DECODE_AUTO, stream=None)
     a.update(kw)
     return getattr(B.load(), fn)(
         a["q"], a["dt"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"], a["bt"], a["mbs"],
         a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"],
-        a["out"], a["ws"], a["wsb"], a["tps"], a["stream"])
+        a["out"], a["ws"], a["wsb"], a["tps"], a["form"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expected", [
@@ -100,9 +100,46 @@ def decode(fn="paged_decode_attn_kv8", **kw):
     (dict(out=MIS), B.KV8_ERR_ALIGN),
     (dict(ws=None), B.KV8_ERR_WORKSPACE),
     (dict(wsb=16), B.KV8_ERR_WORKSPACE),
+    (dict(form=-1), B.KV8_ERR_UNSUPPORTED),
+    (dict(form=4), B.KV8_ERR_UNSUPPORTED),
+    (dict(b=8193), B.KV8_ERR_SHAPE),            # batch * Hkv above KV8_DECODE_MAX_PAIRS
+    (dict(b=8192, ws=None), B.KV8_ERR_WORKSPACE),   # exactly at the limit: accepted
 ])
 def test_decode_validation(kw, expected):
     assert decode(**kw) == expected
+
+
+@pytest.mark.parametrize("form", [B.DECODE_AUTO, B.DECODE_DOT, B.DECODE_MFMA,
+                                  B.DECODE_MFMA_ONEPASS])
+@pytest.mark.parametrize("fn", ["paged_decode_attn_kv8", "paged_decode_attn_fp8kv",
+                                "paged_decode_attn_int4kv"])
+def test_decode_kernel_form_argument_accepted(fn, form):
+    """Every kernel form passes validation (the call then stops at the
+    missing workspace, before any HIP call)."""
+    assert decode(fn=fn, form=form, ws=None) == B.KV8_ERR_WORKSPACE
+    assert decode(fn=fn, form=form + 4) == B.KV8_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("form,tps,expected", [
+    (B.DECODE_DOT, 1280, B.KV8_ERR_WORKSPACE), (B.DECODE_DOT, 1344, B.KV8_ERR_UNSUPPORTED),
+    (B.DECODE_MFMA, 1280, B.KV8_ERR_WORKSPACE), (B.DECODE_MFMA, 1344, B.KV8_ERR_UNSUPPORTED),
+    (B.DECODE_MFMA_ONEPASS, 2048, B.KV8_ERR_WORKSPACE),
+])
+def test_decode_split_limit_per_form_at_g8(form, tps, expected):
+    """At G = 8 the forms that hold a split's logits in LDS accept at most
+    1280 tokens per split; the one-pass form takes up to 2048."""
+    assert decode(hq=64, hkv=8, tps=tps, form=form, ws=None) == expected
+
+
+def test_decode_workspace_counter_region_fixed():
+    """The counters occupy a fixed prefix of KV8_DECODE_MAX_PAIRS uint32
+    whatever the shape, so a single-split call needs exactly that prefix
+    plus its partial arrays, and the limit on pairs is enforced."""
+    assert B.MAX_DECODE_PAIRS == 65536
+    one = B.kv8_decode_workspace_size(1, 4, 1, 64, 64, 64)
+    assert one == 4 * 65536 + 1024 + 256     # counters + o (4 heads x 64 fp32) + lse, 256-aligned
+    assert B.kv8_decode_workspace_size(8193, 8, 8, 128, 64, 0) == 0
+    assert B.kv8_decode_workspace_size(8192, 8, 8, 128, 64, 0) > 0
 
 
 def decode_bf16kv(**kw):
@@ -146,8 +183,9 @@ def test_decode_bf16kv_validation(kw, expected):
 def test_decode_workspace_size():
     ws = B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 512)
     n_split = 8
-    assert ws >= 32 * 32 * n_split * (128 + 1) * 4
-    assert ws < 32 * 32 * n_split * (128 + 1) * 4 + 32 * 8 * 4 + 1024   # + split counters
+    counters = 4 * B.MAX_DECODE_PAIRS                # fixed counter region
+    assert ws >= counters + 32 * 32 * n_split * (128 + 1) * 4
+    assert ws < counters + 32 * 32 * n_split * (128 + 1) * 4 + 512
     assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 0) > 0
     assert B.kv8_decode_workspace_size(32, 30, 8, 128, 4096, 0) == 0
     assert B.kv8_decode_workspace_size(32, 32, 8, 96, 4096, 0) == 0
@@ -253,19 +291,6 @@ def test_int4_decode_validation_matches_int8(kw):
     assert decode(fn="paged_decode_attn_int4kv", **kw) == decode(**kw)
 
 
-def test_set_decode_kernel_values():
-    """Host-side only: the four kernel-form values are accepted, others are
-    rejected with the setting unchanged; the automatic choice is restored."""
-    lib = B.load()
-    try:
-        for which in (B.DECODE_DOT, B.DECODE_MFMA, B.DECODE_MFMA_ONEPASS, B.DECODE_AUTO):
-            assert lib.kv8_set_decode_kernel(which) == B.KV8_OK
-        for bad in (-1, 4, 99):
-            assert lib.kv8_set_decode_kernel(bad) == B.KV8_ERR_UNSUPPORTED
-    finally:
-        lib.kv8_set_decode_kernel(B.DECODE_AUTO)
-
-
 def test_decode_workspace_covers_every_form():
     """The workspace query sizes for the smallest default split any kernel
     form may take: at G = 8 and 64 sequences of up to 16384 tokens the
@@ -286,15 +311,31 @@ def test_int4_prefill_validation_matches_int8(kw):
 
 def test_read_probe_validation():
     """Host-side checks of the measurement probe: null pointers, tile sizes
-    that are not a multiple of 16 or do not divide the 32 KB per workgroup,
-    workgroup counts out of range, a misaligned buffer."""
+    that are not a multiple of 256 or do not divide the 32 KB chunk, byte
+    counts that are not whole chunks, workgroup counts out of range, a
+    misaligned buffer."""
     lib = B.load()
-    assert lib.kv8_read_probe_bytes_per_workgroup() == 32768
-    assert lib.kv8_read_probe(None, P, 2048, 10, P2, None) == B.KV8_ERR_NULL
-    assert lib.kv8_read_probe(P, None, 2048, 10, P2, None) == B.KV8_ERR_NULL
-    assert lib.kv8_read_probe(P, P, 2048, 10, None, None) == B.KV8_ERR_NULL
-    for bad in (0, 8, 24, 3000, 65536):
-        assert lib.kv8_read_probe(P, P, bad, 10, P2, None) == B.KV8_ERR_SHAPE
-    assert lib.kv8_read_probe(P, P, 2048, 0, P2, None) == B.KV8_ERR_SHAPE
-    assert lib.kv8_read_probe(P, P, 2048, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
-    assert lib.kv8_read_probe(MIS, P, 2048, 10, P2, None) == B.KV8_ERR_ALIGN
+    assert lib.kv8_read_probe_chunk_bytes() == 32768
+    n = 10 * 32768
+    assert lib.kv8_read_probe(None, P, 2048, n, 10, P2, None) == B.KV8_ERR_NULL
+    assert lib.kv8_read_probe(P, None, 2048, n, 10, P2, None) == B.KV8_ERR_NULL
+    assert lib.kv8_read_probe(P, P, 2048, n, 10, None, None) == B.KV8_ERR_NULL
+    for bad in (0, 16, 24, 128, 768, 3000, 65536):
+        assert lib.kv8_read_probe(P, P, bad, n, 10, P2, None) == B.KV8_ERR_SHAPE
+    for bad_n in (0, -32768, 32768 + 16):
+        assert lib.kv8_read_probe(P, P, 2048, bad_n, 10, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(P, P, 2048, n, 0, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(P, P, 2048, n, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_read_probe(MIS, P, 2048, n, 10, P2, None) == B.KV8_ERR_ALIGN
+
+
+def test_stream_read_validation():
+    lib = B.load()
+    n = 10 * 32768
+    assert lib.kv8_stream_read(None, n, 10, P2, None) == B.KV8_ERR_NULL
+    assert lib.kv8_stream_read(P, n, 10, None, None) == B.KV8_ERR_NULL
+    for bad_n in (0, -32768, 32768 + 16):
+        assert lib.kv8_stream_read(P, bad_n, 10, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_stream_read(P, n, 0, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_stream_read(P, n, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
+    assert lib.kv8_stream_read(MIS, n, 10, P2, None) == B.KV8_ERR_ALIGN

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from oracle import kv8_oracle as O
+from paged_int8_kv_amd import binding as B
 from paged_int8_kv_amd import workloads as W
 from tests.kv8_testutil import (check_close, dev, gpu_append, gpu_decode, needs_gpu,
                                 oracle_cache, upload_cache)
@@ -176,8 +177,29 @@ def test_decode_workspace_reused_across_calls():
                              workspace=ws)
             ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
             check_close(out, ref, f"reused workspace tps={tps}")
-    nb = 8 * 8 * 4      # counters of the largest (B, Hkv) used: all back to zero
-    assert int(ws[:nb].count_nonzero()) == 0
+    assert int(ws[:4 * B.MAX_DECODE_PAIRS].count_nonzero()) == 0   # counters back to zero
+
+
+def test_decode_workspace_reused_across_pair_counts():
+    """One zero-filled workspace reused while batch * Hkv crosses a
+    64-counter boundary both ways (8x8 -> 32x8 -> 3x8 -> 32x8 pairs): the
+    counters live at fixed positions ahead of every partial, so no call
+    reads a counter another call's partials overwrote; every output element
+    is written (NaN-filled beforehand) and within tolerance."""
+    def case_of(batch, seed):
+        rng = np.random.default_rng(seed)
+        return W.make_paged_case(batch=batch, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                 context_lens=list(rng.integers(300, 2500, batch)), seed=seed)
+    cases = [case_of(8, 70), case_of(32, 71), case_of(3, 72), case_of(32, 73)]
+    ws = torch.zeros(max(B.kv8_decode_workspace_size(c.batch, 32, 8, 128,
+                                                     int(c.context_lens.max()), 128)
+                         for c in cases), dtype=torch.uint8, device=dev())
+    for c in cases:
+        kc, vc, ks, vs = oracle_cache(c)
+        out = gpu_decode(c, upload_cache(kc, vc, ks, vs), tokens_per_split=128, workspace=ws)
+        ref = O.paged_decode(c.q, kc, vc, ks, vs, c.block_table, c.context_lens)
+        check_close(out, ref, f"reused workspace, {c.batch} sequences")
+    assert int(ws[:4 * B.MAX_DECODE_PAIRS].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("tps", [0, 128, 1024])

@@ -12,6 +12,7 @@ import torch
 from oracle import kv8_oracle as O
 from paged_int8_kv_amd import binding as B
 from paged_int8_kv_amd import workloads as W
+from tests import kv8_testutil as U
 from tests.kv8_testutil import (bits_tensor, check_close, dev, download_cache, needs_gpu,
                                 oracle_cache, q_tensor, upload_cache)
 from tests.test_gpu_append import assert_cache_equal
@@ -53,25 +54,28 @@ def new_tokens(case, idx):
     return bits_tensor(kb).view(torch.bfloat16), bits_tensor(vb).view(torch.bfloat16)
 
 
-def run_step(case, cache, kn, vn, tps=0, fused=True):
+def run_step(case, cache, kn, vn, tps=0, fused=True, block_table=None):
+    bt = case.block_table if block_table is None else block_table
     qt = q_tensor(case)
     b, hq, d = qt.shape
     mcl = int(case.context_lens.max())
     ws = torch.zeros(B.kv8_decode_workspace_size(b, hq, case.num_kv_heads, d, mcl, tps),
                      dtype=torch.uint8, device=dev())
     out = torch.full((b, hq, d), float("nan"), dtype=torch.float32, device=dev())
-    table = torch.from_numpy(case.block_table).to(dev())
+    table = torch.from_numpy(np.ascontiguousarray(bt, np.int32)).to(dev())
     lens = torch.from_numpy(case.context_lens).to(dev())
     if fused:
         B.paged_decode_attn_kv8_append(qt, kn, vn, *cache, table, lens, mcl, out, ws,
-                                       tokens_per_split=tps)
+                                       tokens_per_split=tps, kernel_form=U.form())
     else:
         p = case.context_lens.astype(np.int64) - 1
         slots = np.where(case.context_lens > 0,
-                         case.block_table[np.arange(case.batch), np.maximum(p, 0) // 16] * 16
-                         + np.maximum(p, 0) % 16, -1).astype(np.int32)
+                         bt[np.arange(case.batch), np.maximum(p, 0) // 16].astype(np.int64)
+                         * 16 + np.maximum(p, 0) % 16, -1)
+        slots = np.where((slots < 0) | (slots >= 16 * case.num_blocks), -1, slots).astype(np.int32)
         B.kv8_quant_append(kn, vn, torch.from_numpy(slots).to(dev()), *cache)
-        B.paged_decode_attn_kv8(qt, *cache, table, lens, mcl, out, ws, tokens_per_split=tps)
+        B.paged_decode_attn_kv8(qt, *cache, table, lens, mcl, out, ws, tokens_per_split=tps,
+                                kernel_form=U.form())
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -134,9 +138,40 @@ def test_fused_steps_long_context_loop():
         q = torch.from_numpy(case.extra["step_q"][s].astype(np.float32)).to(dev())
         out = torch.empty((4, 32, 128), dtype=torch.float32, device=dev())
         B.paged_decode_attn_kv8_append(q, kn, vn, *cache, table, torch.from_numpy(ctx).to(dev()),
-                                       int(ctx.max()), out, ws)
+                                       int(ctx.max()), out, ws, kernel_form=U.form())
         if s in (0, 7):
             ref = O.paged_decode(case.extra["step_q"][s], kc, vc, ks, vs, case.block_table, ctx)
             check_close(out.cpu().numpy(), ref, f"fused long-context step {s}")
     torch.cuda.synchronize()
     assert_cache_equal(download_cache(cache), (kc, vc, ks, vs), "fused loop cache")
+
+
+def test_fused_step_bad_last_block_id_matches_separate_calls():
+    """A last-block id outside [0, num_blocks) (-1, num_blocks, a large
+    value): the fused step stores nothing, as kv8_quant_append skips such a
+    slot, so cache and output are bitwise those of the two separate calls
+    and no other sequence's block is touched."""
+    case = W.make_paged_case(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             context_lens=[40, 17, 300, 1], seed=97)
+    idx = newest_rows(case)
+    before = cache_before_step(case, idx)
+    kn, vn = new_tokens(case, idx)
+    bt = case.block_table.copy()
+    last = (case.context_lens - 1) // 16
+    bt[0, last[0]] = -1
+    bt[1, last[1]] = case.num_blocks
+    bt[2, last[2]] = 1 << 30
+    fused_cache = upload_cache(*before)
+    sep_cache = upload_cache(*before)
+    out_f = run_step(case, fused_cache, kn, vn, fused=True, block_table=bt)
+    out_s = run_step(case, sep_cache, kn, vn, fused=False, block_table=bt)
+    got = download_cache(fused_cache)
+    assert_cache_equal(got, download_cache(sep_cache), "fused vs separate cache, bad ids")
+    assert np.array_equal(out_f, out_s), "fused vs separate output, bad ids"
+    # only sequence 3's newest slot was written
+    exp = [a.copy() for a in before]
+    full = oracle_cache(case)
+    blk, off = divmod(int(case.slot_mapping[idx[3]]), 16)
+    for e, f in zip(exp, full):
+        e[blk, :, off] = f[blk, :, off]
+    assert_cache_equal(got, tuple(exp), "cache after bad ids")

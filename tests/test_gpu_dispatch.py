@@ -24,14 +24,8 @@ FORMS = {"dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA, "mfma1": B.DECODE_MFMA_ONEP
 
 
 def run_forms(run):
-    outs = {}
-    try:
-        for name, which in [("auto", B.DECODE_AUTO)] + list(FORMS.items()):
-            B.kv8_set_decode_kernel(which)
-            outs[name] = run()
-    finally:
-        B.kv8_set_decode_kernel(B.DECODE_AUTO)
-    return outs
+    """run(kernel_form) under the automatic choice and every form."""
+    return {name: run(which) for name, which in [("auto", B.DECODE_AUTO)] + list(FORMS.items())}
 
 
 @pytest.mark.parametrize("hq,hkv,lens,expected", [
@@ -45,7 +39,7 @@ def test_auto_form_int8(hq, hkv, lens, expected):
                              context_lens=lens, q_dtype="bf16", k_outliers=True, seed=hq + sum(lens))
     kc, vc, ks, vs = oracle_cache(case)
     cache = upload_cache(kc, vc, ks, vs)
-    outs = run_forms(lambda: gpu_decode(case, cache))
+    outs = run_forms(lambda f: gpu_decode(case, cache, kernel_form=f))
     assert np.array_equal(outs["auto"], outs[expected]), f"auto is not {expected}"
     for other in FORMS:
         if other != expected:
@@ -63,7 +57,7 @@ def test_auto_form_int4(lens, expected):
                              seed=91 + sum(lens))
     host = oracle_cache_int4(case)
     cache = upload_int4(*host)
-    outs = run_forms(lambda: gpu_decode_int4(case, cache))
+    outs = run_forms(lambda f: gpu_decode_int4(case, cache, kernel_form=f))
     assert np.array_equal(outs["auto"], outs[expected])
     for other in FORMS:
         if other != expected:
@@ -74,11 +68,11 @@ def test_auto_form_int4(lens, expected):
 
 def test_int4_head_dim_64_takes_dot():
     """The matrix-core forms serve INT4 at d = 128 only: at d = 64 every
-    setting runs the v_dot2 kernel."""
+    requested form runs the v_dot2 kernel."""
     case = W.make_paged_case(batch=2, num_q_heads=16, num_kv_heads=4, head_dim=64,
                              context_lens=[700, 33], q_dtype="bf16", seed=17)
     host = oracle_cache_int4(case)
     cache = upload_int4(*host)
-    outs = run_forms(lambda: gpu_decode_int4(case, cache))
+    outs = run_forms(lambda f: gpu_decode_int4(case, cache, kernel_form=f))
     for name in ("auto", "mfma", "mfma1"):
         assert np.array_equal(outs[name], outs["dot"]), name

@@ -12,6 +12,7 @@ import torch
 from oracle import kv8_oracle as O
 from paged_int8_kv_amd import binding as B
 from paged_int8_kv_amd import workloads as W
+from tests import kv8_testutil as U
 from tests.kv8_testutil import (bits_tensor, check_close, dev, f16_to_i16, needs_gpu,
                                 q_tensor)
 from tests.test_gpu_append import assert_cache_equal, rows_case
@@ -47,7 +48,7 @@ def gpu_append_fp8(case, cache=None, slots=None):
     return cache
 
 
-def gpu_decode_fp8(case, cache, tokens_per_split=0, q=None):
+def gpu_decode_fp8(case, cache, tokens_per_split=0, q=None, kernel_form=None):
     qt = q_tensor(case, q)
     b, hq, d = qt.shape
     mcl = int(case.context_lens.max())
@@ -57,7 +58,8 @@ def gpu_decode_fp8(case, cache, tokens_per_split=0, q=None):
     out = torch.full((b, hq, d), float("nan"), dtype=torch.float32, device=dev())
     B.paged_decode_attn_fp8kv(qt, *cache, torch.from_numpy(case.block_table).to(dev()),
                               torch.from_numpy(case.context_lens).to(dev()), mcl, out, ws,
-                              tokens_per_split=tokens_per_split)
+                              tokens_per_split=tokens_per_split,
+                              kernel_form=U.form(kernel_form))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
