@@ -252,6 +252,38 @@ int paged_decode_attn_kv8(const void* q, int q_dtype,
                           int tokens_per_split, int kernel_form, void* stream);
 
 /*
+ * paged_decode_attn_kv8_noalloc - paged_decode_attn_kv8 for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation,
+ * kernels and results (bitwise those of paged_decode_attn_kv8 with the
+ * same tokens_per_split and kernel_form), with no workspace argument.  The
+ * split counters and partial results live in a fixed scratch array of
+ * KV8_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends; the call allocates and frees nothing.
+ * The first call on a device resolves that device's scratch address and
+ * clears its counters with a kernel on `stream`.
+ *   arguments     as for paged_decode_attn_kv8, without workspace and
+ *                 workspace_bytes
+ * Returns as paged_decode_attn_kv8, and KV8_ERR_WORKSPACE when the call
+ * needs more than KV8_DECODE_NOALLOC_SCRATCH_BYTES (the size
+ * kv8_decode_workspace_size reports for the same sizes, tokens_per_split
+ * and kernel form), before any HIP call.  Every call on a device shares
+ * that device's scratch: calls that overlap in time on one device (several
+ * streams or host threads) race and give undefined results.
+ */
+#define KV8_DECODE_NOALLOC_SCRATCH_BYTES 33554432
+int paged_decode_attn_kv8_noalloc(const void* q, int q_dtype,
+                                  const int8_t* k_cache, const int8_t* v_cache,
+                                  const uint16_t* k_scale, const uint16_t* v_scale,
+                                  int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks_per_seq,
+                                  const int32_t* context_lens, int max_context_len,
+                                  int batch, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, float sm_scale,
+                                  float* out, int tokens_per_split, int kernel_form,
+                                  void* stream);
+
+/*
  * paged_decode_attn_kv8_append - one decode step in one launch: append the
  * newest token of every sequence, then paged_decode_attn_kv8.  The result
  * (cache contents and output) is that of kv8_quant_append on the new

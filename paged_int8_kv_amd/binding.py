@@ -30,7 +30,7 @@ EXPORTED = (
     "paged_prefill_chunk_attn_fp8kv", "kv8_rope_quant_append", "paged_decode_attn_kv8_append",
     "kv8_quant_append_int4", "paged_decode_attn_int4kv",
     "paged_prefill_chunk_attn_int4kv", "kv8_read_probe_chunk_bytes", "kv8_read_probe",
-    "kv8_stream_read",
+    "kv8_stream_read", "paged_decode_attn_kv8_noalloc",
 )
 
 _lib = None
@@ -76,6 +76,10 @@ def load():
     lib.paged_decode_attn_kv8.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp, i32,
                                           i32, i32, i32, i32, i32, f32, vp, vp, sz, i32, i32,
                                           vp]
+    lib.paged_decode_attn_kv8_noalloc.restype = i32
+    lib.paged_decode_attn_kv8_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, i64, vp, i32, vp,
+                                                  i32, i32, i32, i32, i32, i32, f32, vp, i32,
+                                                  i32, vp]
     lib.paged_decode_attn_kv8_append.restype = i32
     lib.paged_decode_attn_kv8_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, i32,
                                                  vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
@@ -210,6 +214,28 @@ def paged_decode_attn_kv8(q, k_cache, v_cache, k_scale, v_scale, block_table, co
     _decode("paged_decode_attn_kv8", q, k_cache, v_cache, k_scale, v_scale, block_table,
             context_lens, max_context_len, out, workspace, sm_scale, tokens_per_split,
             kernel_form, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_decode_attn_kv8_noalloc(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                  context_lens, max_context_len, out, sm_scale=None,
+                                  tokens_per_split=0, kernel_form=DECODE_AUTO, stream=None):
+    """As paged_decode_attn_kv8 with the library's fixed scratch in place of
+    a workspace: allocates nothing (calls that overlap on one device race)."""
+    import torch
+    b, hq, d = q.shape
+    nb, hkv = k_cache.shape[0], k_cache.shape[1]
+    dt = KV8_BF16 if q.dtype == torch.bfloat16 else KV8_F32
+    if sm_scale is None:
+        sm_scale = d ** -0.5
+    st = load().paged_decode_attn_kv8_noalloc(
+        _ptr(q), dt, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nb,
+        _ptr(block_table), block_table.shape[1], _ptr(context_lens), int(max_context_len),
+        b, hq, hkv, d, BLOCK_SIZE, float(sm_scale), _ptr(out), int(tokens_per_split),
+        int(kernel_form), _stream(stream))
+    _check(st, "paged_decode_attn_kv8_noalloc")
 
 
 def paged_decode_attn_int4kv(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,

@@ -9,6 +9,9 @@
 
 #include "kv8_launch.h"
 
+static_assert(kv8::kDecodeScratchBytes == KV8_DECODE_NOALLOC_SCRATCH_BYTES,
+              "the header states the allocation-free decode's scratch size");
+
 namespace {
 
 constexpr int kVersion = 200;   // 0.2.0
@@ -58,7 +61,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                           int tokens_per_split, int kernel_form, int fmt, const uint16_t* k_new,
-                          const uint16_t* v_new, void* stream) {
+                          const uint16_t* v_new, void* stream, bool use_scratch = false) {
   if (!q || !block_table || !context_lens || !out) return KV8_ERR_NULL;
   const int rc = check_cache(k_cache, v_cache, k_scale, v_scale, num_blocks, block_size);
   if (rc != KV8_OK) return rc;
@@ -84,8 +87,16 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
                                          max_context_len, head_dim),
                         &plan))
     return KV8_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return KV8_ERR_ALIGN;
+  if (use_scratch) {
+    // allocation-free entry: the library's fixed scratch stands in for the
+    // workspace; a call that needs more is rejected before any HIP call
+    if (plan.total_bytes > kv8::kDecodeScratchBytes) return KV8_ERR_WORKSPACE;
+    workspace = kv8::decode_scratch(static_cast<hipStream_t>(stream));
+    if (!workspace) return KV8_ERR_HIP;
+  } else {
+    if (!workspace || workspace_bytes < plan.total_bytes) return KV8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KV8_ERR_ALIGN;
+  }
   const long long cap_blocks = (long long)max_blocks_per_seq * KV8_BLOCK_SIZE;
   const int ctx_cap = (int)(cap_blocks < max_context_len ? cap_blocks : max_context_len);
   const int r = kv8::launch_decode(q, q_dtype == KV8_F32, k_cache, v_cache, k_scale, v_scale,
@@ -226,6 +237,21 @@ int paged_decode_attn_kv8(const void* q, int q_dtype, const int8_t* k_cache,
                      num_kv_heads, head_dim, block_size, sm_scale, out, workspace,
                      workspace_bytes, tokens_per_split, kernel_form, kv8::kFmtInt8, nullptr,
                      nullptr, stream);
+}
+
+int paged_decode_attn_kv8_noalloc(const void* q, int q_dtype, const int8_t* k_cache,
+                                  const int8_t* v_cache, const uint16_t* k_scale,
+                                  const uint16_t* v_scale, int64_t num_blocks,
+                                  const int32_t* block_table, int max_blocks_per_seq,
+                                  const int32_t* context_lens, int max_context_len, int batch,
+                                  int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, float sm_scale, float* out,
+                                  int tokens_per_split, int kernel_form, void* stream) {
+  return decode_impl(q, q_dtype, k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
+                     max_blocks_per_seq, context_lens, max_context_len, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, sm_scale, out, nullptr, 0,
+                     tokens_per_split, kernel_form, kv8::kFmtInt8, nullptr, nullptr, stream,
+                     /*use_scratch=*/true);
 }
 
 int paged_decode_attn_fp8kv(const void* q, int q_dtype, const uint8_t* k_cache,

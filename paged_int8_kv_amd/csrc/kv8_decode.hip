@@ -39,11 +39,59 @@
 // Each wave keeps kPf blocks in flight in a register ring; the ring is
 // branch-free around its loads so that the compiler's wait counts stay
 // exact, and scheduling barriers keep later slots' waits from being hoisted.
+#include <mutex>
+
 #include "kv8_decode_common.h"
 #include "kv8_device.h"
 #include "kv8_launch.h"
 
 namespace kv8 {
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry (paged_decode_attn_kv8_noalloc):
+// a fixed device array that stands in for the caller's workspace, laid out
+// as a workspace is (the split counters first, then the partials).  Each
+// device the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel: decode_scratch
+// resolves this device's address with hipGetSymbolAddress once, with the
+// device current, and returns that address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+}  // namespace
+
+void* decode_scratch(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p != nullptr) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+    return nullptr;
+  // The counters must start at zero: clear them once, by a kernel on the
+  // caller's stream (ordered before the call's own launch), after which
+  // every completed call leaves them at zero again.
+  const int64_t words = (int64_t)(kCounterBytes / sizeof(unsigned));
+  zero_words_kernel<<<dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream>>>(
+      static_cast<unsigned*>(addr), words);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  g_scratch_ptr[dev].store(addr, std::memory_order_release);
+  return addr;
+}
 
 namespace {
 

@@ -48,6 +48,13 @@ int decode_form(int requested, int fmt, int G, long long grid_bound, int max_con
 constexpr int64_t kMaxDecodePairs = 65536;
 constexpr size_t kCounterBytes = (size_t)kMaxDecodePairs * sizeof(unsigned);
 
+// Fixed scratch of the allocation-free decode entry: its bytes, and this
+// device's address of it (resolved once per device; on the first call the
+// counter prefix is cleared by a kernel on `stream`).  nullptr on a HIP
+// error.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+void* decode_scratch(hipStream_t stream);
+
 struct DecodePlan {
   int form;              // kDecodeKernelDot / Mfma / MfmaOnePass
   int split_tokens;      // tokens per workgroup (multiple of 64)

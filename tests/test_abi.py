@@ -339,3 +339,44 @@ def test_stream_read_validation():
     assert lib.kv8_stream_read(P, n, 0, P2, None) == B.KV8_ERR_SHAPE
     assert lib.kv8_stream_read(P, n, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
     assert lib.kv8_stream_read(MIS, n, 10, P2, None) == B.KV8_ERR_ALIGN
+
+
+def decode_noalloc(**kw):
+    a = dict(q=P, dt=B.KV8_BF16, kc=P, vc=P, ks=P, vs=P, nb=100, bt=P, mbs=16, ctx=P,
+             maxctx=256, b=2, hq=32, hkv=8, d=128, bs=16, scale=0.088, out=P, tps=0,
+             form=B.DECODE_AUTO, stream=None)
+    a.update(kw)
+    return B.load().paged_decode_attn_kv8_noalloc(
+        a["q"], a["dt"], a["kc"], a["vc"], a["ks"], a["vs"], a["nb"], a["bt"], a["mbs"],
+        a["ctx"], a["maxctx"], a["b"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"],
+        a["out"], a["tps"], a["form"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(q=None), B.KV8_ERR_NULL),
+    (dict(ks=None), B.KV8_ERR_NULL),
+    (dict(b=0), B.KV8_ERR_SHAPE),
+    (dict(b=8193), B.KV8_ERR_SHAPE),
+    (dict(hq=24), B.KV8_ERR_UNSUPPORTED),
+    (dict(form=7), B.KV8_ERR_UNSUPPORTED),
+    (dict(tps=100), B.KV8_ERR_UNSUPPORTED),
+    (dict(q=MIS), B.KV8_ERR_ALIGN),
+    # 64 x 64/8 heads at 65536 tokens in 64-token splits: partials far beyond
+    # the fixed scratch, rejected before any HIP call
+    (dict(b=64, hq=64, hkv=8, maxctx=65536, mbs=4096, tps=64, form=B.DECODE_MFMA_ONEPASS),
+     B.KV8_ERR_WORKSPACE),
+])
+def test_noalloc_decode_validation(kw, expected):
+    """The allocation-free decode validates as paged_decode_attn_kv8 does and
+    rejects a call whose partials exceed its fixed scratch, all on the host."""
+    assert decode_noalloc(**kw) == expected
+
+
+def test_noalloc_scratch_covers_the_workloads():
+    """The fixed scratch holds the decode workspace of the Llama-3.1-8B-shaped
+    batch and of the long-context config under every form, and of a
+    Llama-3-70B-shaped layer at the one-pass form's 2048-token splits."""
+    cap = B.NOALLOC_SCRATCH_BYTES
+    assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 0) <= cap
+    assert B.kv8_decode_workspace_size(4, 32, 8, 128, 32768 + 64, 0) <= cap
+    assert B.kv8_decode_workspace_size(64, 64, 8, 128, 16384, 2048) <= cap
