@@ -35,7 +35,8 @@ def parse():
                    help="untimed steps first (the GPU clocks settle over ~100 ms)")
     p.add_argument("--replicas", type=int, default=4)
     p.add_argument("--tokens-per-split", type=int, default=0)
-    p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma", "mfma1"], default="auto",
+    p.add_argument("--decode-kernel", choices=["auto", "dot", "mfma", "mfma1", "sk"],
+                   default="auto",
                    help="form of the INT8/FP8/INT4 decode kernel passed to every decode call "
                         "(auto: the library's choice by group size and size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,7 +124,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     args.form = {"auto": B.DECODE_AUTO, "dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA,
-                 "mfma1": B.DECODE_MFMA_ONEPASS}[args.decode_kernel]
+                 "mfma1": B.DECODE_MFMA_ONEPASS, "sk": B.DECODE_STREAMK}[args.decode_kernel]
     if args.calibrate_copy:
         calibrate_copy(dev)
         return

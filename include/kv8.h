@@ -99,15 +99,24 @@ int kv8_version(void);
  *   KV8_DECODE_AUTO (0): by group size G = Hq / Hkv and size (v_dot2 below
  *     G = 4; at G = 4 two-pass matrix-core for max_context_len <= 8192 with
  *     a grid bound, every sequence at max_context_len in 1024-token splits,
- *     of at most 4096 workgroups, else one-pass; one-pass matrix-core from
- *     G = 8; for the INT4 cache one-pass from G = 4 at d = 128, else v_dot2);
+ *     of at most 4096 workgroups, else stream-K; stream-K from G = 8; for the
+ *     INT4 cache one-pass from G = 4 at d = 128, else v_dot2);
  *   KV8_DECODE_DOT (1): the v_dot2 kernel;
  *   KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of the
  *     split to LDS, then the weighted values; logits and values as 16x16
  *     MFMA tiles over all G heads of a group at once);
  *   KV8_DECODE_MFMA_ONEPASS (3): the one-pass matrix-core kernel (online
  *     softmax over K and V tiles streamed together, weights kept in
- *     registers).
+ *     registers);
+ *   KV8_DECODE_STREAMK (4): the stream-K matrix-core kernel: the
+ *     (sequence, KV head, block) units of the whole batch cut into equal
+ *     contiguous ranges, one per compute unit and within it one per wave,
+ *     each streamed with the one-pass arithmetic; pieces of one (sequence,
+ *     KV head) are merged by log-sum-exp in LDS and, across workgroups,
+ *     through the workspace in the same launch.  tokens_per_split does not
+ *     apply to it (any valid value is accepted), and its output for a
+ *     reordered batch agrees with the reordered output within the
+ *     attention tolerance, not bitwise (the cuts move with the order).
  * The INT4 cache at d = 64 always runs the v_dot2 kernel.  All forms
  * compute the same attention (the same work items and in-launch merge);
  * results agree within the attention tolerance, not bitwise.  The form can
@@ -125,6 +134,7 @@ int kv8_version(void);
 #define KV8_DECODE_DOT 1
 #define KV8_DECODE_MFMA 2
 #define KV8_DECODE_MFMA_ONEPASS 3
+#define KV8_DECODE_STREAMK 4
 
 /* Most (sequence, KV head) pairs, batch * num_kv_heads, of one decode
  * call; more returns KV8_ERR_SHAPE. */

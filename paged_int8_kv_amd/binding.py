@@ -112,8 +112,9 @@ def load():
 
 
 # decode kernel forms (the kernel_form argument of the INT8 / FP8 / INT4
-# decode calls): automatic, v_dot2, two-pass matrix-core, one-pass matrix-core
-DECODE_AUTO, DECODE_DOT, DECODE_MFMA, DECODE_MFMA_ONEPASS = 0, 1, 2, 3
+# decode calls): automatic, v_dot2, two-pass matrix-core, one-pass
+# matrix-core, stream-K matrix-core
+DECODE_AUTO, DECODE_DOT, DECODE_MFMA, DECODE_MFMA_ONEPASS, DECODE_STREAMK = 0, 1, 2, 3, 4
 MAX_DECODE_PAIRS = 65536
 
 

@@ -23,8 +23,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libkv8.so")
 
 ARCH = "gfx950"
 SOURCES = ["kv8_api.cpp", "kv8_append.hip", "kv8_decode.hip", "kv8_decode_mfma.hip",
-           "kv8_prefill.hip",
-           "kvbf16_decode.hip", "kv8_probe.hip"]
+           "kv8_decode_sk.hip", "kv8_prefill.hip", "kvbf16_decode.hip", "kv8_probe.hip"]
 
 # Packed fp32 VALU instructions are kept out of the code object: the
 # compiler's automatic use of them is switched off for every HIP source.
@@ -44,6 +43,7 @@ COMMON_FLAGS = [
 EXTRA_FLAGS = {
     "kv8_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
     "kv8_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "kv8_decode_sk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
 }
 
 

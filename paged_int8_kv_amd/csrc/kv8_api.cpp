@@ -73,7 +73,7 @@ int decode_impl(const void* q, int q_dtype, const int8_t* k_cache,
   if (q_dtype != KV8_F32 && q_dtype != KV8_BF16) return KV8_ERR_UNSUPPORTED;
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads))
     return KV8_ERR_UNSUPPORTED;
-  if (kernel_form < KV8_DECODE_AUTO || kernel_form > KV8_DECODE_MFMA_ONEPASS)
+  if (kernel_form < KV8_DECODE_AUTO || kernel_form > KV8_DECODE_STREAMK)
     return KV8_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(out)) return KV8_ERR_ALIGN;
   if (tokens_per_split > 0 && (tokens_per_split % 64 != 0 || tokens_per_split > 2048))
@@ -215,7 +215,8 @@ size_t kv8_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, i
   if (!supported_dim(head_dim) || !supported_group(num_q_heads, num_kv_heads)) return 0;
   // enough for every kernel form (a call may ask for any of them)
   size_t need = 0;
-  for (int form : {kv8::kDecodeKernelDot, kv8::kDecodeKernelMfma, kv8::kDecodeKernelMfmaOnePass}) {
+  for (int form : {kv8::kDecodeKernelDot, kv8::kDecodeKernelMfma, kv8::kDecodeKernelMfmaOnePass,
+                   kv8::kDecodeKernelStreamK}) {
     kv8::DecodePlan plan;
     if (kv8::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                          tokens_per_split, form, &plan) && plan.total_bytes > need)

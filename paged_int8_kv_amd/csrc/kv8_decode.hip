@@ -518,34 +518,33 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-// Automatic choice (measured on MI355X): from four query heads per KV head
-// up, the dot-product kernel's vector work per cache byte (G/2 v_dot2 issues
-// per lane) outgrows the memory stream and the matrix cores take over.
-// - G = 8: the two-pass form's logits take 50 KB of LDS per workgroup; the
-//   one-pass form keeps none and takes 2048-token splits (136.7 against
-//   159.7 us per layer of the Llama-3-70B-shaped sweep).
+// Automatic choice (measured on MI355X):
+// - below G = 4: the v_dot2 kernel (the vector work per cache byte, G/2
+//   v_dot2 issues per lane, still fits under the memory stream);
 // - G = 4, short contexts (at most 8192 tokens) in a grid of about one
-//   round of workgroups: the two-pass form, whose 84 VGPRs leave room for
-//   five workgroups per CU (37.5 against 39.7 us on the Llama-3.1-8B-shaped
-//   batch: 1024..4096 tokens, 1024 workgroups at most).
-// - G = 4 otherwise: the one-pass form (58.4 against 67.4 us per step on 4
-//   sequences of 32768 tokens; 1513 against 1663 us on 15 sequences of
-//   264192 tokens, about 31000 workgroups).
+//   round of workgroups: the two-pass matrix-core form, whose 84 VGPRs leave
+//   room for five workgroups per CU (37.3 us on the Llama-3.1-8B-shaped
+//   batch, 1024..4096 tokens, against 41.6 us for stream-K and 39.5 us for
+//   the one-pass form);
+// - G = 4 otherwise, and from G = 8: the stream-K form (61.3 against 66.5 us
+//   per step for the one-pass form on 4 sequences of 32768 tokens, 1488
+//   against 1525 us on 15 sequences of 264192 tokens, 125.7 against 139.8 us
+//   per layer of the Llama-3-70B-shaped sweep at G = 8).
 // `grid_bound` is the workgroup count with every sequence at the longest
 // context and 1024-token splits.
 // - INT4 codes: the matrix-core forms serve d = 128 only (the v_dot2
-//   kernel otherwise); from G = 4 the one-pass form (28.5 against 28.8 us
-//   for the two-pass form and 36.5 for v_dot2 on the Llama-3.1-8B-shaped
-//   batch; 1801 against 1971 and 2655 us on 31 sequences of 264192 tokens).
+//   kernel otherwise); from G = 4 the one-pass form (28.9 us on the
+//   Llama-3.1-8B-shaped batch against 34.5 us for stream-K; 1911 against
+//   2081 us on 31 sequences of 264192 tokens).
 int decode_form(int requested, int fmt, int G, long long grid_bound, int max_context_len,
                 int head_dim) {
   if (fmt == kFmtInt4 && head_dim != 128) return kDecodeKernelDot;
   if (requested != kDecodeKernelAuto) return requested;
   if (fmt == kFmtInt4) return G >= 4 ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
-  if (G >= 8) return kDecodeKernelMfmaOnePass;
+  if (G >= 8) return kDecodeKernelStreamK;
   if (G >= 4)
     return grid_bound <= 4096 && max_context_len <= 8192 ? kDecodeKernelMfma
-                                                         : kDecodeKernelMfmaOnePass;
+                                                         : kDecodeKernelStreamK;
   return kDecodeKernelDot;
 }
 
@@ -557,6 +556,23 @@ bool plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim,
   const int G = num_q_heads / num_kv_heads;
   // LDS of one workgroup at a split size: the one-pass kernel's does not
   // grow with the split
+  if (form == kDecodeKernelStreamK) {
+    // units are counted in 32 bits: at most batch * Hkv * ceil(max_context_len / 16)
+    if ((int64_t)batch * num_kv_heads * (((int64_t)max_context_len + 15) / 16) > 0x7FFFFFFF)
+      return false;
+    if (tokens_per_split < 0 || tokens_per_split > 2048 || tokens_per_split % 64 != 0)
+      return false;
+    plan->form = form;
+    plan->split_tokens = 0;
+    plan->n_split = 1;
+    plan->counter_bytes = kCounterBytes;
+    plan->o_bytes = align256((size_t)kSkMaxWorkgroups * 2 *
+                             ((size_t)num_q_heads / num_kv_heads * head_dim +
+                              2 * (size_t)(num_q_heads / num_kv_heads)) * sizeof(float));
+    plan->lse_bytes = 0;
+    plan->total_bytes = plan->counter_bytes + plan->o_bytes;
+    return true;
+  }
   auto smem = [&](int tps) {
     if (form == kDecodeKernelMfmaOnePass) return 0;
     if (form == kDecodeKernelMfma) return decode_mfma2_smem(tps, G, head_dim);
@@ -627,7 +643,10 @@ int launch_decode(const void* q, bool q_f32, const int8_t* k_cache, const int8_t
   a.qk_scale_log2 = sm_scale * kLog2e;
   const int G = num_q_heads / num_kv_heads;
   bool ok;
-  if (plan.form != kDecodeKernelDot) {
+  if (plan.form == kDecodeKernelStreamK) {
+    a.period = decode_sk_workgroups();
+    ok = launch_decode_sk(a, head_dim, G, q_f32, fmt, stream);
+  } else if (plan.form != kDecodeKernelDot) {
     ok = launch_decode_mfma(a, head_dim, G, q_f32, fmt, plan.form == kDecodeKernelMfmaOnePass,
                             stream);
   } else if (fmt == kFmtFp8) ok = dispatch_fmt<CodesFp8>(head_dim, q_f32, G, a, batch, stream);

@@ -166,6 +166,10 @@ __device__ __forceinline__ void append_newest(const SplitArgs& a, int b, int g, 
 // they do not serve.  decode_mfma2_smem: LDS bytes of a two-pass workgroup.
 bool launch_decode_mfma(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
                         bool one_pass, hipStream_t stream);
+// Stream-K form (kv8_decode_sk.hip): a.period workgroups, a.o_part the
+// per-workgroup partial states.
+bool launch_decode_sk(const SplitArgs& a, int head_dim, int G, bool q_f32, int fmt,
+                      hipStream_t stream);
 int decode_mfma2_smem(int split_tokens, int G, int head_dim);
 
 struct Item {

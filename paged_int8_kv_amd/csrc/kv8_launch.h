@@ -35,8 +35,16 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 // 1024-token splits), longest context and head dim takes when `requested`
 // is asked for.
 enum : int {
-  kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3
+  kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3,
+  kDecodeKernelStreamK = 4
 };
+
+// The stream-K form launches one workgroup per compute unit (at most
+// kSkMaxWorkgroups); its workspace holds two partial states per workgroup
+// after the counters.  decode_sk_workgroups: the workgroups of a launch on
+// the current device.
+constexpr int kSkMaxWorkgroups = 1024;
+int decode_sk_workgroups();
 int decode_form(int requested, int fmt, int G, long long grid_bound, int max_context_len,
                 int head_dim);
 

@@ -101,7 +101,7 @@ def decode(fn="paged_decode_attn_kv8", **kw):
     (dict(ws=None), B.KV8_ERR_WORKSPACE),
     (dict(wsb=16), B.KV8_ERR_WORKSPACE),
     (dict(form=-1), B.KV8_ERR_UNSUPPORTED),
-    (dict(form=4), B.KV8_ERR_UNSUPPORTED),
+    (dict(form=5), B.KV8_ERR_UNSUPPORTED),
     (dict(b=8193), B.KV8_ERR_SHAPE),            # batch * Hkv above KV8_DECODE_MAX_PAIRS
     (dict(b=8192, ws=None), B.KV8_ERR_WORKSPACE),   # exactly at the limit: accepted
 ])
@@ -110,14 +110,14 @@ def test_decode_validation(kw, expected):
 
 
 @pytest.mark.parametrize("form", [B.DECODE_AUTO, B.DECODE_DOT, B.DECODE_MFMA,
-                                  B.DECODE_MFMA_ONEPASS])
+                                  B.DECODE_MFMA_ONEPASS, B.DECODE_STREAMK])
 @pytest.mark.parametrize("fn", ["paged_decode_attn_kv8", "paged_decode_attn_fp8kv",
                                 "paged_decode_attn_int4kv"])
 def test_decode_kernel_form_argument_accepted(fn, form):
     """Every kernel form passes validation (the call then stops at the
     missing workspace, before any HIP call)."""
     assert decode(fn=fn, form=form, ws=None) == B.KV8_ERR_WORKSPACE
-    assert decode(fn=fn, form=form + 4) == B.KV8_ERR_UNSUPPORTED
+    assert decode(fn=fn, form=form + 5) == B.KV8_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("form,tps,expected", [
@@ -137,7 +137,9 @@ def test_decode_workspace_counter_region_fixed():
     plus its partial arrays, and the limit on pairs is enforced."""
     assert B.MAX_DECODE_PAIRS == 65536
     one = B.kv8_decode_workspace_size(1, 4, 1, 64, 64, 64)
-    assert one == 4 * 65536 + 1024 + 256     # counters + o (4 heads x 64 fp32) + lse, 256-aligned
+    split_forms = 1024 + 256                 # o (4 heads x 64 fp32) + lse, 256-aligned
+    stream_k = 1024 * 2 * (4 * 64 + 2 * 4) * 4   # two states per workgroup, 1024 at most
+    assert one == 4 * 65536 + max(split_forms, stream_k)
     assert B.kv8_decode_workspace_size(8193, 8, 8, 128, 64, 0) == 0
     assert B.kv8_decode_workspace_size(8192, 8, 8, 128, 64, 0) > 0
 
@@ -184,8 +186,10 @@ def test_decode_workspace_size():
     ws = B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 512)
     n_split = 8
     counters = 4 * B.MAX_DECODE_PAIRS                # fixed counter region
-    assert ws >= counters + 32 * 32 * n_split * (128 + 1) * 4
-    assert ws < counters + 32 * 32 * n_split * (128 + 1) * 4 + 512
+    split_forms = 32 * 32 * n_split * (128 + 1) * 4  # partial outputs and log-sum-exps
+    stream_k = 1024 * 2 * (4 * 128 + 2 * 4) * 4      # two states per workgroup, 1024 at most
+    assert ws >= counters + max(split_forms, stream_k)
+    assert ws < counters + max(split_forms, stream_k) + 512
     assert B.kv8_decode_workspace_size(32, 32, 8, 128, 4096, 0) > 0
     assert B.kv8_decode_workspace_size(32, 30, 8, 128, 4096, 0) == 0
     assert B.kv8_decode_workspace_size(32, 32, 8, 96, 4096, 0) == 0

@@ -3,7 +3,7 @@ side of the rule, a launch under KV8_DECODE_AUTO must be bitwise the launch
 of the form the rule names:
 - v_dot2 below 4 query heads per KV head;
 - two-pass matrix-core at 4 for short contexts in a small grid;
-- one-pass matrix-core for long contexts and from 8 heads per KV head;
+- stream-K matrix-core for long contexts and from 8 heads per KV head;
 - INT4: one-pass matrix-core from 4 heads per KV head at d = 128, v_dot2 at
   d = 64.
 The named form must also differ from the other forms on that input, so that
@@ -20,7 +20,8 @@ from tests.test_gpu_int4kv import gpu_decode_int4, oracle_cache_int4, upload_int
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
-FORMS = {"dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA, "mfma1": B.DECODE_MFMA_ONEPASS}
+FORMS = {"dot": B.DECODE_DOT, "mfma": B.DECODE_MFMA, "mfma1": B.DECODE_MFMA_ONEPASS,
+         "sk": B.DECODE_STREAMK}
 
 
 def run_forms(run):
@@ -31,8 +32,8 @@ def run_forms(run):
 @pytest.mark.parametrize("hq,hkv,lens,expected", [
     (16, 8, [300, 700, 41], "dot"),              # G = 2
     (32, 8, [1500, 3000, 17, 999], "mfma"),      # G = 4, short contexts, small grid
-    (32, 8, [9000, 100], "mfma1"),               # G = 4, a context past 8192 tokens
-    (64, 8, [500, 2000, 1], "mfma1"),            # G = 8
+    (32, 8, [9000, 100], "sk"),                  # G = 4, a context past 8192 tokens
+    (64, 8, [500, 2000, 1], "sk"),               # G = 8
 ])
 def test_auto_form_int8(hq, hkv, lens, expected):
     case = W.make_paged_case(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
@@ -74,5 +75,5 @@ def test_int4_head_dim_64_takes_dot():
     host = oracle_cache_int4(case)
     cache = upload_int4(*host)
     outs = run_forms(lambda f: gpu_decode_int4(case, cache, kernel_form=f))
-    for name in ("auto", "mfma", "mfma1"):
+    for name in ("auto", "mfma", "mfma1", "sk"):
         assert np.array_equal(outs[name], outs["dot"]), name

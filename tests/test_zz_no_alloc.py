@@ -54,9 +54,12 @@ def test_noalloc_refuses_beyond_scratch():
     cache = upload_cache(*oracle_cache(case))
     qt = q_tensor(case)
     out = torch.zeros((2, 32, 128), dtype=torch.float32, device=dev())
-    # a host bound of 1M tokens in 64-token splits sizes partials beyond the scratch
+    # a host bound of 1M tokens in 64-token splits of the one-pass form sizes
+    # its partials beyond the scratch (the stream-K form's partials do not
+    # grow with the context, so the form is named)
     with pytest.raises(B.Kv8Error) as e:
         B.paged_decode_attn_kv8_noalloc(
             qt, *cache, torch.from_numpy(case.block_table).to(dev()),
-            torch.from_numpy(case.context_lens).to(dev()), 1 << 20, out, tokens_per_split=64)
+            torch.from_numpy(case.context_lens).to(dev()), 1 << 20, out, tokens_per_split=64,
+            kernel_form=B.DECODE_MFMA_ONEPASS)
     assert e.value.status == B.KV8_ERR_WORKSPACE
