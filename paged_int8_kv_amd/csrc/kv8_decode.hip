@@ -28,8 +28,9 @@
 //
 // Dot products use v_dot2_f32_f16 on fp16 pairs.  An INT8 code c enters as
 // the fp16 value c + 1152 built by one byte permute (see kv8_device.h); the
-// bias is removed once per token (pass 1: the sums start at minus 1152 *
-// sum q_h) and once per output (pass 2: 1152 * sum w).  The same kernel
+// bias is removed once per token in pass 1 (the sums start at minus 1152 *
+// sum q_h) and from each V code pair in pass 2 (one packed fp16 subtract,
+// exact).  The same kernel
 // serves the FP8 (e4m3) cache ("KV Cache 优化全景解析", section 7.4), whose
 // codes become exact fp16 pairs by one hardware convert and carry no bias.
 // q enters as fp16 after an exact
@@ -120,7 +121,7 @@ __host__ __device__ inline SmemLayout smem_layout(int split_tokens, int G, int D
   L.vs_off = L.z_off + align16(zbytes > finbytes ? zbytes : finbytes);
   L.pp_off = L.vs_off + align16(split_tokens * 2);
   L.red_off = L.pp_off + align16((split_tokens / 2) * G * 4);
-  L.flag_off = L.red_off + align16(3 * kWaves * G * 4);
+  L.flag_off = L.red_off + align16(2 * kWaves * G * 4);
   L.total = L.flag_off + 16;
   return L;
 }
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
   float* s_fin = s_z;
   uint16_t* s_vs = reinterpret_cast<uint16_t*>(smem + L.vs_off);
   uint32_t* s_pp = reinterpret_cast<uint32_t*>(smem + L.pp_off);
-  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [2][kWaves][G]
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           qsum += (float)l0 + (float)l1;
         }
       }
-      cz[h] = ldexpf(a.qk_scale_log2, e);
-      nqb[h] = -C::kBias * qsum;
+      cz[h] = ldexpf(a.qk_scale_log2, e) * (1.0f / C::kLogitStep);
+      nqb[h] = -C::kLogitBias * qsum;
     }
   }
   // per-lane constants of the logits this lane stores after the reduction
@@ -299,18 +300,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const int i = base + s;
         if (i < nmine) {
           const Row w0 = r0[s], w1 = r1[s];
-          // the sums start at minus the code bias of the lane's channels, so
-          // the 8-lane reduction yields the unbiased dot products
+          // the sums start at minus the codes' logit bias times the lane's
+          // q, so the 8-lane reduction yields the unbiased dot products
           float S[2 * G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) S[h] = S[G + h] = C::kBiased ? nqb[h] : 0.0f;
+          for (int h = 0; h < G; ++h) S[h] = S[G + h] = nqb[h];
           if constexpr (NIB) {
 #pragma unroll
             for (int k = 0; k < NDC; ++k) {
               const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const half2_t a0 = C::nib_pair(x0, j), a1 = C::nib_pair(x1, j);
+                const half2_t a0 = C::logit_pair(x0, j), a1 = C::logit_pair(x1, j);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                   S[h] = fdot2(qh[h][4 * k + j], a0, S[h]);
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
     float Mh = s_red[h];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_red[w * G + h]);
-    float lsum = 0.0f, psum = 0.0f;
+    float lsum = 0.0f;
     _Float16* pph = reinterpret_cast<_Float16*>(s_pp);
     const int total = nblk * kBlock * G;
     for (int e = tid; e < total; e += kThreads) {
@@ -401,20 +402,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         const float p = __builtin_amdgcn_exp2f(z - Mh);
         p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
         lsum += p;
-        if constexpr (C::kBiased && !NIB) psum += (float)p16;
       }
       const int jj = t / kBlock, r = t % kBlock;
       pph[((jj * 8 + (r & 7)) * G + h) * 2 + (r >> 3)] = p16;
     }
 #pragma unroll
-    for (int off = G; off < 64; off <<= 1) {
-      lsum += __shfl_xor(lsum, off);
-      psum += __shfl_xor(psum, off);
-    }
-    if (lane < G) {
-      s_red[kWaves * G + wave * G + lane] = lsum;
-      s_red[2 * kWaves * G + wave * G + lane] = psum;
-    }
+    for (int off = G; off < 64; off <<= 1) lsum += __shfl_xor(lsum, off);
+    if (lane < G) s_red[kWaves * G + wave * G + lane] = lsum;
   }
   __syncthreads();
 
@@ -444,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
             const uint32_t hi = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              // unbiased exactly here (4-bit codes: biased sums over a long
-              // split would cancel away too many bits)
+              // unbiased exactly here: biased sums over a long split would
+              // cancel away too many bits
               const half2_t fl = C::exact(C::nib_pair(lo, j)), fh = C::exact(C::nib_pair(hi, j));
 #pragma unroll
               for (int h = 0; h < G; ++h) {
@@ -459,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
         for (int k = 0; k < NDW; ++k) {
           const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
           const uint32_t i01 = interleave_lo(x0, x1), i23 = interleave_hi(x0, x1);
-          const half2_t f0 = C::lo(i01), f1 = C::hi(i01);
-          const half2_t f2 = C::lo(i23), f3 = C::hi(i23);
+          const half2_t f0 = C::exact(C::lo(i01)), f1 = C::exact(C::hi(i01));
+          const half2_t f2 = C::exact(C::lo(i23)), f3 = C::exact(C::hi(i23));
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             acc[h * CPL + 4 * k] = fdot2(wp[h], f0, acc[h * CPL + 4 * k]);
@@ -477,9 +471,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 
   groups_to_lds<G, CPL, D>(acc, s_fin, wave, lane, chunk);
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, C::kBiased && !NIB>(
+  finish_split<G, D, kThreads, kWaves>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
 template <int D, int G, bool QF32, class C>

@@ -319,29 +319,25 @@ struct PartialArgs {
 
 // Finish one split of (sequence, KV head) bg whose query heads start at bh0:
 // combine the kWaves per-wave results (s_fin [kWaves][G][D]; s_red holds per
-// wave and head the max, the weight sum and, for BIASED codes, the sum of
-// the fp16 weights: bias times that sum is subtracted), then write the output
-// (a single split) or the split's partial; the last workgroup of bg to
-// finish merges the partials of all nvalid splits by log-sum-exp.
-template <int G, int D, int kThreads, int kWaves, bool BIASED>
+// wave and head the max, then the weight sum), then write the output (a
+// single split) or the split's partial; the last workgroup of bg to finish
+// merges the partials of all nvalid splits by log-sum-exp.
+template <int G, int D, int kThreads, int kWaves>
 __device__ __forceinline__ void finish_split(const PartialArgs& a, const float* s_fin,
                                              const float* s_red, int* s_flag, int64_t bh0,
-                                             int64_t bg, int split, int nvalid, int tid,
-                                             float bias) {
+                                             int64_t bg, int split, int nvalid, int tid) {
   // ---- normalise; write the output or this split's partial ----------------
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, c = e % D;
     float s = s_fin[h * D + c];
     float Mh = s_red[h], Lh = s_red[kWaves * G + h];
-    float Ph = BIASED ? s_red[2 * kWaves * G + h] : 0.0f;
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
       s += s_fin[(w * G + h) * D + c];
       Mh = fmaxf(Mh, s_red[w * G + h]);
       Lh += s_red[kWaves * G + w * G + h];
-      if constexpr (BIASED) Ph += s_red[2 * kWaves * G + w * G + h];
     }
-    const float o = (s - (BIASED ? bias * Ph : 0.0f)) / Lh;
+    const float o = s / Lh;
     if (nvalid == 1) {
       a.out[(bh0 + h) * D + c] = o;
     } else {

@@ -45,10 +45,11 @@
 //
 // INT8 codes enter as the biased fp16 values c + 1152 (one byte permute per
 // pair, kv8_device.h); the bias is removed from the logits by starting the
-// accumulator at minus 1152 * sum(q_h) and from the outputs by 1152 * the sum
-// of the fp16 weights.  FP8 codes become exact fp16 by one hardware convert
-// per pair.  INT4 codes (one-pass kernel) enter as c + 1032: a flip of each
-// nibble's sign bit and one and-or with the fp16 pattern per nibble pair.  q
+// accumulator at minus 1152 * sum(q_h), and from the V codes themselves, one
+// packed fp16 subtract per pair, before they meet the weights.  FP8 codes
+// become exact fp16 by one hardware convert per pair.  INT4 codes (one-pass
+// kernel) enter as c + 1032: a flip of each nibble's sign bit and one and-or
+// with the fp16 pattern per nibble pair, unbiased like INT8's V codes.  q
 // enters as fp16 after an exact per-head power-of-two rescale; an fp32 q is
 // split into a high and a low fp16 part (two MFMAs).
 #include "kv8_decode_common.h"
@@ -84,7 +85,7 @@ __host__ __device__ inline M2Smem m2smem_layout(int split_tokens, int G, int D) 
   L.vs_off = L.z_off + align16m(zbytes > finbytes ? zbytes : finbytes);
   L.w_off = L.vs_off + align16m(split_tokens * 2);
   L.red_off = L.w_off + align16m(split_tokens * G * 2);
-  L.flag_off = L.red_off + align16m(3 * kWaves * G * 4);
+  L.flag_off = L.red_off + align16m(2 * kWaves * G * 4);
   L.total = L.flag_off + 16;
   return L;
 }
@@ -99,7 +100,7 @@ __host__ __device__ inline MSmem msmem_layout(int G, int D) {
   MSmem L{};
   L.fin_off = 0;
   L.red_off = align16m(kWaves * G * D * 4);
-  L.flag_off = L.red_off + align16m(3 * kWaves * G * 4);
+  L.flag_off = L.red_off + align16m(2 * kWaves * G * 4);
   L.total = L.flag_off + 16;
   return L;
 }
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
   float* s_fin = s_z;
   uint16_t* s_vs = reinterpret_cast<uint16_t*>(smem + L.vs_off);
   _Float16* s_w = reinterpret_cast<_Float16*>(smem + L.w_off);
-  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [2][kWaves][G]
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
     float Mh = s_red[h];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) Mh = fmaxf(Mh, s_red[w * G + h]);
-    float lsum = 0.0f, psum = 0.0f;
+    float lsum = 0.0f;
     const int total = nblk * kBlock * G;
     for (int e = tid; e < total; e += kThreads) {
       const int t = e / G;
@@ -267,20 +268,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
         const float p = __builtin_amdgcn_exp2f(z - Mh);
         p16 = (_Float16)(p * fp16_bits_to_f32(s_vs[t]));
         lsum += p;
-        if constexpr (value_bias_kept<C>()) psum += (float)p16;
       }
       const int jj = t / kBlock, r = t % kBlock;
       s_w[(jj * G + h) * kBlock + r] = p16;
     }
 #pragma unroll
-    for (int off = G; off < 64; off <<= 1) {
-      lsum += __shfl_xor(lsum, off);
-      psum += __shfl_xor(psum, off);
-    }
-    if (lane < G) {
-      s_red[kWaves * G + wave * G + lane] = lsum;
-      s_red[2 * kWaves * G + wave * G + lane] = psum;
-    }
+    for (int off = G; off < 64; off <<= 1) lsum += __shfl_xor(lsum, off);
+    if (lane < G) s_red[kWaves * G + wave * G + lane] = lsum;
   }
   __syncthreads();
 
@@ -315,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
     }
   }
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, value_bias_kept<C>()>(
+  finish_split<G, D, kThreads, kWaves>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
 template <int D, int G, bool QF32, class C>
@@ -336,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const MSmem L = msmem_layout(G, D);
   float* s_fin = reinterpret_cast<float*>(smem + L.fin_off);   // [kWaves][G][D]
-  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [2][kWaves][G]
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -415,9 +409,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
 
   // ---- one pass: logits, online softmax, weighted values ---------------------
   // Lane l holds, for head hl, the running max m (the same in the four lanes
-  // of the head), its partial weight sum l and fp16-weight sum ps over its
-  // tokens, and O[hl][channel (D/16)(4 q4 + r) + j] in acc[j][r].
-  float m_run = kNegInf, l_run = 0.0f, p_run = 0.0f;
+  // of the head), its partial weight sum l over its tokens, and
+  // O[hl][channel (D/16)(4 q4 + r) + j] in acc[j][r].
+  float m_run = kNegInf, l_run = 0.0f;
   float4_t acc[NVT];
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -452,7 +446,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           const float f = bm > m_run ? __builtin_amdgcn_exp2f(m_run - bm) : 1.0f;
           m_run = fmaxf(m_run, bm);
           l_run *= f;
-          p_run *= f;
 #pragma unroll
           for (int j = 0; j < NVT; ++j) acc[j] *= f;
         }
@@ -463,7 +456,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           const float vs = fp16_bits_to_f32((uint16_t)(vw[r / 2] >> (16 * (r % 2))));
           w[r] = (_Float16)(tb + r < ntok ? p * vs : 0.0f);   // never reads a stale scale
           l_run += p;
-          if constexpr (value_bias_kept<C>()) p_run += (float)w[r];
         }
         const half4_t wb = {w[0], w[1], w[2], w[3]};
         value_mfmas<C, NVT>(rv[s], wb, acc);
@@ -481,15 +473,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_red[w * G + (hl < G ? hl : 0)]);
     // a wave without blocks holds m = -inf and nothing else: factor 0
     const float f = m_run == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-    float lw = l_run * f, pw = p_run * f;
+    float lw = l_run * f;
     lw += __shfl_xor(lw, 16);
     lw += __shfl_xor(lw, 32);
-    pw += __shfl_xor(pw, 16);
-    pw += __shfl_xor(pw, 32);
-    if (lane < G) {
-      s_red[kWaves * G + wave * G + lane] = lw;
-      s_red[2 * kWaves * G + wave * G + lane] = pw;
-    }
+    if (lane < G) s_red[kWaves * G + wave * G + lane] = lw;
     if (hl < G) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -500,9 +487,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
     }
   }
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, value_bias_kept<C>()>(
+  finish_split<G, D, kThreads, kWaves>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, C::kBias);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
 template <int D, int G, bool QF32, class C, bool ONEPASS>

@@ -135,7 +135,7 @@ __device__ __forceinline__ int wg_of(int64_t u, int64_t T, int nw) {
 
 template <int G, int D>
 struct SkLds {
-  float acc[kSkWaves][2][G * D];   // piece sums relative to the piece max, bias removed
+  float acc[kSkWaves][2][G * D];   // piece sums relative to the piece max
   float m[kSkWaves][2][G];         // piece max (log2 domain)
   float l[kSkWaves][2][G];         // piece weight sum
   int meta[kSkWaves][2][4];        // pair (-1: empty), flags (1: first block, 2: last), P0, nb
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
   // ---- stream the wave's units ----------------------------------------------
   half8_t qb[NKM], qlo[QF32 ? NKM : 1];
   float cz = 0.0f, nqb = 0.0f;
-  float m_run = kNegInf, l_run = 0.0f, p_run = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f;
   float4_t acc[NVT];
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -206,12 +206,9 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
   // piece of a pair goes to the wave's LDS slot (0: its first piece, 1: its
   // last one; only those can be cut).
   auto flush = [&]() {
-    float lw = l_run, pw = p_run;
+    float lw = l_run;
     lw += __shfl_xor(lw, 16);
     lw += __shfl_xor(lw, 32);
-    pw += __shfl_xor(pw, 16);
-    pw += __shfl_xor(pw, 32);
-    const float bias = value_bias_kept<C>() ? C::kBias * pw : 0.0f;
     const int64_t bh0 = (int64_t)cur_b * Hq + (int64_t)cur_g * G;
     if (seg_flags == 3) {
       if (hl < G) {
@@ -220,7 +217,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
         for (int r = 0; r < 4; ++r) {
           float* dst = a.out + (bh0 + hl) * D + NVT * (4 * q4 + r);
 #pragma unroll
-          for (int j = 0; j < NVT; ++j) dst[j] = (acc[j][r] - bias) * inv;
+          for (int j = 0; j < NVT; ++j) dst[j] = acc[j][r] * inv;
         }
       }
     } else {
@@ -230,7 +227,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
         for (int r = 0; r < 4; ++r) {
           float* dst = &lds.acc[wave][s][hl * D + NVT * (4 * q4 + r)];
 #pragma unroll
-          for (int j = 0; j < NVT; ++j) dst[j] = acc[j][r] - bias;
+          for (int j = 0; j < NVT; ++j) dst[j] = acc[j][r];
         }
         if (q4 == 0) {
           lds.m[wave][s][hl] = m_run;
@@ -328,7 +325,6 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             seg_nb = nbp;
             m_run = kNegInf;
             l_run = 0.0f;
-            p_run = 0.0f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             q_operands<D, G, QF32, C>(a, (int64_t)b * Hq + (int64_t)g * G, hl, q4, qb, qlo, cz, nqb);
@@ -346,7 +342,8 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
           float z[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float ks = fp16_bits_to_f32((uint16_t)((r < 2 ? ksc[sl].x : ksc[sl].y) >> (16 * (r % 2))));
+            const uint32_t kw = r < 2 ? ksc[sl].x : ksc[sl].y;
+            const float ks = fp16_bits_to_f32((uint16_t)(kw >> (16 * (r % 2))));
             z[r] = 4 * q4 + r < nt ? (ks * cz) * S[r] : kNegInf;
           }
           float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -355,7 +352,6 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             const float f = bm > m_run ? __builtin_amdgcn_exp2f(m_run - bm) : 1.0f;
             m_run = fmaxf(m_run, bm);
             l_run *= f;
-            p_run *= f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] *= f;
           }
@@ -363,10 +359,10 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = __builtin_amdgcn_exp2f(z[r] - m_run);   // 0 for masked tokens
-            const float vs = fp16_bits_to_f32((uint16_t)((r < 2 ? vsc[sl].x : vsc[sl].y) >> (16 * (r % 2))));
+            const uint32_t vw = r < 2 ? vsc[sl].x : vsc[sl].y;
+            const float vs = fp16_bits_to_f32((uint16_t)(vw >> (16 * (r % 2))));
             wv[r] = (_Float16)(4 * q4 + r < nt ? p * vs : 0.0f);     // never a stale scale
             l_run += p;
-            if constexpr (value_bias_kept<C>()) p_run += (float)wv[r];
           }
           issue_k(sl, i + kSkPf);
           const half4_t wb = {wv[0], wv[1], wv[2], wv[3]};

@@ -134,9 +134,14 @@ __device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
 //   CodesInt8  symmetric INT8, codes -127..127 (the KV8 method);
 //   CodesFp8   OCP e4m3 ("KV Cache 优化全景解析", section 7.4), largest 448.
 // pre() + lo()/hi() turn a dword of 4 codes into two fp16 pairs (bytes 0,1
-// and 2,3).  For INT8 the pairs carry the +1152 bias described above
-// (kBiased); exact() removes it.  e4m3 values are all exact in fp16, so the
-// FP8 pairs come from one hardware convert each and need no bias.
+// and 2,3).  For INT8 the pairs carry the +1152 bias described above;
+// exact() removes it.  e4m3 values are all exact in fp16, so the FP8 pairs
+// come from one hardware convert each and need no bias (exact() is the
+// identity).  The decode kernels feed K codes to the logit products as the
+// values kLogitBias + kLogitStep * c and start each sum at minus kLogitBias
+// * sum(q); the logit scale absorbs 1 / kLogitStep (a power of two).  The
+// cancellation this leaves costs an INT8 logit about 3e-5 (log2 units) at
+// most.
 // code() quantises one value: the fp32 quotient x / s (IEEE division), then
 // INT8: round half to even and clamp to +-127; FP8: round to nearest even
 // on the e4m3 grid and saturate to +-448, the sign of a zero kept.
@@ -144,8 +149,9 @@ __device__ __forceinline__ float fdot2(half2_t a, half2_t b, float c) {
 struct CodesInt8 {
   static constexpr int kBits = 8;
   static constexpr bool kIntCodes = true;   // code = clamp(rint(quotient))
-  static constexpr bool kBiased = true;
   static constexpr float kBias = kCodeBias;
+  static constexpr float kLogitBias = kCodeBias;
+  static constexpr float kLogitStep = 1.0f;
   static constexpr float kQmax = 127.0f;
   __device__ static uint32_t pre(uint32_t u) { return u ^ kXor80; }
   __device__ static half2_t lo(uint32_t x) { return biased_pair_lo(x); }
@@ -167,8 +173,9 @@ struct CodesInt8 {
 struct CodesFp8 {
   static constexpr int kBits = 8;
   static constexpr bool kIntCodes = false;
-  static constexpr bool kBiased = false;
   static constexpr float kBias = 0.0f;
+  static constexpr float kLogitBias = 0.0f;
+  static constexpr float kLogitStep = 1.0f;
   static constexpr float kQmax = 448.0f;
   __device__ static uint32_t pre(uint32_t u) { return u; }
   __device__ static half2_t lo(uint32_t x) {
@@ -200,16 +207,26 @@ struct CodesFp8 {
 // i.  A dword holds 8 codes.  Flipping each nibble's sign bit (xor 0x8)
 // gives u = c + 8, and u under the fp16 pattern 0x6400 is the value
 // 1024 + u = c + 1032 exactly.  nib_pair(x, j) makes the fp16 pair of
-// nibbles j and j + 4 of the (already flipped) dword x.
+// nibbles j and j + 4 of the (already flipped) dword x.  logit_pair(x, j)
+// makes the same pair with u in the top four mantissa bits under 0x3C00,
+// the value 1 + u / 16 = 1.5 + c / 16 exactly, for the logit products: a
+// bias of 24 code steps in place of 1032 (summed against q of up to 2^15,
+// the 1032 bias cost the logits enough to put 6e-4 relative error into the
+// output at 264K tokens), at the same two operations per pair.
 struct CodesInt4 {
   static constexpr int kBits = 4;
   static constexpr bool kIntCodes = true;
-  static constexpr bool kBiased = true;
   static constexpr float kBias = 1032.0f;
+  static constexpr float kLogitBias = 1.5f;
+  static constexpr float kLogitStep = 0.0625f;
   static constexpr float kQmax = 7.0f;
   __device__ static uint32_t pre(uint32_t u) { return u ^ 0x88888888u; }
   __device__ static half2_t nib_pair(uint32_t x, int j) {
     return __builtin_bit_cast(half2_t, ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
+  }
+  __device__ static half2_t logit_pair(uint32_t x, int j) {
+    const uint32_t y = j < 2 ? x << (6 - 4 * j) : x >> (4 * j - 6);
+    return __builtin_bit_cast(half2_t, (y & 0x03C003C0u) | 0x3C003C00u);
   }
   __device__ static half2_t exact(half2_t p) {
     const half2_t bias = {(_Float16)kBias, (_Float16)kBias};

@@ -52,8 +52,8 @@ __device__ __forceinline__ uint32_t dw(const uint32_t& r, int) { return r; }
 // 7) in the order the nibble pairs come out, in fp16
 // after the head's power-of-two rescale (bf16 q is exact then; an fp32 q
 // also gets its fp16 remainder in qlo).  cz = log2(e) * sm_scale undoing the
-// rescale; nqb = minus the code bias times the head's fp16 q sum (the
-// logit accumulators start there).
+// rescale and the K codes' value step; nqb = minus the K codes' logit bias
+// times the head's fp16 q sum (the logit accumulators start there).
 template <int D, int G, bool QF32, class C>
 __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int hl, int q4,
                                            half8_t (&qb)[D / 32],
@@ -117,8 +117,8 @@ __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int 
   }
   qsum += __shfl_xor(qsum, 16);
   qsum += __shfl_xor(qsum, 32);
-  cz = ldexpf(a.qk_scale_log2, e);
-  nqb = -C::kBias * qsum;
+  cz = ldexpf(a.qk_scale_log2, e) * (1.0f / C::kLogitStep);
+  nqb = -C::kLogitBias * qsum;
 }
 
 // The logit MFMA's A operand j of a block: the lane's 8 channels of MFMA j
@@ -129,7 +129,8 @@ template <class C, int NCH>
 __device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) {
   if constexpr (C::kBits == 4) {
     const uint32_t x = C::pre(dw(rk[0], j));
-    return cat8(C::nib_pair(x, 0), C::nib_pair(x, 1), C::nib_pair(x, 2), C::nib_pair(x, 3));
+    return cat8(C::logit_pair(x, 0), C::logit_pair(x, 1), C::logit_pair(x, 2),
+                C::logit_pair(x, 3));
   } else {
     const uint4 r = rk[j / 2];
     const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
@@ -139,16 +140,15 @@ __device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) 
 
 // The value MFMAs of a block: acc[j] += A_j . wb with A_j the codes of
 // channel (D/16) hl + j for the 4 tokens whose rows the lane holds.  Byte
-// codes: one interleave per token pair and dword, then byte pairs, biased
-// (INT8: c + 1152; the split removes 1152 * sum(w) at its end).  4-bit codes
-// (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
+// codes: one interleave per token pair and dword, then byte pairs.  4-bit
+// codes (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
 // permute joins two tokens' low (high) halves, whose nibble pairs are then
-// (token t, token t+1) of channel j (4 + j); their bias is taken off here,
-// exactly, by one packed fp16 subtract per pair, because with codes of at
-// most 7 the biased sums over a long split would cancel away too many bits
-// (measured at 264K tokens: relative error 1.5e-3 with the bias kept).
-template <class C>
-constexpr bool value_bias_kept() { return C::kBiased && C::kBits == 8; }
+// (token t, token t+1) of channel j (4 + j).  Biased integer codes (INT8
+// c + 1152, INT4 c + 1032) are unbiased here, exactly, by one packed fp16
+// subtract per pair: summing biased codes over a long split and taking
+// bias * sum(w) off at its end cancels away too many bits (measured at 264K
+// tokens: INT4 relative error 1.5e-3, INT8 7.3e-4 against 2.1e-4 unbiased,
+// the rest being the fp16 rounding of the weights).
 
 template <class C, int NVT, class VRow>
 __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
@@ -176,10 +176,10 @@ __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
       const uint32_t x2 = C::pre(dw(rv[2], k)), x3 = C::pre(dw(rv[3], k));
       const uint32_t l01 = interleave_lo(x0, x1), h01 = interleave_hi(x0, x1);
       const uint32_t l23 = interleave_lo(x2, x3), h23 = interleave_hi(x2, x3);
-      const half4_t t0 = cat4(C::lo(l01), C::lo(l23));   // byte 4k   of tokens 0..3
-      const half4_t t1 = cat4(C::hi(l01), C::hi(l23));   // byte 4k+1
-      const half4_t t2 = cat4(C::lo(h01), C::lo(h23));   // byte 4k+2
-      const half4_t t3 = cat4(C::hi(h01), C::hi(h23));   // byte 4k+3
+      const half4_t t0 = cat4(C::exact(C::lo(l01)), C::exact(C::lo(l23)));   // byte 4k
+      const half4_t t1 = cat4(C::exact(C::hi(l01)), C::exact(C::hi(l23)));   // byte 4k+1
+      const half4_t t2 = cat4(C::exact(C::lo(h01)), C::exact(C::lo(h23)));   // byte 4k+2
+      const half4_t t3 = cat4(C::exact(C::hi(h01)), C::exact(C::hi(h23)));   // byte 4k+3
       acc[4 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(t0, wb, acc[4 * k], 0, 0, 0);
       acc[4 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(t1, wb, acc[4 * k + 1], 0, 0, 0);
       acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);

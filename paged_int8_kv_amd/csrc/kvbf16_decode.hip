@@ -72,7 +72,7 @@ __host__ __device__ inline Bf16Smem bf16_smem(int split_tokens, int G, int D) {
   L.z_off = align16b((split_tokens / kBlock) * 4);
   L.fin_off = L.z_off + align16b(split_tokens * G * 4);
   L.red_off = L.fin_off + align16b(kWaves * G * D * 4);
-  L.flag_off = L.red_off + align16b(3 * kWaves * G * 4);
+  L.flag_off = L.red_off + align16b(2 * kWaves * G * 4);
   L.total = L.flag_off + 16;
   return L;
 }
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(Bf16Args a) {
   int* s_blk = reinterpret_cast<int*>(smem + L.blk_off);
   float* s_z = reinterpret_cast<float*>(smem + L.z_off);
   float* s_fin = reinterpret_cast<float*>(smem + L.fin_off);
-  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [3][kWaves][G]
+  float* s_red = reinterpret_cast<float*>(smem + L.red_off);   // [2][kWaves][G]
   int* s_flag = reinterpret_cast<int*>(smem + L.flag_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -340,9 +340,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(Bf16Args a) {
 
   groups_to_lds<G, CPL, D>(acc, s_fin, wave, lane, chunk);
   __syncthreads();
-  finish_split<G, D, kThreads, kWaves, false>(
+  finish_split<G, D, kThreads, kWaves>(
       PartialArgs{a.out, a.o_part, a.lse_part, a.counters, a.n_split}, s_fin, s_red, s_flag,
-      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid, 0.0f);
+      bh0, (int64_t)b * Hkv + g, split, it.nsplit, tid);
 }
 
 template <int D, int G, bool QF32>

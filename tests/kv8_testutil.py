@@ -102,6 +102,8 @@ def check_close(out, ref, what=""):
     max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
     den = float(np.linalg.norm(r))
     rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    print(f"parity margin [{what}]: max|delta| {max_abs:.3e} ({max_abs / MAX_ABS:.3f} of bound), "
+          f"rel L2 {rel:.3e} ({rel / REL_L2:.3f} of bound)")
     assert max_abs <= MAX_ABS, f"{what}: max|delta| {max_abs:.3e} > {MAX_ABS}"
     assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e} > {REL_L2}"
     return max_abs, rel
@@ -130,10 +132,12 @@ def gpu_prefill(case, cache, q=None, q_start_loc=None, context_lens=None, max_q_
     return out.cpu().numpy()
 
 
-def oracle_prefill_rows(case, cache_host, picks, q=None, context_lens=None):
+def oracle_prefill_rows(case, cache_host, picks, q=None, context_lens=None, gather=None):
     """fp64 oracle output for selected (sequence b, chunk row i) pairs, all
-    query heads: the oracle's gather, causal rule and softmax applied to
-    those rows only.  Returns [len(picks), Hq, d]."""
+    query heads: the oracle's gather (INT8 unless another code format's
+    gather is given), causal rule and softmax applied to those rows only.
+    Returns [len(picks), Hq, d]."""
+    gather = O.gather_dequant if gather is None else gather
     kc, vc, ks, vs = cache_host
     qv = case.q if q is None else q
     cl = case.context_lens if context_lens is None else context_lens
@@ -142,14 +146,16 @@ def oracle_prefill_rows(case, cache_host, picks, q=None, context_lens=None):
     G = hq // hkv
     sm = 1.0 / np.sqrt(case.head_dim)
     res = np.zeros((len(picks), hq, case.head_dim), np.float64)
-    for n, (b, i) in enumerate(picks):
+    for b in sorted({b for b, _ in picks}):
         ctx = int(cl[b])
         lc = int(qsl[b + 1] - qsl[b])
-        vis = O.causal_visibility(ctx, lc)[i:i + 1]
+        rows = [(n, i) for n, (bb, i) in enumerate(picks) if bb == b]
         for g in range(hkv):
-            k = O.gather_dequant(kc, ks, case.block_table[b], ctx, g)
-            v = O.gather_dequant(vc, vs, case.block_table[b], ctx, g)
-            for h in range(g * G, g * G + G):
-                qrow = np.asarray(qv[qsl[b] + i, h], np.float64)[None, :]
-                res[n, h] = O.softmax_attention(qrow, k, v, sm, vis)[0]
+            k = gather(kc, ks, case.block_table[b], ctx, g)
+            v = gather(vc, vs, case.block_table[b], ctx, g)
+            for n, i in rows:
+                vis = O.causal_visibility(ctx, lc)[i:i + 1]
+                for h in range(g * G, g * G + G):
+                    qrow = np.asarray(qv[qsl[b] + i, h], np.float64)[None, :]
+                    res[n, h] = O.softmax_attention(qrow, k, v, sm, vis)[0]
     return res

@@ -2,6 +2,8 @@
 dequantised cache), plus the invariants the method fixes: block-permutation
 invariance (bitwise), single-token exactness, poisoned unused slots, empty
 contexts, determinism, any split count."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -248,3 +250,44 @@ def test_decode_many_sequences_both_item_orders(batch):
                              context_lens=lens, seed=60 + batch)
     run_parity(case)
     run_parity(case, tokens_per_split=128)
+
+
+@functools.lru_cache(maxsize=None)
+def constant_sign_case(hq, hkv, logits):
+    """The adversarial case below with its oracle cache and output, built
+    once per shape and shared by the kernel forms."""
+    case = W.make_paged_case(batch=4, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                             context_lens=[32768, 20000, 2049, 4097], q_dtype="f32",
+                             seed=80 + hq)
+    rng = np.random.default_rng(81 + hq)
+    sign = np.where(rng.random((hkv, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    mag = rng.uniform(0.5, 4.0, size=(case.k.shape[0], 1, 1)).astype(np.float32)
+    v = sign[None] * mag * (1.0 - 0.02 * rng.random(case.v.shape, dtype=np.float32))
+    case.v, case.v_bits = W.to_bf16(v)
+    if logits == "flat":
+        case.q[:] = 0.0
+    else:
+        case.q *= np.float32(0.004)
+    cache = oracle_cache(case)
+    ref = O.paged_decode(case.q, *cache, case.block_table, case.context_lens)
+    return case, cache, ref
+
+
+@pytest.mark.parametrize("logits", ["flat", "near_flat"])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8)])
+def test_decode_adversarial_long_splits_constant_sign_values(hq, hkv, logits):
+    """Accumulator headroom.  Every V element of a head keeps one sign over
+    all tokens and sits within 2% of the token's absmax, so the INT8 codes
+    are all near +-127 of one sign and nothing cancels; Q is zero (every
+    logit 0, every weight equal) or tiny (logits within about +-0.05).  Each
+    split then sums its weighted codes to roughly split_len * 127 before the
+    merge, the largest sums the kernels ever hold.  Splits of 2048 tokens
+    (1280 at G = 8 for the forms that keep a split's logits in LDS), a
+    32768-token sequence beside shorter ragged ones."""
+    G = hq // hkv
+    tps = 1280 if G == 8 and U.FORM in (B.DECODE_DOT, B.DECODE_MFMA) else 2048
+    case, (kc, vc, ks, vs), ref = constant_sign_case(hq, hkv, logits)
+    codes = vc.astype(np.int32)
+    assert np.abs(codes[codes != 0]).min() >= 120
+    out = gpu_decode(case, upload_cache(kc, vc, ks, vs), tokens_per_split=tps)
+    check_close(out, ref, f"constant-sign V, {logits} logits, G={G}, tps={tps}")

@@ -14,7 +14,7 @@ from paged_int8_kv_amd import binding as B
 from paged_int8_kv_amd import workloads as W
 from tests import kv8_testutil as U
 from tests.kv8_testutil import (bits_tensor, check_close, dev, f16_to_i16, needs_gpu,
-                                q_tensor)
+                                oracle_prefill_rows, q_tensor)
 from tests.test_gpu_append import assert_cache_equal, rows_case
 
 pytestmark = [pytest.mark.gpu, needs_gpu, pytest.mark.usefixtures("decode_kernel")]
@@ -201,3 +201,23 @@ def test_fp8_prefill_ragged(hq, hkv, d):
 
 def test_fp8_prefill_chunked_config_reduced_batch():
     prefill_parity(W.chunked_prefill(batch=2), "fp8 chunked prefill batch 2")
+
+
+def test_fp8_prefill_chunked_config_full_sampled():
+    """The full chunked-prefill shape (batch 8) as the benchmark times it:
+    cache and chunk written by the GPU's FP8 append (bit-exact with the
+    oracle's), rows sampled across every sequence against the oracle."""
+    case = W.chunked_prefill()
+    host = oracle_cache_fp8(case)
+    cache = gpu_append_fp8(case)
+    assert_cache_equal(download(cache), host, "fp8 chunked prefill cache")
+    out = gpu_prefill_fp8(case, cache)
+    rng = np.random.default_rng(7)
+    picks = []
+    for b in range(case.batch):
+        for i in sorted({0, 1, 63, 64, 255, 256, 511, *rng.integers(0, 512, 3).tolist()}):
+            picks.append((b, int(i)))
+    ref = oracle_prefill_rows(case, host, picks, gather=O.gather_dequant_fp8)
+    qsl = case.extra["q_start_loc"]
+    got = np.stack([out[qsl[b] + i] for b, i in picks])
+    check_close(got, ref, "fp8 chunked prefill full, sampled rows")

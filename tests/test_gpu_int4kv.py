@@ -13,7 +13,8 @@ from oracle import kv8_oracle as O
 from paged_int8_kv_amd import binding as B
 from paged_int8_kv_amd import workloads as W
 from tests import kv8_testutil as U
-from tests.kv8_testutil import bits_tensor, check_close, dev, f16_to_i16, needs_gpu, q_tensor
+from tests.kv8_testutil import (bits_tensor, check_close, dev, f16_to_i16, needs_gpu,
+                                oracle_prefill_rows, q_tensor)
 from tests.test_gpu_append import assert_cache_equal, rows_case
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -186,3 +187,26 @@ def test_int4_prefill_chunked_config_reduced_batch_gpu_cache():
     GPU's INT4 append."""
     prefill_parity_int4(W.chunked_prefill(batch=2), "int4 chunked prefill batch 2",
                         cache_from="gpu")
+
+
+def test_int4_prefill_chunked_config_full_sampled():
+    """The full chunked-prefill shape (batch 8) as the benchmark times it:
+    cache and chunk written by the GPU's INT4 append, rows sampled across
+    every sequence against the oracle over the same cache."""
+    case = W.chunked_prefill()
+    host = oracle_cache_int4(case)
+    cache = gpu_append_int4(case)
+    got_cache = [x.cpu().numpy() for x in cache]
+    assert np.array_equal(got_cache[0], host[0]) and np.array_equal(got_cache[1], host[1])
+    assert np.array_equal(got_cache[2].view(np.float16), host[2])
+    assert np.array_equal(got_cache[3].view(np.float16), host[3])
+    out = gpu_prefill_int4(case, cache)
+    rng = np.random.default_rng(7)
+    picks = []
+    for b in range(case.batch):
+        for i in sorted({0, 1, 63, 64, 255, 256, 511, *rng.integers(0, 512, 3).tolist()}):
+            picks.append((b, int(i)))
+    ref = oracle_prefill_rows(case, host, picks, gather=O.gather_dequant_int4)
+    qsl = case.extra["q_start_loc"]
+    got = np.stack([out[qsl[b] + i] for b, i in picks])
+    check_close(got, ref, "int4 chunked prefill full, sampled rows")
