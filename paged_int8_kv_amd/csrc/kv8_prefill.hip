@@ -157,23 +157,43 @@ struct Stage {
   uint16_t sc;
 };
 
-template <int D>
-__device__ __forceinline__ int64_t block_base(const PrefillArgs& a, const int32_t* table_row,
-                                              int blk_idx, int last_blk, int g) {
-  int id = table_row[blk_idx < last_blk ? blk_idx : last_blk];
+// Cache block ids one thread's staging reads for a key tile (its K row's,
+// its V rows', its scale's), loaded a tile ahead of the data loads that use
+// them, so that those never wait on the block table.
+struct TileIds {
+  int k, v, s;
+};
+
+template <int D, bool NIB>
+__device__ __forceinline__ TileIds load_ids(const int32_t* table_row, int kt, int last_blk,
+                                            int tid) {
+  auto at = [&](int j) {
+    const int i = kt * 4 + j;
+    return table_row[i < last_blk ? i : last_blk];
+  };
+  // unconditional (threads without a V row or a scale load an id they do
+  // not use): no merge of loaded values across branches, which would wait
+  // for every load in flight
+  TileIds t;
+  t.k = at(tid >> 7);                                            // key tid/8, block key/16
+  t.v = at(((tid / (D / 4)) >> 2) & 3);
+  t.s = at((tid & 63) >> 4);
+  return t;
+}
+
+__device__ __forceinline__ int64_t slab_of(const PrefillArgs& a, int id, int g) {
   id = id < 0 ? 0 : (id >= a.num_blocks ? (int)(a.num_blocks - 1) : id);
   return (int64_t)id * a.num_kv_heads + g;       // (block, KV head) slab index
 }
 
 template <int D, bool NIB>
-__device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* table_row,
-                                           int kt, int last_blk, int g, int tid,
-                                           Stage<D, NIB>& st) {
+__device__ __forceinline__ void stage_load(const PrefillArgs& a, const TileIds& ids, int g,
+                                           int tid, Stage<D, NIB>& st) {
   constexpr int RB = NIB ? D / 2 : D;           // code bytes per cache row
   constexpr int KB = Stage<D, NIB>::kKBytes;
   {
     const int key = tid >> 3, part = tid & 7;
-    const int64_t slab = block_base<D>(a, table_row, kt * 4 + (key >> 4), last_blk, g);
+    const int64_t slab = slab_of(a, ids.k, g);
     const int8_t* src = a.k_cache + slab * (kBlock * RB) + (key & 15) * RB + part * KB;
     if constexpr (KB == 16) {
       const uint4 u = *reinterpret_cast<const uint4*>(src);
@@ -185,10 +205,13 @@ __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* 
       st.k[0] = *reinterpret_cast<const uint32_t*>(src);
     }
   }
-  if (tid < Stage<D, NIB>::kVTasks) {
-    const int cq = tid % (D / 4), kq = tid / (D / 4);
-    const int grp = kq >> 2, sub = kq & 3;
-    const int64_t slab = block_base<D>(a, table_row, kt * 4 + grp, last_blk, g);
+  // Branch-free: threads past the V tasks and the scale threads load in-bounds
+  // bytes they do not store, so that the loads of one tile always take one
+  // path and their waits count exactly.
+  {
+    const int cq = tid % (D / 4), kq = (tid / (D / 4)) & 15;
+    const int sub = kq & 3;
+    const int64_t slab = slab_of(a, ids.v, g);
     const int8_t* base = a.v_cache + slab * (kBlock * RB) + cq * (NIB ? 2 : 4);
     const int row0 = 8 * (sub >> 1) + 4 * (sub & 1);
 #pragma unroll
@@ -197,11 +220,11 @@ __device__ __forceinline__ void stage_load(const PrefillArgs& a, const int32_t* 
       else st.v[r] = *reinterpret_cast<const uint32_t*>(base + (row0 + r) * RB);
     }
   }
-  if (tid < 2 * kTileKeys) {
+  {
     const int key = tid & 63;
-    const int64_t slab = block_base<D>(a, table_row, kt * 4 + (key >> 4), last_blk, g);
-    const uint16_t* s = tid < kTileKeys ? a.k_scale : a.v_scale;
-    st.sc = s[slab * kBlock + (key & 15)];
+    const int64_t slab = slab_of(a, ids.s, g);
+    const uint16_t* sp = (tid & kTileKeys) == 0 ? a.k_scale : a.v_scale;
+    st.sc = sp[slab * kBlock + (key & 15)];
   }
 }
 
@@ -453,7 +476,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int32_t* table_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
 
   Stage<D, C::kBits == 4> st;
-  if (nkt > 0) stage_load<D>(a, table_row, 0, last_blk, g, tid, st);
+  TileIds ids_next = {0, 0, 0};
+  if (nkt > 0) {
+    const TileIds ids0 = load_ids<D, C::kBits == 4>(table_row, 0, last_blk, tid);
+    stage_load<D>(a, ids0, g, tid, st);
+    ids_next = load_ids<D, C::kBits == 4>(table_row, nkt > 1 ? 1 : 0, last_blk, tid);
+  }
 
   // ---- this lane's query: load Q, exact fp16 after a power-of-two scale ----
   const int nq = wave * kQueriesPerWave + m;
@@ -498,6 +526,19 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int wave_pos_lo = pos0 + wave_row_lo;   // smallest position of the wave
   const int wave_pos_hi = pos0 + wave_row_hi;   // largest
 
+  // V^T operand of row cb*32 + m, chunk 4kb + 2j + h: the row's swizzle is
+  // 2 (m >> 4 & 1) + (cb & 1), so the chunk stored there is 4kb + 2(j ^ m4)
+  // + (h ^ (cb & 1)); the lane-dependent part is one of four offsets.
+  const _Float16* vlane = &lds.v[0][m][0];
+  int vt_lane_off[2][2];
+  {
+    const int m4 = (m >> 4) & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) vt_lane_off[j][c] = 16 * (j ^ m4) + 8 * (h ^ c);
+  }
+
   f32x16_t acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
@@ -535,7 +576,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < nkt;
-    if (more) stage_load<D>(a, table_row, kt + 1, last_blk, g, tid, st);
+    stage_load<D>(a, ids_next, g, tid, st);   // the last step's load is not stored
+    ids_next = load_ids<D, C::kBits == 4>(table_row, kt + 2 < nkt ? kt + 2 : kt, last_blk, tid);
 
     const int key0 = kt * kTileKeys;
     if (wave_live && key0 <= wave_pos_hi) {
@@ -583,7 +625,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
             va[cb] = as_half8(*reinterpret_cast<const uint4*>(
-                &lds.v[buf][cb * 32 + m][8 * ((4 * kb + 2 * j + h) ^ vt_swizzle(cb * 32 + m))]));
+                vlane + buf * (D * Lds<D>::kVRow) + vt_lane_off[j][cb & 1] +
+                cb * 32 * Lds<D>::kVRow + 32 * kb));
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
             acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[cb], pw[kb][j], acc[cb], 0, 0, 0);
