@@ -195,6 +195,22 @@ struct Item {
 // per CU; later rounds keep the longest-first order, which the dispatcher
 // fills greedily as CUs free up.  With more sequences the items keep
 // sequence order.  Every wave locates its item itself.
+//
+// XCD grouping.  Workgroup i runs on XCD i mod 8, and one 128-byte line of
+// a block's scales holds 4 KV heads' rows.  So the ranks of each window of
+// 8 * Hkv are transposed (position 8a + x takes item Hkv * x + a): the Hkv
+// heads of one (sequence, split), of equal size and Hkv-aligned in the
+// order, share a rank residue mod 8, hence one XCD and its L2, and a scale
+// line comes from HBM once instead of once per head.  A last, partial
+// window keeps its order.
+__device__ __forceinline__ int xcd_group_rank(int rank, int total, int num_kv_heads) {
+  const int win = 8 * num_kv_heads;
+  const int w0 = rank - rank % win;
+  if (w0 + win > total) return rank;            // partial last window
+  const int p = rank - w0;
+  return w0 + num_kv_heads * (p % 8) + p / 8;
+}
+
 __device__ __forceinline__ Item locate_item(const int32_t* context_lens, int batch, int ctx_cap,
                                             int num_kv_heads, int split_tokens, int period,
                                             int snake_rounds, int lane) {
@@ -224,6 +240,7 @@ __device__ __forceinline__ Item locate_item(const int32_t* context_lens, int bat
       rank = r * period + ((r & 1) ? period - 1 - c : c);
     }
     if (rank < total) {
+      rank = xcd_group_rank(rank, total, num_kv_heads);
       const uint64_t hit = __ballot(lane < batch && start <= rank && rank < start + cnt);
       it.b = (int)__builtin_ctzll(hit);
       const int j = rank - __builtin_amdgcn_readlane(start, it.b);
@@ -233,8 +250,11 @@ __device__ __forceinline__ Item locate_item(const int32_t* context_lens, int bat
       it.nbt = __builtin_amdgcn_readlane(nb, it.b);
     }
   } else {
-    const int sg = (int)blockIdx.x / num_kv_heads;      // global split index
-    it.g = (int)blockIdx.x - sg * num_kv_heads;
+    // the grid covers every item (extra workgroups exit), so grouping over
+    // the grid size is a bijection onto the items and the empty tail
+    const int idx0 = xcd_group_rank((int)blockIdx.x, (int)gridDim.x, num_kv_heads);
+    const int sg = idx0 / num_kv_heads;                 // global split index
+    it.g = idx0 - sg * num_kv_heads;
     int base = 0;
     for (int c0 = 0; c0 < batch; c0 += 64) {
       const int bi = c0 + lane;
