@@ -308,10 +308,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
           if constexpr (NIB) {
 #pragma unroll
             for (int k = 0; k < NDC; ++k) {
-              const uint32_t x0 = C::pre(dword(w0, k)), x1 = C::pre(dword(w1, k));
+              const uint32_t x0 = dword(w0, k), x1 = dword(w1, k);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const half2_t a0 = C::logit_pair(x0, j), a1 = C::logit_pair(x1, j);
+                const half2_t a0 = C::logit_pair_raw(x0, j), a1 = C::logit_pair_raw(x1, j);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                   S[h] = fdot2(qh[h][4 * k + j], a0, S[h]);
@@ -434,13 +434,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a) {
 #pragma unroll
           for (int k = 0; k < NDC; ++k) {
             const uint32_t u0 = dword(w0, k), u1 = dword(w1, k);
-            const uint32_t lo = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
-            const uint32_t hi = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
+            const uint32_t lo = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               // unbiased exactly here: biased sums over a long split would
               // cancel away too many bits
-              const half2_t fl = C::exact(C::nib_pair(lo, j)), fh = C::exact(C::nib_pair(hi, j));
+              const half2_t fl = C::exact(C::nib_pair_raw(lo, j));
+              const half2_t fh = C::exact(C::nib_pair_raw(hi, j));
 #pragma unroll
               for (int h = 0; h < G; ++h) {
                 acc[h * CPL + 8 * k + j] = fdot2(wp[h], fl, acc[h * CPL + 8 * k + j]);

@@ -207,8 +207,8 @@ struct CodesFp8 {
 // i.  A dword holds 8 codes.  Flipping each nibble's sign bit (xor 0x8)
 // gives u = c + 8, and u under the fp16 pattern 0x6400 is the value
 // 1024 + u = c + 1032 exactly.  nib_pair(x, j) makes the fp16 pair of
-// nibbles j and j + 4 of the (already flipped) dword x.  logit_pair(x, j)
-// makes the same pair with u in the top four mantissa bits under 0x3C00,
+// nibbles j and j + 4 of the (already flipped) dword x.  The logit pairs
+// (logit_pair_raw) hold u in the top four mantissa bits under 0x3C00,
 // the value 1 + u / 16 = 1.5 + c / 16 exactly, for the logit products: a
 // bias of 24 code steps in place of 1032 (summed against q of up to 2^15,
 // the 1032 bias cost the logits enough to put 6e-4 relative error into the
@@ -224,9 +224,16 @@ struct CodesInt4 {
   __device__ static half2_t nib_pair(uint32_t x, int j) {
     return __builtin_bit_cast(half2_t, ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
   }
-  __device__ static half2_t logit_pair(uint32_t x, int j) {
+  // The pairs from the raw dword, without pre(): the sign flip commutes
+  // with the shift and the mask, and its bit meets none of the fp16
+  // pattern's, so it folds into that constant; a pair is then one shift and
+  // one three-input bit operation.
+  __device__ static half2_t nib_pair_raw(uint32_t x, int j) {
+    return __builtin_bit_cast(half2_t, ((x >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
+  }
+  __device__ static half2_t logit_pair_raw(uint32_t x, int j) {
     const uint32_t y = j < 2 ? x << (6 - 4 * j) : x >> (4 * j - 6);
-    return __builtin_bit_cast(half2_t, (y & 0x03C003C0u) | 0x3C003C00u);
+    return __builtin_bit_cast(half2_t, (y & 0x03C003C0u) ^ 0x3E003E00u);
   }
   __device__ static half2_t exact(half2_t p) {
     const half2_t bias = {(_Float16)kBias, (_Float16)kBias};

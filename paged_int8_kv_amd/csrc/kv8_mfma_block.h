@@ -128,9 +128,9 @@ __device__ __forceinline__ void q_operands(const SplitArgs& a, int64_t bh0, int 
 template <class C, int NCH>
 __device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) {
   if constexpr (C::kBits == 4) {
-    const uint32_t x = C::pre(dw(rk[0], j));
-    return cat8(C::logit_pair(x, 0), C::logit_pair(x, 1), C::logit_pair(x, 2),
-                C::logit_pair(x, 3));
+    const uint32_t x = dw(rk[0], j);
+    return cat8(C::logit_pair_raw(x, 0), C::logit_pair_raw(x, 1), C::logit_pair_raw(x, 2),
+                C::logit_pair_raw(x, 3));
   } else {
     const uint4 r = rk[j / 2];
     const uint32_t x0 = C::pre(dw(r, 2 * (j % 2))), x1 = C::pre(dw(r, 2 * (j % 2) + 1));
@@ -156,17 +156,17 @@ __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
   if constexpr (C::kBits == 4) {
     const uint32_t u0 = dw(rv[0], 0), u1 = dw(rv[1], 0);
     const uint32_t u2 = dw(rv[2], 0), u3 = dw(rv[3], 0);
-    const uint32_t l01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x05040100u));
-    const uint32_t h01 = C::pre(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
-    const uint32_t l23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x05040100u));
-    const uint32_t h23 = C::pre(__builtin_amdgcn_perm(u3, u2, 0x07060302u));
+    const uint32_t l01 = __builtin_amdgcn_perm(u1, u0, 0x05040100u);
+    const uint32_t h01 = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    const uint32_t l23 = __builtin_amdgcn_perm(u3, u2, 0x05040100u);
+    const uint32_t h23 = __builtin_amdgcn_perm(u3, u2, 0x07060302u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::exact(C::nib_pair(l01, j)), C::exact(C::nib_pair(l23, j))), wb, acc[j], 0, 0,
+          cat4(C::exact(C::nib_pair_raw(l01, j)), C::exact(C::nib_pair_raw(l23, j))), wb, acc[j], 0, 0,
           0);
       acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::exact(C::nib_pair(h01, j)), C::exact(C::nib_pair(h23, j))), wb, acc[4 + j], 0,
+          cat4(C::exact(C::nib_pair_raw(h01, j)), C::exact(C::nib_pair_raw(h23, j))), wb, acc[4 + j], 0,
           0, 0);
     }
   } else {
