@@ -73,8 +73,15 @@ __global__ __launch_bounds__(256) void quant_append_kernel(
   const int64_t slot = slot_mapping[n];
   const bool keep = slot >= 0 && slot < num_slots;
 
-  const uint4 kraw = *reinterpret_cast<const uint4*>(k_new + row * D + part * 8);
-  const uint4 vraw = *reinterpret_cast<const uint4*>(v_new + row * D + part * 8);
+  // K and V are read once: nontemporal loads (fill 185 -> 153 us per call
+  // for 131,072 tokens x 8 heads; nontemporal code stores measured slower)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 kv4 =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + row * D + part * 8));
+  const u32x4 vv4 =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + row * D + part * 8));
+  const uint4 kraw = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
+  const uint4 vraw = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
   float kx[8], vx[8], ka, va;
   unpack8(kraw, kx, ka);
   unpack8(vraw, vx, va);
