@@ -272,7 +272,9 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
     // counts exact).  kSkPf blocks are in flight per wave: the K codes and
     // both scale rows of block i + kSkPf are requested once block i's
     // weights are formed, its V codes once block i's value MFMAs have read
-    // theirs.
+    // theirs.  Codes are read once per call and come nontemporal (long
+    // context: 62 -> 59 us per step; the 80-layer sweep 122 -> 115 us per
+    // layer); the scales stay ordinary loads, one line serving several heads.
     auto row0_of = [&](int i, bool& real) {
       real = i < cnt;
       const int ii = real ? i : cnt - 1;
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
       const int8_t* pk = a.k_cache + row0 * RB + (real ? hl * RB + 16 * q4 : 0);
 #pragma unroll
       for (int u = 0; u < (NIB ? 1 : NCH); ++u)
-        rk[sl][u] = *reinterpret_cast<const uint4*>(pk + 64 * u);
+        rk[sl][u] = nt_load(reinterpret_cast<const uint4*>(pk + 64 * u));
       const int so = real ? 4 * q4 : 0;
       ksc[sl] = *reinterpret_cast<const uint2*>(a.k_scale + row0 + so);
       vsc[sl] = *reinterpret_cast<const uint2*>(a.v_scale + row0 + so);
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
           a.v_cache + row0 * RB + (real ? 4 * q4 * RB + hl * (NIB ? NVT / 2 : NVT) : 0);
       const int stride = real ? RB : 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) rv[sl][t] = *reinterpret_cast<const VRow*>(pv + t * stride);
+      for (int t = 0; t < 4; ++t) rv[sl][t] = nt_load(reinterpret_cast<const VRow*>(pv + t * stride));
     };
 #pragma unroll
     for (int sl = 0; sl < kSkPf; ++sl) {

@@ -40,6 +40,22 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(a, b);
 }
 
+// Nontemporal loads of cache codes, for kernels that stream every code once
+// over a footprint larger than the last-level cache.
+typedef unsigned int ntu32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int ntu32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+  const ntu32x4 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 nt_load(const uint2* p) {
+  const ntu32x2 v = __builtin_nontemporal_load(reinterpret_cast<const ntu32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t nt_load(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 template <int NDW> struct VRowT;
 template <> struct VRowT<2> { using type = uint2; };
 template <> struct VRowT<1> { using type = uint32_t; };
