@@ -506,14 +506,13 @@ def bench_read_ceiling(dev, n_bytes, tile_bytes=2048, buffer_bytes=1 << 30, repl
     """The measured HBM read rate of the decode's access pattern: the
     library's kv8_read_probe streams about n_bytes per launch as random
     tile_bytes tiles (one (block, KV head) code tile of the decode) out of a
-    1 GiB buffer, rotating `replicas` tile orders, persistent workgroups
-    with nontemporal loads, launches back to back between HIP events on the
-    current stream."""
+    1 GiB buffer, rotating `replicas` tile orders, each wave of the
+    persistent workgroups streaming its own tiles, launches back to back
+    between HIP events on the current stream."""
     import torch
     from paged_int8_kv_amd import binding as B
-    chunk = B.load().kv8_read_probe_chunk_bytes()
-    n_read = max(1, n_bytes // chunk) * chunk
-    n_tiles_read = n_read // tile_bytes
+    n_tiles_read = max(1, n_bytes // tile_bytes)
+    n_read = n_tiles_read * tile_bytes
     n_tiles_buf = buffer_bytes // tile_bytes
     buf = torch.zeros(buffer_bytes, dtype=torch.uint8, device=dev)
     rng = np.random.Generator(np.random.PCG64(11))
@@ -534,8 +533,8 @@ def bench_read_ceiling(dev, n_bytes, tile_bytes=2048, buffer_bytes=1 << 30, repl
     us = e0.elapsed_time(e1) * 1e3 / launches
     del buf, orders, out
     torch.cuda.empty_cache()
-    return {"kernel": "kv8_read_probe: read-only, random tiles, persistent workgroups, "
-                      "nontemporal 16-byte loads",
+    return {"kernel": "kv8_read_probe: read-only, random tiles streamed per wave, "
+                      "persistent workgroups, ordinary 16-byte loads, 4 KB in flight per wave",
             "tile_bytes": tile_bytes, "buffer_bytes": buffer_bytes, "bytes_per_launch": int(n_read),
             "workgroups": wg, "us_per_launch": round(us, 2),
             "gbs": round(n_read / (us * 1e-6) / 1e9, 1),

@@ -491,27 +491,29 @@ int paged_prefill_chunk_attn_int4kv(const uint16_t* q, const int32_t* q_start_lo
  * Read ceilings - measurement utilities, not part of the attention method:
  * HBM read rates of this device against which the decode kernels' achieved
  * bandwidth is reported (the memory-bound decode argument of the
- * garden.houmin.site KV-cache optimisation page, section 1.3).  Both read
- * n_bytes (a positive multiple of kv8_read_probe_chunk_bytes(), 32 KB)
- * with `workgroups` persistent workgroups of 256 threads: workgroup w reads
- * chunks w, w + workgroups, w + 2 * workgroups, ... with nontemporal 16-byte
- * loads, 8 per lane in flight, and writes one xor per thread to `out`
- * (device uint32 [workgroups * 256]).  A few workgroups per compute unit
- * (e.g. 4 x 256 on MI355X) give the highest rate.  Make buf far larger
- * than the last-level cache.  Both return KV8_OK, KV8_ERR_NULL,
- * KV8_ERR_SHAPE (sizes out of range), KV8_ERR_ALIGN (buf not 16-byte
- * aligned) or KV8_ERR_HIP, asynchronously on `stream`.
+ * garden.houmin.site KV-cache optimisation page, section 1.3).  Both are
+ * read-only, persistent (`workgroups` workgroups of 256 threads; a few per
+ * compute unit, e.g. 4 x 256 on MI355X, give the highest rate) and write
+ * one xor per thread of the 16-byte units the thread read to `out` (device
+ * uint32 [workgroups * 256]).  Make buf far larger than the last-level
+ * cache.  Both return KV8_OK, KV8_ERR_NULL, KV8_ERR_SHAPE (sizes out of
+ * range), KV8_ERR_ALIGN (buf not 16-byte aligned) or KV8_ERR_HIP,
+ * asynchronously on `stream`.
  *
- * kv8_stream_read - plain streaming read: chunk c is bytes
- *   [c * chunk, (c + 1) * chunk) of buf, which holds n_bytes.
- * kv8_read_probe - the access pattern of the paged decode: logical 16-byte
- *   position p of the stream reads
- *     buf[tiles[p / (tile_bytes / 16)] * tile_bytes + (p % (tile_bytes / 16)) * 16]
- *   tiles: device int32 [n_bytes / tile_bytes], each in [0, n_tiles) for a
- *   buf of n_tiles * tile_bytes bytes (not checked on the device: an index
- *   outside the buffer is undefined); tile_bytes a multiple of 256 that
- *   divides the chunk.  A workgroup loads the tile indices of its next chunk
- *   while the current chunk's data loads are in flight.
+ * kv8_stream_read - plain streaming read of n_bytes (a positive multiple
+ *   of kv8_read_probe_chunk_bytes(), 32 KB): workgroup w reads chunks w,
+ *   w + workgroups, ... (chunk c is bytes [c * chunk, (c + 1) * chunk) of
+ *   buf) with nontemporal 16-byte loads, 8 per lane in flight; thread t of
+ *   a workgroup reads units t, t + 256, ... of each of its chunks.
+ * kv8_read_probe - the access pattern of the paged decode: n_bytes / tile_bytes
+ *   random tiles, tile i being bytes [tiles[i] * tile_bytes, (tiles[i] + 1) *
+ *   tile_bytes) of buf.  tiles: device int32 [n_bytes / tile_bytes], each in
+ *   [0, n_tiles) for a buf of n_tiles * tile_bytes bytes (not checked on the
+ *   device: an index outside the buffer is undefined); tile_bytes a multiple
+ *   of 1024 up to 32768; n_bytes a positive multiple of tile_bytes.  Wave v
+ *   (v = 4 * workgroup + wave) of the nw = 4 * workgroups waves reads tiles
+ *   v, v + nw, v + 2 nw, ... in order as 1 KB rows, lane l reading unit l of
+ *   each row, 4 rows in flight, ordinary loads.
  */
 int64_t kv8_read_probe_chunk_bytes(void);
 int kv8_stream_read(const void* buf, int64_t n_bytes, int64_t workgroups, uint32_t* out,

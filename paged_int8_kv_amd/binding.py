@@ -352,10 +352,10 @@ def paged_prefill_chunk_attn_int4kv(q, q_start_loc, max_q_len, k_cache, v_cache,
 
 def kv8_read_probe(buf, tiles, tile_bytes, workgroups, out, stream=None):
     """Measurement utility: one launch of the random-tile read over `buf`
-    (uint8 device tensor) in the tile order `tiles` (int32; tiles.numel() *
-    tile_bytes must be a multiple of the chunk size) by `workgroups`
-    persistent workgroups; `out` uint32 [workgroups * 256].  Returns the
-    bytes the launch reads."""
+    (uint8 device tensor) in the tile order `tiles` (int32, tiles of
+    tile_bytes, a multiple of 1024 up to 32768) by `workgroups` persistent
+    workgroups; `out` uint32 [workgroups * 256].  Returns the bytes the
+    launch reads."""
     n_bytes = tiles.numel() * tile_bytes
     if workgroups * 256 > out.numel():
         raise ValueError("out too small")

@@ -405,9 +405,8 @@ int64_t kv8_read_probe_chunk_bytes(void) { return kv8::read_probe_chunk_bytes();
 int kv8_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t n_bytes,
                    int64_t workgroups, uint32_t* out, void* stream) {
   if (!buf || !tiles || !out) return KV8_ERR_NULL;
-  const int64_t chunk = kv8::read_probe_chunk_bytes();
-  if (tile_bytes < 256 || tile_bytes % 256 != 0 || chunk % tile_bytes != 0) return KV8_ERR_SHAPE;
-  if (n_bytes <= 0 || n_bytes % chunk != 0) return KV8_ERR_SHAPE;
+  if (tile_bytes < 1024 || tile_bytes > 32768 || tile_bytes % 1024 != 0) return KV8_ERR_SHAPE;
+  if (n_bytes <= 0 || n_bytes % tile_bytes != 0) return KV8_ERR_SHAPE;
   if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return KV8_ERR_SHAPE;
   if (!aligned16(buf)) return KV8_ERR_ALIGN;
   return kv8::launch_read_probe(buf, tiles, tile_bytes, n_bytes, workgroups, out,

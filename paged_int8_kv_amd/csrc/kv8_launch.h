@@ -99,10 +99,10 @@ int launch_prefill(const uint16_t* q, const int32_t* q_start_loc, int64_t total_
                    int num_q_heads, int num_kv_heads, int head_dim, float sm_scale, float* out,
                    int fmt, hipStream_t stream);
 
-// The read-only kernels behind kv8_read_probe (tiles given) and
-// kv8_stream_read (tiles null: contiguous), in kv8_probe.hip: `workgroups`
-// persistent workgroups read n_bytes (a multiple of read_probe_chunk_bytes)
-// in chunks.
+// The read-only kernels behind kv8_read_probe (tiles given: n_bytes /
+// tile_bytes random tiles, streamed per wave) and kv8_stream_read (tiles
+// null: contiguous n_bytes, a multiple of read_probe_chunk_bytes, in
+// chunks), in kv8_probe.hip, on `workgroups` persistent workgroups.
 int64_t read_probe_chunk_bytes();
 int launch_read_probe(const void* buf, const int32_t* tiles, int tile_bytes, int64_t n_bytes,
                       int64_t workgroups, uint32_t* out, hipStream_t stream);

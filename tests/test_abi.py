@@ -315,18 +315,17 @@ def test_int4_prefill_validation_matches_int8(kw):
 
 def test_read_probe_validation():
     """Host-side checks of the measurement probe: null pointers, tile sizes
-    that are not a multiple of 256 or do not divide the 32 KB chunk, byte
-    counts that are not whole chunks, workgroup counts out of range, a
-    misaligned buffer."""
+    that are not a multiple of 1 KB or exceed 32 KB, byte counts that are
+    not whole tiles, workgroup counts out of range, a misaligned buffer."""
     lib = B.load()
     assert lib.kv8_read_probe_chunk_bytes() == 32768
     n = 10 * 32768
     assert lib.kv8_read_probe(None, P, 2048, n, 10, P2, None) == B.KV8_ERR_NULL
     assert lib.kv8_read_probe(P, None, 2048, n, 10, P2, None) == B.KV8_ERR_NULL
     assert lib.kv8_read_probe(P, P, 2048, n, 10, None, None) == B.KV8_ERR_NULL
-    for bad in (0, 16, 24, 128, 768, 3000, 65536):
+    for bad in (0, 16, 24, 128, 256, 512, 768, 1536, 3000, 33792, 65536):
         assert lib.kv8_read_probe(P, P, bad, n, 10, P2, None) == B.KV8_ERR_SHAPE
-    for bad_n in (0, -32768, 32768 + 16):
+    for bad_n in (0, -2048, 1024, 32768 + 16):
         assert lib.kv8_read_probe(P, P, 2048, bad_n, 10, P2, None) == B.KV8_ERR_SHAPE
     assert lib.kv8_read_probe(P, P, 2048, n, 0, P2, None) == B.KV8_ERR_SHAPE
     assert lib.kv8_read_probe(P, P, 2048, n, 1 << 31, P2, None) == B.KV8_ERR_SHAPE
