@@ -516,15 +516,19 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Automatic choice (measured on MI355X):
 // - below G = 4: the v_dot2 kernel (the vector work per cache byte, G/2
 //   v_dot2 issues per lane, still fits under the memory stream);
-// - G = 4, short contexts (at most 8192 tokens) in a grid of about one
-//   round of workgroups: the two-pass matrix-core form, whose 84 VGPRs leave
-//   room for five workgroups per CU (37.3 us on the Llama-3.1-8B-shaped
-//   batch, 1024..4096 tokens, against 41.6 us for stream-K and 39.5 us for
-//   the one-pass form);
-// - G = 4 otherwise, and from G = 8: the stream-K form (61.3 against 66.5 us
-//   per step for the one-pass form on 4 sequences of 32768 tokens, 1488
-//   against 1525 us on 15 sequences of 264192 tokens, 125.7 against 139.8 us
-//   per layer of the Llama-3-70B-shaped sweep at G = 8).
+// - G = 4, a grid bound of at most 1024 workgroups (one round at five
+//   two-pass workgroups per CU) and a longest context in (2048, 8192]: the
+//   two-pass matrix-core form, 3-7% ahead of stream-K there (37.3 against
+//   41.6 us on the Llama-3.1-8B-shaped batch, 32 x 1024..4096 tokens; 39.3
+//   against 42.2 us on 16 x 2048..8192);
+// - G = 4 otherwise, and from G = 8: the stream-K form.  With more work items
+//   than one round the two-pass form falls behind by 5-18% (32 x
+//   2048..8192: 79.3 against 66.8 us; 96 x 1024..4096: 117.5 against
+//   95.9 us), and with short contexts it ties or loses (64 x 512..2048: 44.8
+//   against 42.8 us).  Long contexts: 61.3 against 66.5 us per step for the
+//   one-pass form on 4 sequences of 32768 tokens, 1488 against 1525 us on
+//   15 sequences of 264192 tokens; 125.7 against 139.8 us per layer of the
+//   Llama-3-70B-shaped sweep at G = 8.
 // `grid_bound` is the workgroup count with every sequence at the longest
 // context and 1024-token splits.
 // - INT4 codes: the matrix-core forms serve d = 128 only (the v_dot2
@@ -538,8 +542,9 @@ int decode_form(int requested, int fmt, int G, long long grid_bound, int max_con
   if (fmt == kFmtInt4) return G >= 4 ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
   if (G >= 8) return kDecodeKernelStreamK;
   if (G >= 4)
-    return grid_bound <= 4096 && max_context_len <= 8192 ? kDecodeKernelMfma
-                                                         : kDecodeKernelStreamK;
+    return grid_bound <= 1024 && max_context_len > 2048 && max_context_len <= 8192
+               ? kDecodeKernelMfma
+               : kDecodeKernelStreamK;
   return kDecodeKernelDot;
 }
 
