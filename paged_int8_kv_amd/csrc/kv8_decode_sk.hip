@@ -183,9 +183,9 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
 
   const int64_t T = total_units(a, lane);
   const int64_t wu0 = (int64_t)w * T / nw, wu1 = (int64_t)(w + 1) * T / nw;
-  // Wave parts: 16 near-equal contiguous parts, each non-empty when the
-  // workgroup holds at least 16 units; with fewer, one unit for each of the
-  // first waves.  Either way the empty parts come last, so the waves holding
+  // Wave parts: kSkWaves near-equal contiguous parts, each non-empty when
+  // the workgroup holds at least kSkWaves units; with fewer, one unit for
+  // each of the first waves.  Either way the empty parts come last, so the waves holding
   // pieces of one pair are consecutive.
   const int64_t n = wu1 - wu0;
   const int64_t u0 = wu0 + (n >= kSkWaves ? (int64_t)wave * n / kSkWaves : min((int64_t)wave, n));
