@@ -97,10 +97,10 @@ int kv8_version(void);
  * paged_decode_attn_kv8_append, paged_decode_attn_fp8kv and
  * paged_decode_attn_int4kv chooses, for that call only, which kernel runs:
  *   KV8_DECODE_AUTO (0): by group size G = Hq / Hkv and size (v_dot2 below
- *     G = 4; at G = 4 two-pass matrix-core for 2048 < max_context_len <= 8192
- *     with a grid bound, every sequence at max_context_len in 1024-token
- *     splits, of at most 1024 workgroups, else stream-K; stream-K from
- *     G = 8; for the INT4 cache one-pass from G = 4 at d = 128, else v_dot2);
+ *     G = 4; from G = 4 two-pass matrix-core for 2048 < max_context_len <=
+ *     8192 with a grid bound, every sequence at max_context_len in
+ *     1024-token splits, of at most 1024 workgroups, else stream-K; for the
+ *     INT4 cache one-pass from G = 4 at d = 128, else v_dot2);
  *   KV8_DECODE_DOT (1): the v_dot2 kernel;
  *   KV8_DECODE_MFMA (2): the two-pass matrix-core kernel (logits of the
  *     split to LDS, then the weighted values; logits and values as 16x16

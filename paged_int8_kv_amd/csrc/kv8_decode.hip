@@ -516,12 +516,13 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Automatic choice (measured on MI355X):
 // - below G = 4: the v_dot2 kernel (the vector work per cache byte, G/2
 //   v_dot2 issues per lane, still fits under the memory stream);
-// - G = 4, a grid bound of at most 1024 workgroups (one round at five
+// - from G = 4, a grid bound of at most 1024 workgroups (one round at five
 //   two-pass workgroups per CU) and a longest context in (2048, 8192]: the
-//   two-pass matrix-core form, 3-7% ahead of stream-K there (37.3 against
-//   41.6 us on the Llama-3.1-8B-shaped batch, 32 x 1024..4096 tokens; 39.3
-//   against 42.2 us on 16 x 2048..8192);
-// - G = 4 otherwise, and from G = 8: the stream-K form.  With more work items
+//   two-pass matrix-core form, 3-7% ahead of stream-K there at G = 4 (37.3
+//   against 41.6 us on the Llama-3.1-8B-shaped batch, 32 x 1024..4096
+//   tokens; 39.3 against 42.2 us on 16 x 2048..8192) and 1-6% at G = 8
+//   (42.0 against 44.5 us on 16 x 2048..8192);
+// - otherwise the stream-K form.  With more work items
 //   than one round the two-pass form falls behind by 5-18% (32 x
 //   2048..8192: 79.3 against 66.8 us; 96 x 1024..4096: 117.5 against
 //   95.9 us), and with short contexts it ties or loses (64 x 512..2048: 44.8
@@ -540,7 +541,6 @@ int decode_form(int requested, int fmt, int G, long long grid_bound, int max_con
   if (fmt == kFmtInt4 && head_dim != 128) return kDecodeKernelDot;
   if (requested != kDecodeKernelAuto) return requested;
   if (fmt == kFmtInt4) return G >= 4 ? kDecodeKernelMfmaOnePass : kDecodeKernelDot;
-  if (G >= 8) return kDecodeKernelStreamK;
   if (G >= 4)
     return grid_bound <= 1024 && max_context_len > 2048 && max_context_len <= 8192
                ? kDecodeKernelMfma

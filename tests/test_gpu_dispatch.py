@@ -2,9 +2,9 @@
 side of the rule, a launch under KV8_DECODE_AUTO must be bitwise the launch
 of the form the rule names:
 - v_dot2 below 4 query heads per KV head;
-- two-pass matrix-core at 4 for contexts of 2049..8192 tokens in a grid
-  bound of at most 1024 workgroups;
-- stream-K matrix-core for long contexts and from 8 heads per KV head;
+- two-pass matrix-core from 4 heads per KV head for contexts of
+  2049..8192 tokens in a grid bound of at most 1024 workgroups;
+- stream-K matrix-core otherwise from 4 heads per KV head;
 - INT4: one-pass matrix-core from 4 heads per KV head at d = 128, v_dot2 at
   d = 64.
 The named form must also differ from the other forms on that input, so that
@@ -36,7 +36,9 @@ def run_forms(run):
     (32, 8, [9000, 100], "sk"),                  # G = 4, a context past 8192 tokens
     (32, 8, [2048, 700, 1], "sk"),               # G = 4, no context past 2048 tokens
     (32, 8, [4096] + [16] * 32, "sk"),           # G = 4, grid bound 33 * 4 * 8 > 1024
-    (64, 8, [500, 2000, 1], "sk"),               # G = 8
+    (64, 8, [500, 2000, 1], "sk"),               # G = 8, no context past 2048 tokens
+    (64, 8, [3000, 100, 2500], "mfma"),          # G = 8, mid-length contexts, small grid
+    (64, 8, [9000, 700], "sk"),                  # G = 8, a context past 8192 tokens
 ])
 def test_auto_form_int8(hq, hkv, lens, expected):
     case = W.make_paged_case(batch=len(lens), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
