@@ -60,14 +60,22 @@ __device__ __forceinline__ int seq_blocks(const SplitArgs& a, int b, int& ctx) {
   return (ctx + kBlock - 1) / kBlock;
 }
 
+// The first 64 sequences' context lengths, block counts and their
+// inclusive scan, kept from total_units for locate_units.
+struct Chunk0 {
+  int ctx, nb, incl, ntot;
+};
+
 // Total units T = Hkv * sum_b nb_b (every lane receives it).
-__device__ __forceinline__ int64_t total_units(const SplitArgs& a, int lane) {
+__device__ __forceinline__ int64_t total_units(const SplitArgs& a, int lane, Chunk0& k0) {
   int64_t tot = 0;
   for (int c0 = 0; c0 < a.batch; c0 += 64) {
     int ctx = 0;
     const int nb = c0 + lane < a.batch ? seq_blocks(a, c0 + lane, ctx) : 0;
     const int incl = wave_incl_scan(nb, lane);
-    tot += __builtin_amdgcn_readlane(incl, 63);
+    const int n = __builtin_amdgcn_readlane(incl, 63);
+    if (c0 == 0) k0 = Chunk0{ctx, nb, incl, n};
+    tot += n;
   }
   return tot * a.num_kv_heads;
 }
@@ -77,13 +85,21 @@ __device__ __forceinline__ int64_t total_units(const SplitArgs& a, int lane) {
 // sequence of the batch's first unit; a wave-uniform walk then takes the
 // few sequences the batch spans in order, each giving its lanes' KV head and
 // block by one division by the sequence's block count.
-__device__ __forceinline__ Unit locate_units(const SplitArgs& a, int base, int cnt, int lane) {
+__device__ __forceinline__ Unit locate_units(const SplitArgs& a, int base, int cnt, int lane,
+                                            const Chunk0& k0) {
   Unit x{0, 0, 0, 16};
   const int Hkv = a.num_kv_heads;
   const int u = base + lane;
   int before = 0;             // units of the sequences before chunk c0
   int c0 = 0, ctx = 0, nb = 0, incl = 0, ntot = 0;
   auto load_chunk = [&]() {
+    if (c0 == 0) {            // wave-uniform: the first chunk is already at hand
+      ctx = k0.ctx;
+      nb = k0.nb;
+      incl = k0.incl;
+      ntot = k0.ntot;
+      return;
+    }
     ctx = 0;
     nb = c0 + lane < a.batch ? seq_blocks(a, c0 + lane, ctx) : 0;
     incl = wave_incl_scan(nb, lane);
@@ -181,7 +197,8 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
     }
   }
 
-  const int64_t T = total_units(a, lane);
+  Chunk0 k0{0, 0, 0, 0};
+  const int64_t T = total_units(a, lane, k0);
   const int64_t wu0 = (int64_t)w * T / nw, wu1 = (int64_t)(w + 1) * T / nw;
   // Wave parts: kSkWaves near-equal contiguous parts, each non-empty when
   // the workgroup holds at least kSkWaves units; with fewer, one unit for
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
 
   for (int64_t base = u0; base < u1; base += 64) {
     const int cnt = (int)min((int64_t)64, u1 - base);
-    const Unit un = locate_units(a, (int)base, cnt, lane);
+    const Unit un = locate_units(a, (int)base, cnt, lane, k0);
 
     // the decode step with append: the newest token of every pair whose
     // last block is in this batch, stored before the batch's loads
