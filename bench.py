@@ -62,6 +62,10 @@ def parse():
                    help="sequences the 16-bit cache holds; sets the memory budget")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain elementwise copy of known size (for HBM counters)")
+    p.add_argument("--decode-scaling", action="store_true",
+                   help="only time the decode against bytes: the Llama-3.1-8B-shaped batch with "
+                        "contexts scaled x0.5..x4, every matrix-core form and the random-tile "
+                        "read probe on the same bytes (one JSON line)")
     return p.parse_args()
 
 
@@ -127,6 +131,9 @@ def main():
                  "mfma1": B.DECODE_MFMA_ONEPASS, "sk": B.DECODE_STREAMK}[args.decode_kernel]
     if args.calibrate_copy:
         calibrate_copy(dev)
+        return
+    if args.decode_scaling:
+        decode_scaling(dev)
         return
     case = W.llama8b_decode()
     bsz, hq, hkv, d = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim
@@ -814,6 +821,85 @@ def bench_equal_budget(args, dev):
         (outs["int4_kv"][:n] - outs["bf16_kv"][:n]).abs().max().item())
     res["pages_figure"] = "1.64x KV8 over FA2 at 258K, same memory budget, L40S, system level"
     return res
+
+
+def decode_scaling(dev, scales=(0.5, 1.0, 2.0, 4.0), launches=100, seed=12):
+    """Decode time against bytes.  The Llama-3.1-8B-shaped batch (32
+    sequences, 32/8 heads, d=128, bf16 q) with contexts U[1024 f, 4096 f]
+    for each f: random codes and scales drawn on the device (the kernels'
+    time does not depend on the values), a permuted block table, enough
+    cache copies rotated back to back to pass the last-level cache.  Each
+    matrix-core form, and the random-tile read probe over the same bytes.
+    The line through the two smallest points gives each form's fixed cost
+    (intercept) and streaming rate (slope) where its grid is one round; the
+    line through the two largest, the same at sizes of several rounds."""
+    import torch
+    from paged_int8_kv_amd import binding as B
+    hq, hkv, d, bsz = 32, 8, 128, 32
+    forms = {"two_pass": B.DECODE_MFMA, "one_pass": B.DECODE_MFMA_ONEPASS,
+             "stream_k": B.DECODE_STREAMK}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    rows = []
+    for f in scales:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        ctx = rng.integers(int(1024 * f), int(4096 * f) + 1, size=bsz)
+        nb = (ctx + 15) // 16
+        nblocks, maxb = int(nb.sum()), int(nb.max())
+        perm = rng.permutation(nblocks).astype(np.int32)
+        table = np.zeros((bsz, maxb), np.int32)
+        o = 0
+        for b in range(bsz):
+            table[b, :nb[b]] = perm[o:o + nb[b]]
+            o += nb[b]
+        nbytes = decode_bytes(ctx, hkv, d, hq, 2)
+        reps = max(2, int(np.ceil(800e6 / nbytes)))
+        caches = []
+        for _ in range(reps):
+            kc, vc, ks, vs = B.alloc_cache(nblocks, hkv, d, dev)
+            kc.copy_(torch.randint(-127, 128, kc.shape, dtype=torch.int8, device=dev, generator=gen))
+            vc.copy_(torch.randint(-127, 128, vc.shape, dtype=torch.int8, device=dev, generator=gen))
+            for sc in (ks, vs):
+                sc.copy_((torch.rand(sc.shape, device=dev, generator=gen) * 0.05 + 0.01)
+                         .half().view(torch.int16))
+            caches.append((kc, vc, ks, vs))
+        q = torch.randn((bsz, hq, d), device=dev, generator=gen).to(torch.bfloat16)
+        tab = torch.from_numpy(table).to(dev)
+        lens = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        out = torch.empty((bsz, hq, d), dtype=torch.float32, device=dev)
+        ws = torch.zeros(B.kv8_decode_workspace_size(bsz, hq, hkv, d, int(ctx.max()), 0),
+                         dtype=torch.uint8, device=dev)
+        row = {"scale": f, "bytes_per_call": int(nbytes), "us": {}}
+        for name, form in forms.items():
+            def call(i):
+                B.paged_decode_attn_kv8(q, *caches[i % reps], tab, lens, int(ctx.max()), out, ws,
+                                        kernel_form=form)
+            for i in range(30):
+                call(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(launches):
+                call(i)
+            e1.record()
+            torch.cuda.synchronize()
+            row["us"][name] = round(e0.elapsed_time(e1) * 1e3 / launches, 2)
+        del caches, ws
+        torch.cuda.empty_cache()
+        row["us"]["read_probe"] = bench_read_ceiling(dev, nbytes)["us_per_launch"]
+        rows.append(row)
+        print(f"scale {f}: {row}", file=sys.stderr, flush=True)
+    def line(r0, r1, name):
+        x0, x1 = r0["bytes_per_call"], r1["bytes_per_call"]
+        y0, y1 = r0["us"][name], r1["us"][name]
+        slope = (y1 - y0) / (x1 - x0)                   # us per byte
+        return {"fixed_us": round(y0 - slope * x0, 2), "stream_gbs": round(1e-3 / slope, 1)}
+    fits = {name: {"smallest_two": line(rows[0], rows[1], name),
+                   "largest_two": line(rows[-2], rows[-1], name)}
+            for name in list(forms) + ["read_probe"]}
+    print(json.dumps({"decode_scaling": "Llama-3.1-8B-shaped batch, contexts U[1024 f, 4096 f]",
+                      "points": rows, "lines": fits}), flush=True)
 
 
 def calibrate_copy(dev, n_bytes=256 << 20, launches=5):
