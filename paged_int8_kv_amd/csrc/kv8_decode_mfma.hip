@@ -280,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
 
   // ---- pass 2: weighted sum of V codes ------------------------------------
   float4_t acc[NVT];
+  float4_t accw = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int base = 0; base < nmine; base += kPf2) {
@@ -293,11 +294,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma2_kernel(SplitArgs a) {
         if (hl < G)
           wb = *reinterpret_cast<const half4_t*>(
               s_w + ((wave + i * kWaves) * G + hl) * kBlock + 4 * q4);
-        value_mfmas<C, NVT>(rv[s], wb, acc);
+        value_mfmas<C, NVT>(rv[s], wb, acc, accw);
       }
       issue_v(s, i + kPf2);
     }
   }
+  value_unbias<C, NVT>(acc, accw);
 
   // this wave's [G][D] result to LDS (the logits are no longer needed)
   if (hl < G) {
@@ -413,6 +415,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
   // O[hl][channel (D/16)(4 q4 + r) + j] in acc[j][r].
   float m_run = kNegInf, l_run = 0.0f;
   float4_t acc[NVT];
+  float4_t accw = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int base = 0; base < nmine; base += kPf) {
@@ -448,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           l_run *= f;
 #pragma unroll
           for (int j = 0; j < NVT; ++j) acc[j] *= f;
+          accw *= f;
         }
         _Float16 w[4];
 #pragma unroll
@@ -458,11 +462,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma1_kernel(SplitArgs a) {
           l_run += p;
         }
         const half4_t wb = {w[0], w[1], w[2], w[3]};
-        value_mfmas<C, NVT>(rv[s], wb, acc);
+        value_mfmas<C, NVT>(rv[s], wb, acc, accw);
       }
       issue(s, i + kPf);
     }
   }
+  value_unbias<C, NVT>(acc, accw);
 
   // ---- the four waves to one split result, all relative to the split max ----
   if (lane < G) s_red[wave * G + lane] = m_run;

@@ -214,6 +214,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
   float cz = 0.0f, nqb = 0.0f;
   float m_run = kNegInf, l_run = 0.0f;
   float4_t acc[NVT];
+  float4_t accw = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   int cur_b = -1, cur_g = 0, seg_flags = 0, seg_nb = 1, nseg = 0;
@@ -223,6 +224,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
   // piece of a pair goes to the wave's LDS slot (0: its first piece, 1: its
   // last one; only those can be cut).
   auto flush = [&]() {
+    value_unbias<C, NVT>(acc, accw);
     float lw = l_run;
     lw += __shfl_xor(lw, 16);
     lw += __shfl_xor(lw, 32);
@@ -346,6 +348,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             l_run = 0.0f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            accw = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             q_operands<D, G, QF32, C>(a, (int64_t)b * Hq + (int64_t)g * G, hl, q4, qb, qlo, cz, nqb);
           }
           if (jb == nbp - 1) seg_flags |= 2;
@@ -373,6 +376,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             l_run *= f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] *= f;
+            accw *= f;
           }
           _Float16 wv[4];
 #pragma unroll
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
           }
           issue_k(sl, i + kSkPf);
           const half4_t wb = {wv[0], wv[1], wv[2], wv[3]};
-          value_mfmas<C, NVT>(rv[sl], wb, acc);
+          value_mfmas<C, NVT>(rv[sl], wb, acc, accw);
           issue_v(sl, i + kSkPf);
         } else {
           issue_k(sl, i + kSkPf);

@@ -231,6 +231,12 @@ struct CodesInt4 {
   __device__ static half2_t nib_pair_raw(uint32_t x, int j) {
     return __builtin_bit_cast(half2_t, ((x >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
   }
+  // The value operands use the logits' encoding, 1 + u/16 = kValueBias +
+  // c * kValueStep: one shift and one bit-op per pair, no subtract; the
+  // bias leaves once per split through the weight sums (value_unbias).
+  static constexpr float kValueBias = 1.5f;
+  static constexpr float kValueStep = 0.0625f;
+  __device__ static half2_t value_pair_raw(uint32_t x, int j) { return logit_pair_raw(x, j); }
   __device__ static half2_t logit_pair_raw(uint32_t x, int j) {
     const uint32_t y = j < 2 ? x << (6 - 4 * j) : x >> (4 * j - 6);
     return __builtin_bit_cast(half2_t, (y & 0x03C003C0u) ^ 0x3E003E00u);

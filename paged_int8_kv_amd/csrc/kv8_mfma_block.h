@@ -159,16 +159,18 @@ __device__ __forceinline__ half8_t logit_operand(const uint4 (&rk)[NCH], int j) 
 // codes: one interleave per token pair and dword, then byte pairs.  4-bit
 // codes (D = 128): the 4 tokens' dwords hold channels 8 hl .. + 7; one byte
 // permute joins two tokens' low (high) halves, whose nibble pairs are then
-// (token t, token t+1) of channel j (4 + j).  Biased integer codes (INT8
-// c + 1152, INT4 c + 1032) are unbiased here, exactly, by one packed fp16
-// subtract per pair: summing biased codes over a long split and taking
-// bias * sum(w) off at its end cancels away too many bits (measured at 264K
-// tokens: INT4 relative error 1.5e-3, INT8 7.3e-4 against 2.1e-4 unbiased,
-// the rest being the fp16 rounding of the weights).
+// (token t, token t+1) of channel j (4 + j).  INT8 codes (c + 1152) are
+// unbiased here, exactly, by one packed fp16 subtract per pair: summing
+// biased codes over a long split and taking bias * sum(w) off at its end
+// cancels away too many bits (measured at 264K tokens: INT8 7.3e-4, INT4
+// with a bias of 1032 1.5e-3, against 2.1e-4 unbiased).  INT4 codes enter
+// as 1.5 + c/16, a bias of 24 code steps, and leave it through the weight
+// sums accw (one more MFMA per block, value_unbias at the end; 258K INT4
+// relative error 6.3e-5) in place of the 16 subtracts per block.
 
 template <class C, int NVT, class VRow>
 __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
-                                            float4_t (&acc)[NVT]) {
+                                            float4_t (&acc)[NVT], float4_t& accw) {
   if constexpr (C::kBits == 4) {
     const uint32_t u0 = dw(rv[0], 0), u1 = dw(rv[1], 0);
     const uint32_t u2 = dw(rv[2], 0), u3 = dw(rv[3], 0);
@@ -179,12 +181,13 @@ __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::exact(C::nib_pair_raw(l01, j)), C::exact(C::nib_pair_raw(l23, j))), wb, acc[j], 0, 0,
-          0);
+          cat4(C::value_pair_raw(l01, j), C::value_pair_raw(l23, j)), wb, acc[j], 0, 0, 0);
       acc[4 + j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-          cat4(C::exact(C::nib_pair_raw(h01, j)), C::exact(C::nib_pair_raw(h23, j))), wb, acc[4 + j], 0,
-          0, 0);
+          cat4(C::value_pair_raw(h01, j), C::value_pair_raw(h23, j)), wb, acc[4 + j], 0, 0, 0);
     }
+    // the weight sums of the 4 tokens per head, for value_unbias
+    const half4_t ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+    accw = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, wb, accw, 0, 0, 0);
   } else {
 #pragma unroll
     for (int k = 0; k < NVT / 4; ++k) {
@@ -201,6 +204,20 @@ __device__ __forceinline__ void value_mfmas(const VRow (&rv)[4], half4_t wb,
       acc[4 * k + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(t2, wb, acc[4 * k + 2], 0, 0, 0);
       acc[4 * k + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(t3, wb, acc[4 * k + 3], 0, 0, 0);
     }
+  }
+}
+
+// The accumulators as sums of w * c: 4-bit value codes enter value_mfmas as
+// kValueBias + c * kValueStep, which value_unbias takes off through the
+// weight sums accw (byte codes enter exact and are left as they are).
+template <class C, int NVT>
+__device__ __forceinline__ void value_unbias(float4_t (&acc)[NVT], const float4_t& accw) {
+  if constexpr (C::kBits == 4) {
+    constexpr float inv = 1.0f / C::kValueStep;
+#pragma unroll
+    for (int j = 0; j < NVT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[j][r] = acc[j][r] * inv - (C::kValueBias * inv) * accw[r];
   }
 }
 
