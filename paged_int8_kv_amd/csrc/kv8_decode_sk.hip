@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
   // piece of a pair goes to the wave's LDS slot (0: its first piece, 1: its
   // last one; only those can be cut).
   auto flush = [&]() {
-    value_unbias<C, NVT>(acc, accw);
+    if constexpr (NIB) value_unbias<C, NVT>(acc, accw);
     float lw = l_run;
     lw += __shfl_xor(lw, 16);
     lw += __shfl_xor(lw, 32);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             l_run = 0.0f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            accw = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (NIB) accw = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             q_operands<D, G, QF32, C>(a, (int64_t)b * Hq + (int64_t)g * G, hl, q4, qb, qlo, cz, nqb);
           }
           if (jb == nbp - 1) seg_flags |= 2;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kSkThreads) void decode_sk_kernel(SplitArgs a) {
             l_run *= f;
 #pragma unroll
             for (int j = 0; j < NVT; ++j) acc[j] *= f;
-            accw *= f;
+            if constexpr (NIB) accw *= f;
           }
           _Float16 wv[4];
 #pragma unroll
