@@ -1,6 +1,6 @@
 // kv8_quant_append kernel: per-token, per-KV-head quantisation of new K/V
-// rows to INT8 (or to FP8 e4m3 for the FP8 cache) and their scatter into
-// 16-token physical blocks.
+// rows to INT8 (or to FP8 e4m3, or to nibble-packed INT4, for those caches)
+// and their scatter into 16-token physical blocks.
 //
 // The method keeps K/V as INT8 produced by dynamic per-token quantisation
 // ("KV-Cache 全栈优化系统" README, section 主要特性); slots address physical
@@ -12,9 +12,10 @@
 // DPP; the fp32 scale is divided with IEEE-correct division (hipcc's
 // default), rounded to fp16 (round-to-nearest-even, subnormals kept) and
 // saturated to 65504; codes use IEEE division, then v_rndne (ties to even)
-// and a symmetric clamp for INT8, or round-to-nearest-even on the e4m3 grid
-// with saturation for FP8 (the code formats are described in kv8_device.h).  Each lane stores its 8 codes (8 bytes) so that the LPR
-// lanes write one contiguous d-byte row of the block.
+// and a symmetric clamp for INT8 (and INT4), or round-to-nearest-even on
+// the e4m3 grid with saturation for FP8 (the code formats are described in
+// kv8_device.h).  Each lane stores its 8 codes (8 bytes; 4 for INT4) so
+// that the LPR lanes write one contiguous row of the block.
 #include "kv8_device.h"
 #include "kv8_launch.h"
 

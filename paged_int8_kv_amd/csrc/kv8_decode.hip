@@ -1,5 +1,6 @@
-// paged_decode_attn_kv8 / paged_decode_attn_fp8kv kernel: split-K
-// flash-decoding over the paged INT8 (or FP8 e4m3) cache for gfx950.
+// paged_decode_attn_kv8 / _fp8kv / _int4kv, v_dot2 form: split-K
+// flash-decoding over the paged INT8 (or FP8 e4m3, or INT4) cache for
+// gfx950.
 //
 // Attention softmax(q K^T * sm_scale) V ("KV Cache 优化全景解析", section 2.1)
 // per GQA group (section 3.3) over K/V restored on the fly from INT8 codes
@@ -30,12 +31,14 @@
 // the fp16 value c + 1152 built by one byte permute (see kv8_device.h); the
 // bias is removed once per token in pass 1 (the sums start at minus 1152 *
 // sum q_h) and from each V code pair in pass 2 (one packed fp16 subtract,
-// exact).  The same kernel
-// serves the FP8 (e4m3) cache ("KV Cache 优化全景解析", section 7.4), whose
-// codes become exact fp16 pairs by one hardware convert and carry no bias.
-// q enters as fp16 after an exact
-// per-head power-of-two rescale (bf16 q is exact in fp16 then); an fp32 q
-// is split into a high and a low fp16 part.
+// exact).  The same kernel serves the FP8 (e4m3) cache ("KV Cache 优化全景
+// 解析", section 7.4), whose codes become exact fp16 pairs by one hardware
+// convert and carry no bias, and the INT4 cache, whose nibbles enter the
+// logits as 1.5 + c/16 (one shift and one bit operation per pair; the sums
+// start at minus 1.5 * sum q_h) and the values as c + 1032 less the bias,
+// exactly.  q enters as fp16 after an exact per-head power-of-two rescale
+// (bf16 q is exact in fp16 then); an fp32 q is split into a high and a low
+// fp16 part.
 //
 // Each wave keeps kPf blocks in flight in a register ring; the ring is
 // branch-free around its loads so that the compiler's wait counts stay

@@ -1,8 +1,8 @@
 // Decode machinery shared by the paged-attention decode kernels of libkv8
-// (INT8 and bf16 caches) on gfx950: the work items and their order, the
-// span of blocks a split covers, the cross-lane reductions, and the end of a
-// split (partial results and the in-launch log-sum-exp merge).  Nothing here
-// is used outside the HIP library.
+// (INT8, FP8, INT4 and bf16 caches) on gfx950: the work items and their
+// order, the span of blocks a split covers, the cross-lane reductions, and
+// the end of a split (partial results and the in-launch log-sum-exp merge).
+// Nothing here is used outside the HIP library.
 #pragma once
 
 #include <atomic>

@@ -47,11 +47,15 @@
 // pair, kv8_device.h); the bias is removed from the logits by starting the
 // accumulator at minus 1152 * sum(q_h), and from the V codes themselves, one
 // packed fp16 subtract per pair, before they meet the weights.  FP8 codes
-// become exact fp16 by one hardware convert per pair.  INT4 codes (one-pass
-// kernel) enter as c + 1032: a flip of each nibble's sign bit and one and-or
-// with the fp16 pattern per nibble pair, unbiased like INT8's V codes.  q
-// enters as fp16 after an exact per-head power-of-two rescale; an fp32 q is
-// split into a high and a low fp16 part (two MFMAs).
+// become exact fp16 by one hardware convert per pair.  INT4 codes (d = 128,
+// both kernels) enter both products as 1.5 + c/16 exactly: one shift and one
+// three-input bit operation per nibble pair put the sign-flipped nibble into
+// the top mantissa bits of 1.0.  The logits start their accumulator at minus
+// 1.5 * sum(q_h) and take the 1/16 into the logit scale; the values keep the
+// bias in their sums and take it off once per split through the weight sums
+// that one more MFMA per block accumulates (value_unbias).  q enters as fp16
+// after an exact per-head power-of-two rescale; an fp32 q is split into a
+// high and a low fp16 part (two MFMAs).
 #include "kv8_decode_common.h"
 #include "kv8_device.h"
 #include "kv8_launch.h"

@@ -10,14 +10,14 @@
 //
 // Work units are the (sequence b, KV head g, block j) triples in that
 // order: pair p = b * Hkv + g holds nb_b = ceil(ctx_b / 16) consecutive
-// units.  With T units in all and NW workgroups (one per compute unit, 16
-// waves each), workgroup w takes units [w T / NW, (w + 1) T / NW) and wave v
-// of it the v-th of 16 near-equal contiguous parts of that range.  A wave streams
-// its units in order with the one-pass online softmax (K and V tiles of the
-// next block in flight while the current block is computed), starting a new
-// softmax state at every pair boundary, so its memory stream never waits on
-// another wave: there are no per-item prologues, no mid-item barriers and no
-// tail of unequal items.
+// units.  With T units in all and NW workgroups (one per compute unit,
+// kSkWaves = 8 waves each), workgroup w takes units [w T / NW, (w + 1) T /
+// NW) and wave v of it the v-th of kSkWaves near-equal contiguous parts of
+// that range.  A wave streams its units in order with the one-pass online
+// softmax (K and V tiles of the next blocks in flight while the current
+// block is computed), starting a new softmax state at every pair boundary,
+// so its memory stream never waits on another wave: there are no per-item
+// prologues, no mid-item barriers and no tail of unequal items.
 //
 // A pair wholly inside one wave's part is normalised and written by that
 // wave.  A pair cut by wave boundaries leaves the state of each piece (sums

@@ -1,10 +1,10 @@
 // Internal launchers of libkv8: called by the C ABI layer (kv8_api.cpp)
 // after host validation.  `fmt` selects the code format of the cache
 // (kFmtInt8, kFmtFp8 = e4m3, kFmtInt4 = packed nibbles); caches are passed
-// as bytes either way.  A
-// non-null k_new/v_new makes launch_decode append each sequence's newest
-// token (position context_lens[b] - 1) before attending.  Each returns 0 on
-// success and -1 when the HIP runtime reports a launch error.
+// as bytes either way.  A non-null k_new/v_new makes launch_decode append
+// each sequence's newest token (position context_lens[b] - 1) before
+// attending.  Each returns 0 on success and -1 when the HIP runtime reports
+// a launch error.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,12 +28,12 @@ int launch_rope_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                              hipStream_t stream);
 
 // Which form of the INT8 / FP8 / INT4 decode kernel a call launches:
-// automatic (by group size and size), the v_dot2 kernel, the two-pass or the
-// one-pass matrix-core kernel.  A per-call choice (the library keeps no
-// setting).  decode_form: the form a launch of this code format, group size,
-// grid bound (workgroups with every sequence at the longest context and
-// 1024-token splits), longest context and head dim takes when `requested`
-// is asked for.
+// automatic (by group size and size), the v_dot2 kernel, or the two-pass,
+// one-pass or stream-K matrix-core kernel.  A per-call choice (the library
+// keeps no setting).  decode_form: the form a launch of this code format,
+// group size, grid bound (workgroups with every sequence at the longest
+// context and 1024-token splits), longest context and head dim takes when
+// `requested` is asked for.
 enum : int {
   kDecodeKernelAuto = 0, kDecodeKernelDot = 1, kDecodeKernelMfma = 2, kDecodeKernelMfmaOnePass = 3,
   kDecodeKernelStreamK = 4
@@ -64,7 +64,7 @@ constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
 void* decode_scratch(hipStream_t stream);
 
 struct DecodePlan {
-  int form;              // kDecodeKernelDot / Mfma / MfmaOnePass
+  int form;              // kDecodeKernelDot / Mfma / MfmaOnePass / StreamK
   int split_tokens;      // tokens per workgroup (multiple of 64)
   int n_split;           // workgroups per (sequence, KV head)
   size_t counter_bytes;  // kCounterBytes: uint32 finished-split counters (self-resetting)

@@ -29,8 +29,10 @@
 // INT8 codes become fp16 without a convert per code: u = c xor 0x80 under
 // the fp16 high byte 0x64 is the value c + 1152, and one packed fp16
 // subtract of 1152 leaves c exactly.  The same kernel serves the FP8 (e4m3)
-// cache ("KV Cache 优化全景解析", section 7.4): its codes become exact fp16
-// pairs by one hardware convert.
+// cache ("KV Cache 优化全景解析", section 7.4), whose codes become exact
+// fp16 pairs by one hardware convert, and the INT4 cache, whose nibble pairs
+// become c + 1032 by a shift and one and-or with the fp16 pattern, and then c
+// by the same kind of subtract; only the staging differs.
 //
 // Per wave and key tile (v_mfma_f32_32x32x16_f16, fp32 accumulate):
 //   S^T[key][query] = K_code . Q^T, with Q scaled by one power of two 2^e
