@@ -211,6 +211,40 @@ def test_decode_workspace_reused_across_pair_counts():
     assert int(ws[:4 * B.MAX_DECODE_PAIRS].count_nonzero()) == 0
 
 
+@functools.lru_cache(maxsize=None)
+def max_pairs_case():
+    """4096 sequences x 16 KV heads, contexts of 0..40 tokens (every 97th
+    empty), with its oracle cache and output, built once and shared by the
+    kernel forms."""
+    def lens(rng):
+        c = rng.integers(0, 41, size=4096)
+        c[::97] = 0
+        return c
+    case = W.make_paged_case(batch=4096, num_q_heads=64, num_kv_heads=16, head_dim=64,
+                             context_lens=lens, seed=130)
+    kc, vc, ks, vs = oracle_cache(case)
+    ref = O.paged_decode(case.q, kc, vc, ks, vs, case.block_table, case.context_lens)
+    return case, (kc, vc, ks, vs), ref
+
+
+def test_decode_max_pairs():
+    """The most (sequence, KV head) pairs one call takes: 4096 x 16 = 65536,
+    KV8_DECODE_MAX_PAIRS.  The split counters fill the fixed counter region
+    to its last word (stream-K's one word apart), and the items keep
+    sequence order (more than 64 sequences).  Every output element is
+    written (NaN-filled beforehand) and within tolerance of the oracle, the
+    empty contexts give exact zeros, and the counters are left zero."""
+    case, oc, ref = max_pairs_case()
+    assert case.batch * case.num_kv_heads == B.MAX_DECODE_PAIRS
+    ws = torch.zeros(B.kv8_decode_workspace_size(case.batch, 64, 16, 64,
+                                                 int(case.context_lens.max()), 0),
+                     dtype=torch.uint8, device=dev())
+    out = gpu_decode(case, upload_cache(*oc), workspace=ws)
+    check_close(out, ref, "65536 pairs")
+    assert np.all(out[case.context_lens == 0] == 0.0)
+    assert int(ws[:4 * B.MAX_DECODE_PAIRS].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("tps", [0, 128, 1024])
 def test_decode_rising_logits_rescale_every_block(tps):
     """Keys whose logits climb block after block (about 9 in log2 units per
