@@ -293,7 +293,100 @@ def _unpack_int4_sign_magnitude(packed):
     return out.astype(np.int8)
 
 
+def _gather_scale_of_head0(codes, scales, block_table_row, ctx, kv_head, block_size=16):
+    t = np.arange(ctx)
+    blk, off = O.logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return O.dequantize_rows(codes[blk, kv_head, off, :], scales[blk, 0, off])   # head 0's scales
+
+
+def _gather_scale_next_token(codes, scales, block_table_row, ctx, kv_head, block_size=16):
+    t = np.arange(ctx)
+    blk, off = O.logical_to_physical(np.asarray(block_table_row), t, block_size)
+    return O.dequantize_rows(codes[blk, kv_head, off, :],
+                             scales[blk, kv_head, (off + 1) % block_size])
+
+
+def _append_no_skip(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                    block_size=16):
+    kc, ks = O.quantize_rows(k_new)
+    vc, vs = O.quantize_rows(v_new)
+    for n, slot in enumerate(np.asarray(slot_mapping).tolist()):   # negative slots written too
+        blk, off = O.slot_to_block(slot, block_size)
+        k_cache[blk, :, off, :] = kc[n]
+        v_cache[blk, :, off, :] = vc[n]
+        k_scale[blk, :, off] = ks[n]
+        v_scale[blk, :, off] = vs[n]
+
+
+def _decode_drops_newest(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens,
+                         sm_scale=None, block_size=16):
+    return _REAL["paged_decode"](q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                 np.maximum(np.asarray(context_lens) - 1, 0), sm_scale, block_size)
+
+
+def _prefill_rows_from_zero(q, q_start_loc, k_cache, v_cache, k_scale, v_scale, block_table,
+                            context_lens, sm_scale=None, block_size=16):
+    qs = np.asarray(q_start_loc).copy()
+    lens = np.diff(qs)
+    out = np.zeros(np.asarray(q).shape, np.float64)
+    for b in range(len(lens)):      # every sequence's rows read from row 0
+        one = _REAL["paged_prefill_chunk"](np.asarray(q)[:lens[b]], np.array([0, lens[b]]),
+                                           k_cache, v_cache, k_scale, v_scale,
+                                           np.asarray(block_table)[b:b + 1],
+                                           np.asarray(context_lens)[b:b + 1], sm_scale, block_size)
+        out[qs[b]:qs[b + 1]] = one
+    return out
+
+
+def _int4_codes_clamp_8(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = x32 / np.where(zero, np.float32(1), s32)
+    q = np.clip(np.rint(quot.astype(np.float64)), -8, 7)
+    return np.where(zero, 0.0, q).astype(np.int8)
+
+
+def _int4_codes_half_away(x, s):
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    s32 = np.asarray(s, dtype=np.float16).astype(np.float32)[..., None]
+    zero = s32 == 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quot = (x32 / np.where(zero, np.float32(1), s32)).astype(np.float64)
+    q = np.clip(np.sign(quot) * np.floor(np.abs(quot) + 0.5), -7, 7)
+    return np.where(zero, 0.0, q).astype(np.int8)
+
+
+def _fp8_dequant_no_scale(codes, scales):
+    return O.e4m3_value(codes) + 0.0 * np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+def _int4_dequant_no_scale(packed, scales):
+    return O.unpack_int4(packed).astype(np.float64) + \
+        0.0 * np.asarray(scales, np.float16).astype(np.float64)[..., None]
+
+
+def _rope_append_position_plus_one(k_pre, v_new, positions, cos_sin, slot_mapping, k_cache,
+                                   v_cache, k_scale, v_scale, block_size=16):
+    k_rot = O.rope_rotate_half(k_pre, np.asarray(positions) + 1, cos_sin)
+    O.quant_append(k_rot, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, block_size)
+
+
+_REAL = {"paged_decode": O.paged_decode, "paged_prefill_chunk": O.paged_prefill_chunk}
+
+
 MUTANTS = {
+    "gather_scale_of_head0": ("gather_dequant", _gather_scale_of_head0),
+    "gather_scale_next_token": ("gather_dequant", _gather_scale_next_token),
+    "append_no_skip": ("quant_append", _append_no_skip),
+    "decode_drops_newest": ("paged_decode", _decode_drops_newest),
+    "prefill_rows_from_zero": ("paged_prefill_chunk", _prefill_rows_from_zero),
+    "int4_codes_clamp_8": ("codes_int4_for_scale", _int4_codes_clamp_8),
+    "int4_codes_half_away": ("codes_int4_for_scale", _int4_codes_half_away),
+    "fp8_dequant_no_scale": ("dequantize_rows_fp8", _fp8_dequant_no_scale),
+    "int4_dequant_no_scale": ("dequantize_rows_int4", _int4_dequant_no_scale),
+    "rope_append_position_plus_one": ("rope_quant_append", _rope_append_position_plus_one),
     "head_map_mod": ("kv_head_of", lambda h, group: h % group),
     "page_transposed": ("logical_to_physical", lambda row, t, bs=16: (row[t % bs], t // bs)),
     "page_identity": ("logical_to_physical", lambda row, t, bs=16: (t // bs, t % bs)),

@@ -244,11 +244,16 @@ def test_append_scatter_and_skip():
                              context_lens=[21, 40], seed=9)
     slots = case.slot_mapping.copy()
     slots[3] = -1
-    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks, 2, 16)
+    # one spare block past the pool, never a slot's target: a skipped row
+    # written anyway (e.g. at slot -1, the last slot of the last block)
+    # lands there and shows
+    kc, vc, ks, vs = O.alloc_paged_cache(case.num_blocks + 1, 2, 16)
     O.quant_append(case.k, case.v, slots, kc, vc, ks, vs)
     codes_k, sc_k = quantize_reference_rows(case.k.reshape(-1, 16))
     codes_k = codes_k.reshape(case.k.shape)
     sc_k = sc_k.reshape(case.k.shape[:2])
+    exp_kc = np.zeros(kc.shape, np.int64)
+    exp_ks = np.zeros(ks.shape, np.float64)
     for n in range(len(slots)):
         blk, off = divmod(int(case.slot_mapping[n]), 16)
         if n == 3:
@@ -256,6 +261,18 @@ def test_append_scatter_and_skip():
             continue
         assert np.array_equal(kc[blk, :, off].astype(np.int64), codes_k[n])
         assert np.array_equal(ks[blk, :, off].astype(np.float64), sc_k[n])
+        exp_kc[blk, :, off] = codes_k[n]
+        exp_ks[blk, :, off] = sc_k[n]
+    # nothing is written anywhere else: not the skipped row under any other
+    # reading of its slot, not the blocks' unused tails
+    assert np.array_equal(kc.astype(np.int64), exp_kc)
+    assert np.array_equal(ks.astype(np.float64), exp_ks)
+    written = np.zeros(vs.shape, bool)
+    for n in range(len(slots)):
+        if n != 3:
+            blk, off = divmod(int(case.slot_mapping[n]), 16)
+            written[blk, :, off] = True
+    assert np.all(vc[~written] == 0) and np.all(vs[~written] == 0)
 
 
 # ---------------------------------------------------------------------------
