@@ -37,7 +37,9 @@
  * Conventions
  * -----------
  * - Ownership: the caller allocates every buffer, including the workspace;
- *   the library allocates nothing and keeps no state between calls.
+ *   the library allocates nothing.  It keeps no setting between calls: what
+ *   it does hold (the allocation-free decode's fixed scratch, cached device
+ *   properties) never changes what a call computes.
  * - Ordering: each call validates its host arguments, enqueues its kernels
  *   on `stream` (a hipStream_t; NULL = the default stream) and returns
  *   without synchronising.
