@@ -67,6 +67,28 @@ def test_prefill_chunked_config_full_sampled():
     check_close(got, ref, "chunked prefill full, sampled rows")
 
 
+def test_prefill_long_chunks_sampled():
+    """Chunks of 4096 and 2049 rows after 0 and 12000 earlier tokens (64 and
+    33 query tiles per KV head at G = 4): the longest causal diagonals and
+    the most query tiles per pair.  Rows sampled at tile edges, the chunk's
+    ends and at random, all query heads, against the oracle."""
+    lens = [4096, 2049]
+    case = W.prefill_case([0, 12000], lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                          seed=140, k_outliers=True)
+    host = oracle_cache(case)
+    out = gpu_prefill(case, upload_cache(*host))
+    rng = np.random.default_rng(141)
+    picks = []
+    for b, n in enumerate(lens):
+        rows = {0, 1, 63, 64, 127, 128, 1023, 1024, 2047, 2048, n - 2, n - 1,
+                *rng.integers(0, n, 6).tolist()}
+        picks += [(b, int(i)) for i in sorted(r for r in rows if 0 <= r < n)]
+    ref = oracle_prefill_rows(case, host, picks)
+    qsl = case.extra["q_start_loc"]
+    got = np.stack([out[qsl[b] + i] for b, i in picks])
+    check_close(got, ref, "long chunks, sampled rows")
+
+
 def test_prefill_chunk_of_one_matches_decode():
     """A chunk of one row is a decode step: both kernels agree with the
     oracle's decode."""
