@@ -375,7 +375,11 @@ int paged_decode_attn_bf16kv(const void* q, int q_dtype,
  *   context_lens  device int32 [B], counts the chunk's tokens too; must be
  *                 >= Lc_b (rows of a sequence violating this are undefined)
  *   out           device fp32 [total_q, Hq, d]
- *   workspace     may be NULL when kv8_prefill_workspace_size() returns 0
+ *   workspace     may be NULL when kv8_prefill_workspace_size() returns 0,
+ *                 which it does for every shape: the prefill kernels keep
+ *                 all their state on chip.  The argument stays in the ABI so
+ *                 that a kernel needing one can be added without changing
+ *                 the signature.
  */
 size_t kv8_prefill_workspace_size(int batch, int num_q_heads, int head_dim,
                                   int max_q_len, int max_context_len);
